@@ -1,0 +1,526 @@
+"""Pins of the CPU oracle against facts fixed outside itself.
+
+Each test ties one oracle function to a published value, a closed form, a library
+routine on a special case, or brute force on tiny inputs, chosen so that a plausible
+slip (a dropped term, a wrong sign or index, a transposed operand) fails.
+"""
+import itertools
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import sparsepr_oracle as O
+
+GOLD = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _rows(path):
+    with open(os.path.join(GOLD, path)) as f:
+        return [ln.split() for ln in f if ln.strip() and not ln.startswith("#")]
+
+
+# ---------------------------------------------------------------- hash and selection
+def test_splitmix64_published_vector():
+    want = [int(r[0]) for r in _rows("splitmix64_seed1234567.txt")]
+    g = 0x9E3779B97F4A7C15
+    states = np.array([(1234567 + n * g) % 2 ** 64 for n in range(5)], dtype=np.uint64)
+    with np.errstate(over="ignore"):
+        got = [int(x) for x in O.splitmix64(states)]
+    assert got == want
+
+
+def test_token_hash_is_nested_splitmix():
+    # h(stream, head, i) built from scalar Python big-int arithmetic, independently.
+    M64 = 2 ** 64 - 1
+
+    def sm(x):
+        z = (x + 0x9E3779B97F4A7C15) & M64
+        z = ((z ^ (z >> 30)) * 0xBF58476D1CE4E5B9) & M64
+        z = ((z ^ (z >> 27)) * 0x94D049BB133111EB) & M64
+        return z ^ (z >> 31)
+
+    for seed, stream, head, i in [(0, 1, 0, 0), (7, 4, 39, 118799), (2 ** 63 + 5, 2, 3, 17)]:
+        want = sm(sm(sm(seed ^ stream) ^ head) ^ i)
+        assert int(O.token_hash(seed, stream, head, [i])[0]) == want
+
+
+def test_select_smallest_brute_force():
+    cand = np.array([3, 5, 8, 13, 21, 34, 55, 89])
+    for m in range(0, 9):
+        got = O.select_smallest(11, 2, 5, cand, m)
+        h = [int(x) for x in O.token_hash(11, 2, 5, cand)]
+        ranked = sorted(zip(h, cand.tolist()))[:m]
+        assert got.tolist() == sorted(c for _, c in ranked)
+
+
+def test_select_smallest_is_uniform_without_replacement():
+    # Every candidate is chosen with probability m/n; check over many heads.
+    n, m, heads = 40, 10, 2000
+    hits = np.zeros(n)
+    for h in range(heads):
+        s = O.select_smallest(3, 1, h, np.arange(n), m)
+        assert len(set(s.tolist())) == m
+        hits[s] += 1
+    freq = hits / heads
+    assert np.all(np.abs(freq - m / n) < 5 * math.sqrt(0.25 * 0.75 / heads))
+
+
+# ---------------------------------------------------------------- attention
+def test_dense_attention_matches_torch_sdpa_fp64():
+    rng = np.random.default_rng(0)
+    q, k, v = (rng.standard_normal((37, 16)) for _ in range(3))
+    scale = 0.3
+    got = O.dense_attention(q, k, v, scale, chunk=8)
+    want = torch.nn.functional.scaled_dot_product_attention(
+        torch.from_numpy(q)[None], torch.from_numpy(k)[None], torch.from_numpy(v)[None], scale=scale)[0].numpy()
+    np.testing.assert_allclose(got, want, rtol=1e-12, atol=1e-12)
+
+
+def _tiny_partition(rng, N, Cq, Ck):
+    ql = rng.integers(0, Cq, N)
+    kl = rng.integers(0, Ck, N)
+    ql[:Cq] = np.arange(Cq)
+    kl[:Ck] = np.arange(Ck)
+    return ql, kl
+
+
+def test_block_sparse_equals_masked_dense():
+    rng = np.random.default_rng(1)
+    N, d, Cq, Ck = 50, 8, 4, 5
+    q, k, v = (rng.standard_normal((N, d)) for _ in range(3))
+    ql, kl = _tiny_partition(rng, N, Cq, Ck)
+    sel = rng.random((Cq, Ck)) < 0.5
+    sel[np.arange(Cq), rng.integers(0, Ck, Cq)] = True
+    qp, qo, _ = O.group_permutation(ql, Cq)
+    kp, ko, _ = O.group_permutation(kl, Ck)
+    cols = [np.flatnonzero(sel[a]) for a in range(Cq)]
+    rp = np.concatenate([[0], np.cumsum([len(c) for c in cols])])
+    got = O.block_sparse_attention(q, k, v, 0.5, qp, qo, kp, ko, rp, np.concatenate(cols))
+    # brute force: -inf mask per (query, key) pair from the selected cells
+    logits = 0.5 * q @ k.T
+    mask = sel[ql][:, kl]
+    logits[~mask] = -np.inf
+    p = np.exp(logits - logits.max(1, keepdims=True))
+    want = (p / p.sum(1, keepdims=True)) @ v
+    np.testing.assert_allclose(got, want, rtol=1e-12, atol=1e-12)
+
+
+def test_block_sparse_all_cells_is_dense():
+    rng = np.random.default_rng(2)
+    N, d = 40, 8
+    q, k, v = (rng.standard_normal((N, d)) for _ in range(3))
+    ql, kl = _tiny_partition(rng, N, 3, 4)
+    qp, qo, _ = O.group_permutation(ql, 3)
+    kp, ko, _ = O.group_permutation(kl, 4)
+    rp = np.array([0, 4, 8, 12])
+    cols = np.tile(np.arange(4), 3)
+    got = O.block_sparse_attention(q, k, v, 0.7, qp, qo, kp, ko, rp, cols)
+    np.testing.assert_allclose(got, O.dense_attention(q, k, v, 0.7), rtol=1e-12, atol=1e-12)
+
+
+# ---------------------------------------------------------------- k-means
+def test_sq_dists_matches_direct_differences():
+    rng = np.random.default_rng(3)
+    x, c = rng.standard_normal((9, 5)), rng.standard_normal((4, 5))
+    direct = np.array([[np.sum((xi - cj) ** 2) for cj in c] for xi in x])
+    np.testing.assert_allclose(O.sq_dists(x, c), direct, rtol=1e-12, atol=1e-12)
+
+
+def _lloyd_loops(x, init, max_iter, tol):
+    """Textbook Lloyd written with explicit loops (no vector algebra), for tiny inputs."""
+    cent = [list(x[i]) for i in init]
+    prev, labels, t = None, None, 0
+    for t in range(1, max_iter + 1):
+        labels, inertia = [], 0.0
+        for row in x:
+            ds = [sum((a - b) ** 2 for a, b in zip(row, c)) for c in cent]
+            j = min(range(len(ds)), key=lambda i: (ds[i], i))
+            labels.append(j)
+            inertia += ds[j]
+        if prev is not None and prev - inertia <= tol * prev:
+            break
+        if t == max_iter:
+            break
+        for c in range(len(cent)):
+            mem = [x[i] for i in range(len(x)) if labels[i] == c]
+            if mem:
+                cent[c] = [sum(col) / len(mem) for col in zip(*mem)]
+        prev = inertia
+    return labels, t
+
+
+def test_lloyd_matches_loop_brute_force():
+    rng = np.random.default_rng(4)
+    for trial in range(5):
+        x = rng.standard_normal((30, 3)) + rng.integers(0, 3, (30, 1)) * 2.0
+        init = rng.choice(30, 4, replace=False)
+        r = O.lloyd(x, init, 25, 1e-4)
+        lab, it = _lloyd_loops(x, init, 25, 1e-4)
+        assert r.labels.tolist() == lab and r.iterations == it
+
+
+def test_lloyd_inertia_non_increasing_and_fixed_point():
+    rng = np.random.default_rng(5)
+    x = rng.standard_normal((400, 6))
+    r = O.lloyd(x, np.arange(12), 200, 0.0)
+    assert all(b <= a * (1 + 1e-12) for a, b in zip(r.inertia, r.inertia[1:]))
+    # converged with tol 0: one more update + assignment changes nothing
+    cent = O.group_means(x, r.labels, 12)
+    assert np.array_equal(np.argmin(O.sq_dists(x, cent), axis=1), r.labels)
+
+
+def test_lloyd_recovers_planted_partition():
+    rng = np.random.default_rng(6)
+    C, per, d = 5, 40, 8
+    means = rng.standard_normal((C, d)) * 20
+    truth = np.repeat(np.arange(C), per)
+    x = means[truth] + rng.standard_normal((C * per, d))
+    init = [np.flatnonzero(truth == c)[0] for c in range(C)]
+    r = O.lloyd(x, init, 25, 1e-4)
+    assert np.array_equal(r.labels, truth)
+
+
+def test_lloyd_stops_on_tolerance_and_cap():
+    rng = np.random.default_rng(7)
+    x = rng.standard_normal((200, 4))
+    assert O.lloyd(x, np.arange(6), 3, 0.0).iterations == 3
+    r = O.lloyd(x, np.arange(6), 50, 1e-4)
+    i = r.inertia
+    assert i[-2] - i[-1] <= 1e-4 * i[-2]
+    assert all(a - b > 1e-4 * a for a, b in zip(i[:-2], i[1:-1]))
+
+
+def test_metric_form_of_key_kmeans_is_exact():
+    """Lloyd on R_K = s K Q_S^T equals Lloyd on K under the metric G = s^2 Q_S^T Q_S.
+
+    Every centroid is a mean of response rows, hence s m Q_S^T for a key-space mean m,
+    so |R_K,j - c|^2 = (k_j - m) G (k_j - m)^T: both runs choose the same labels.
+    """
+    rng = np.random.default_rng(8)
+    N, d, S, C, s = 300, 6, 10, 7, 0.4
+    k = rng.standard_normal((N, d)) + rng.integers(0, 4, (N, 1))
+    qs = rng.standard_normal((S, d))
+    init = rng.choice(N, C, replace=False)
+    lit = O.lloyd(O.key_responses(k, qs, s), init, 25, 1e-4)
+    G = s * s * qs.T @ qs
+    # metric Lloyd in key space written out directly
+    cent = k[init].copy()
+    prev, lab = None, None
+    for t in range(1, 26):
+        diff = k[:, None, :] - cent[None, :, :]
+        dist = np.einsum("ncd,de,nce->nc", diff, G, diff)
+        lab = dist.argmin(1)
+        inertia = dist[np.arange(N), lab].sum()
+        if prev is not None and prev - inertia <= 1e-4 * prev:
+            break
+        if t == 25:
+            break
+        for c in range(C):
+            if np.any(lab == c):
+                cent[c] = k[lab == c].mean(0)
+        prev = inertia
+    assert np.array_equal(lab, lit.labels) and t == lit.iterations
+
+
+def test_compact_and_permutation_invariants():
+    labels = np.array([5, 2, 5, 0, 2, 2, 7])
+    c, Cc = O.compact_labels(labels, 9)
+    assert Cc == 4 and c.tolist() == [2, 1, 2, 0, 1, 1, 3]
+    perm, off, cnt = O.group_permutation(c, Cc)
+    assert sorted(perm.tolist()) == list(range(7))
+    assert perm.tolist() == [3, 1, 4, 5, 0, 2, 6]          # stable by token id
+    assert off.tolist() == [0, 1, 4, 6, 7] and cnt.tolist() == [1, 3, 2, 1]
+    inv = np.empty_like(perm)
+    inv[perm] = np.arange(7)
+    assert np.array_equal(perm[inv], np.arange(7))
+
+
+# ---------------------------------------------------------------- responses and masses
+def test_query_features_rms_normalised():
+    rng = np.random.default_rng(9)
+    q, c = rng.standard_normal((20, 4)), rng.standard_normal((6, 4))
+    q[3] = 0.0
+    L, F = O.query_features(q, c, 0.5)
+    assert np.allclose(L, 0.5 * np.einsum("id,bd->ib", q, c))
+    rms = np.sqrt((F ** 2).mean(1))
+    assert np.allclose(np.delete(rms, 3), 1.0) and np.all(F[3] == 0)
+    # scale invariance of F: multiplying a query by 7 leaves its features unchanged
+    _, F7 = O.query_features(q * 7.0, c, 0.5)
+    assert np.allclose(F7, F)
+
+
+def test_group_masses_closed_forms():
+    # equal logits: p_i(b) = n_k[b] / N (softmax of log sizes)
+    n_k = np.array([3, 1, 4, 2])
+    L = np.zeros((6, 4))
+    P, u = O.group_masses(L, n_k, np.array([0, 1, 0, 1, 1, 0]), 2)
+    assert np.allclose(P, np.tile(n_k / n_k.sum(), (2, 1)))
+    # hand value: two groups of one key, logits (ln 3, 0) -> masses (3/4, 1/4)
+    P, u = O.group_masses(np.array([[math.log(3.0), 0.0]]), np.array([1, 1]), np.array([0]), 1)
+    assert np.allclose(P, [[0.75, 0.25]]) and u.tolist() == [[3 * 2 ** 30, 2 ** 30]]
+    rng = np.random.default_rng(10)
+    L = rng.standard_normal((50, 7)) * 3
+    P, u = O.group_masses(L, rng.integers(1, 9, 7), rng.integers(0, 3, 50), 3)
+    assert np.allclose(P.sum(1), 1.0)
+    assert np.all(np.abs(u.sum(1) - 2 ** 32) <= 7)
+
+
+# ---------------------------------------------------------------- routing
+def _route_brute(u, n_q, n_k, N, M, rho):
+    """Scan every candidate selection implied by the sorted rows; keep the cheapest-fitting max."""
+    Cq, Ck = u.shape
+    budget = O.pair_budget(N, M, rho)
+    orders = [sorted(range(Ck), key=lambda b: (-u[a, b], b)) for a in range(Cq)]
+    # the thresholds that matter are 0, each prefix mass, each prefix mass + 1, and the top
+    pts = {0, 2 ** 32 + Ck}
+    for a in range(Cq):
+        c = 0
+        for b in orders[a]:
+            c += int(u[a, b])
+            pts.update({c, c + 1})
+    best = None
+    for tau in sorted(pts):
+        if tau > 2 ** 32 + Ck:
+            continue
+        js, cost = [], 0
+        for a in range(Cq):
+            c, j = 0, 0
+            for j, b in enumerate(orders[a], 1):
+                c += int(u[a, b])
+                if c >= tau:
+                    break
+            js.append(max(j, 1))
+            cost += int(n_q[a]) * sum(int(n_k[b]) for b in orders[a][:js[-1]])
+        if cost <= budget:
+            best = [sorted(orders[a][:js[a]]) for a in range(Cq)]
+    if best is None:
+        return [[orders[a][0]] for a in range(Cq)], True
+    return best, False
+
+
+def test_route_matches_brute_force_threshold_scan():
+    rng = np.random.default_rng(11)
+    for trial in range(40):
+        Cq, Ck = rng.integers(1, 5), rng.integers(1, 6)
+        n_q = rng.integers(1, 9, Cq)
+        n_k = rng.integers(1, 9, Ck)
+        N = int(max(n_q.sum(), n_k.sum()))
+        P = rng.dirichlet(np.ones(Ck) * 0.5, Cq)
+        u = np.rint(P * 2 ** 32).astype(np.int64)
+        if trial % 5 == 0:
+            u[:, -1] = u[:, 0]            # exact ties between groups
+        M = int(rng.integers(0, 3))
+        rho = float(rng.uniform(0.02, 1.2))
+        rt = O.route(u, n_q, n_k, N, M, rho)
+        want, flag = _route_brute(u, n_q, n_k, N, M, rho)
+        got = [rt.cols[rt.row_ptr[a]:rt.row_ptr[a + 1]].tolist() for a in range(Cq)]
+        assert got == want and rt.budget_exceeded == flag
+
+
+def test_route_invariants():
+    rng = np.random.default_rng(12)
+    Cq, Ck, N, M = 12, 15, 600, 6
+    n_q = rng.multinomial(N - Cq, np.ones(Cq) / Cq) + 1
+    n_k = rng.multinomial(N - Ck, np.ones(Ck) / Ck) + 1
+    u = np.rint(rng.dirichlet(np.ones(Ck), Cq) * 2 ** 32).astype(np.int64)
+    prev = None
+    for rho in [0.05, 0.1, 0.2, 0.4, 0.8, 1.0 + M / N]:
+        rt = O.route(u, n_q, n_k, N, M, rho)
+        sel = {(a, b) for a in range(Cq) for b in rt.cols[rt.row_ptr[a]:rt.row_ptr[a + 1]]}
+        assert all(rt.row_ptr[a + 1] > rt.row_ptr[a] for a in range(Cq))
+        pairs = O.executed_pairs(rt, n_q, n_k, N, M)
+        assert rt.budget_exceeded or pairs <= math.floor(rho * N * N)
+        if prev is not None:
+            assert prev <= sel                      # monotone in the budget
+        prev = sel
+    assert len(prev) == Cq * Ck                     # rho = 1 + M/N keeps every cell
+    rt = O.route(u, n_q, n_k, N, M, 1e-4)
+    assert rt.budget_exceeded and np.all(np.diff(rt.row_ptr) == 1)
+    assert all(rt.cols[a] == np.lexsort((np.arange(Ck), -u[a]))[0] for a in range(Cq))
+
+
+# ---------------------------------------------------------------- probes
+def test_allocate_probes_largest_remainder_brute_force():
+    for n_q, M in [([5, 3, 2], 4), ([1, 1, 1, 1], 2), ([7, 7, 7], 5), ([10, 1, 4, 9], 24), ([3], 1)]:
+        n_q = np.array(n_q)
+        N = int(n_q.sum())
+        got = O.allocate_probes(n_q, M, N)
+        quotas = [M * n / N for n in n_q]
+        base = [math.floor(x) for x in quotas]
+        rema = sorted(range(len(n_q)), key=lambda a: (-(quotas[a] - base[a]), a))
+        for a in rema[:M - sum(base)]:
+            base[a] += 1
+        assert got.tolist() == base and got.sum() == M and np.all(got <= n_q)
+
+
+def test_select_probes_stratified_weights():
+    rng = np.random.default_rng(13)
+    N, C, M = 300, 9, 20
+    lab = rng.integers(0, C, N)
+    perm, off, cnt = O.group_permutation(lab, C)
+    idx, w = O.select_probes(0, 2, perm, off, cnt, M, N)
+    m = O.allocate_probes(cnt, M, N)
+    assert len(idx) == M and len(set(idx.tolist())) == M
+    assert np.isclose(w.sum(), M)
+    pos = 0
+    for a in range(C):
+        members = set(perm[off[a]:off[a + 1]].tolist())
+        chunk = idx[pos:pos + m[a]]
+        assert set(chunk.tolist()) <= members and np.all(np.diff(chunk) > 0)
+        if m[a]:
+            assert np.allclose(w[pos:pos + m[a]] * m[a] / cnt[a], w[pos] * m[a] / cnt[a])
+        pos += m[a]
+
+
+# ---------------------------------------------------------------- ridge
+def test_ridge_matches_lstsq_on_augmented_system():
+    rng = np.random.default_rng(14)
+    for M, d, lam, pb in [(40, 6, 0.3, False), (5, 8, 1e-3, False), (30, 4, 2.0, True)]:
+        o_sp = rng.standard_normal((M, d))
+        o_dn = o_sp + rng.standard_normal((M, d)) * 0.2
+        w = rng.uniform(0.5, 2.0, M)
+        th = O.ridge_fit(o_sp, o_dn, w, lam, pb)
+        Z = np.hstack([o_sp, np.ones((M, 1))])
+        reg = np.sqrt(lam) * np.eye(d + 1)
+        if not pb:
+            reg = reg[:d]
+        A = np.vstack([np.sqrt(w)[:, None] * Z, reg])
+        B = np.vstack([np.sqrt(w)[:, None] * (o_dn - o_sp), np.zeros((reg.shape[0], d))])
+        want = np.linalg.lstsq(A, B, rcond=None)[0]
+        np.testing.assert_allclose(th, want, rtol=1e-8, atol=1e-10)
+
+
+def test_ridge_recovers_planted_affine_map():
+    rng = np.random.default_rng(15)
+    M, d = 60, 8
+    o_sp = rng.standard_normal((M, d))
+    theta = rng.standard_normal((d + 1, d))
+    o_dn = o_sp + o_sp @ theta[:d] + theta[d]
+    got = O.ridge_fit(o_sp, o_dn, rng.uniform(0.5, 2, M), 1e-12)
+    np.testing.assert_allclose(got, theta, atol=1e-9)
+
+
+def test_ridge_interpolates_when_underdetermined():
+    rng = np.random.default_rng(16)
+    M, d = 6, 10
+    o_sp = rng.standard_normal((M, d))
+    o_dn = rng.standard_normal((M, d))
+    th = O.ridge_fit(o_sp, o_dn, np.ones(M), 1e-10)
+    fitted = o_sp @ th[:d] + th[d]
+    np.testing.assert_allclose(fitted, o_dn - o_sp, atol=1e-6)
+    # the prediction at any point lies in the span of the probe residuals (any lambda;
+    # a well-conditioned lambda keeps the check at round-off level)
+    R = o_dn - o_sp
+    th = O.ridge_fit(o_sp, o_dn, np.ones(M), 0.1)
+    pred = rng.standard_normal((4, d)) @ th[:d] + th[d]
+    coef = np.linalg.lstsq(R.T, pred.T, rcond=None)[0]
+    np.testing.assert_allclose(R.T @ coef, pred.T, atol=1e-8)
+
+
+def test_ridge_large_lambda_is_mean_only_correction():
+    # Table 4's mean-only family: with the bias unpenalised and lambda -> inf the map
+    # keeps only the weighted mean residual.
+    rng = np.random.default_rng(17)
+    M, d = 25, 5
+    o_sp = rng.standard_normal((M, d))
+    o_dn = rng.standard_normal((M, d))
+    w = rng.uniform(0.2, 3.0, M)
+    th = O.ridge_fit(o_sp, o_dn, w, 1e12)
+    assert np.abs(th[:d]).max() < 1e-9
+    np.testing.assert_allclose(th[d], (w[:, None] * (o_dn - o_sp)).sum(0) / w.sum(), atol=1e-9)
+
+
+def test_ridge_singular_system_is_a_numerical_error():
+    rng = np.random.default_rng(18)
+    o_sp = rng.standard_normal((4, 8))
+    with pytest.raises(O.NumericalError):
+        O.ridge_fit(o_sp, o_sp + 1, np.ones(4), 0.0)
+    assert np.all(O.ridge_fit(np.zeros((0, 8)), np.zeros((0, 8)), np.zeros(0), 1.0) == 0)
+
+
+def test_cholesky_matches_numpy():
+    rng = np.random.default_rng(19)
+    X = rng.standard_normal((20, 9))
+    A = X.T @ X + np.eye(9)
+    np.testing.assert_allclose(O.cholesky(A), np.linalg.cholesky(A), rtol=1e-12, atol=1e-12)
+
+
+# ---------------------------------------------------------------- metric and pages' numbers
+def test_rel_l2_formula():
+    out = np.array([[3.0, 4.0], [1.0, 1.0]])
+    ref = np.array([[0.0, 0.0], [1.0, 1.0]])
+    e = O.rel_l2(out, ref)
+    assert np.isclose(e[0], 5.0 / 1e-8) and e[1] == 0.0
+    e = O.rel_l2(np.array([[1.0, 2.0, 2.0]]), np.array([[0.0, 0.0, 0.0]]) + np.array([[1.0, 0.0, 0.0]]))
+    assert np.isclose(e[0], math.sqrt(8.0) / (1.0 + 1e-8))
+
+
+def test_error_stats_excludes_probes_and_uses_linear_p99():
+    ref = np.ones((101, 2))
+    out = ref.copy()
+    out[:, 0] += np.arange(101) / 100 * math.sqrt(2)      # e_i = i / 100
+    out[50, 0] += 100.0                                     # probe row: excluded
+    mean, p99 = O.error_stats(out, ref, [50])
+    rest = np.delete(np.arange(101) / 100, 50)
+    assert np.isclose(mean, rest.mean()) and np.isclose(p99, np.percentile(rest, 99))
+
+
+def test_table_c2_probe_fractions():
+    for _, n, pct in _rows("table_c2_probe_fraction.txt"):
+        assert round(100 * O.probe_fraction(64, int(n)), 3) == float(pct)
+
+
+def test_table2_error_reduction_matches_abstract_range():
+    rows = _rows("table2_error_reduction.txt")
+    reds = []
+    for r in rows:
+        if r[0] == "RANGE":
+            lo, hi = float(r[1]), float(r[2])
+            continue
+        red = round(100 * O.error_reduction(float(r[1]), float(r[2])), 1)
+        assert red == float(r[3])
+        reds.append(red)
+    assert (min(reds), max(reds)) == (lo, hi)
+
+
+# ---------------------------------------------------------------- whole call
+def _tiny_cfg(N=96, d=8):
+    return dict(scale=1 / math.sqrt(d), seed=0, n_sampled=12, n_key_groups=6, n_query_groups=5,
+                n_probes=7, density=0.3, ridge_lambda=1e-3)
+
+
+def test_full_density_call_is_dense_everywhere():
+    rng = np.random.default_rng(20)
+    N, d = 96, 8
+    q, k, v = (rng.standard_normal((N, d)) for _ in range(3))
+    p = _tiny_cfg(N, d)
+    p["density"] = 1.0 + p["n_probes"] / N
+    r = O.sparsepr_head(q, k, v, p, head=0)
+    dn = O.dense_attention(q, k, v, p["scale"])
+    np.testing.assert_allclose(r.o_sparse, dn, rtol=1e-12, atol=1e-12)
+    assert np.abs(r.theta).max() < 1e-12          # residuals are round-off only
+    np.testing.assert_allclose(r.out, dn, rtol=1e-12, atol=1e-12)
+
+
+def test_probe_rows_return_exact_dense_output():
+    rng = np.random.default_rng(21)
+    N, d = 96, 8
+    q, k, v = (rng.standard_normal((N, d)) for _ in range(3))
+    p = _tiny_cfg(N, d)
+    r = O.sparsepr_head(q, k, v, p, head=3)
+    dn = O.dense_attention(q, k, v, p["scale"])
+    assert len(r.plan.probes) == p["n_probes"]
+    assert np.array_equal(r.out[r.plan.probes], dn[r.plan.probes])
+    assert r.plan.pairs <= math.floor(p["density"] * N * N) or r.plan.route.budget_exceeded
+
+
+def test_single_group_partition_is_dense():
+    rng = np.random.default_rng(22)
+    N, d = 64, 8
+    q, k, v = (rng.standard_normal((N, d)) for _ in range(3))
+    p = dict(_tiny_cfg(N, d), n_key_groups=1, n_query_groups=1, density=0.1)
+    r = O.sparsepr_head(q, k, v, p, head=0)
+    np.testing.assert_allclose(r.o_sparse, O.dense_attention(q, k, v, p["scale"]), rtol=1e-12, atol=1e-12)
