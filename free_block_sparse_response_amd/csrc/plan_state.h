@@ -1,0 +1,97 @@
+// Device-side plan state of one SparsePR call: sizes and the workspace carve-up.
+// Every buffer is per flat head bh (B*H heads) and lives in the caller's workspace.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace spr {
+
+// Lloyd bookkeeping of one head (one k-means run).
+struct KmState {
+  int done_iter;   // iteration whose assignment is final (INT_MAX while running)
+  int iters;       // assignments run
+  int c_final;     // groups left after dropping empty ones
+  int pad;
+  double prev;     // inertia of the previous assignment
+};
+
+// Routing facts of one head.
+struct RouteInfo {
+  long long tau;
+  long long budget;
+  long long pairs;     // executed pairs including probe rows
+  int exceeded;
+  int pad;
+};
+
+struct Dims {
+  int BH, N, d, S, Ck, Cq, M;
+  int C;          // max(Ck, Cq): k-means scratch width
+  int nblk;       // Lloyd row blocks per head (kKmRows rows each)
+  int Npad;       // padded key count of the permuted K / transposed V
+  int qt;         // query rows per attention tile
+  int max_tiles;  // attention tiles per head, upper bound
+  int dtype;      // 0 f32, 1 bf16
+  float scale;
+  float log2_scale;  // scale * log2(e)
+  double density;
+  long long budget;
+  int max_iter;
+  float tol;
+  float lambda;
+  int pen_bias;
+  uint64_t seed;
+};
+
+struct Bufs {
+  int* sampled;      // [BH][S]
+  float* qs;         // [BH][S][d] gathered sampled queries
+  float* metric;     // [BH][d][d] Lloyd metric G
+  float* cent;       // [BH][C][d] Lloyd centroids (row space of X = alpha x)
+  float* cent_t;     // [BH][C][d] G m_b
+  float* cnorm;      // [BH][C]    m_b G m_b
+  float* alpha;      // [BH][N]    row scales of the query features
+  float* rowconst;   // [BH][N]    alpha^2 x G x
+  int* rank;         // [BH][N]    stable rank inside a Lloyd row block
+  int* tab;          // [BH][C][nblk] block counts -> scatter offsets
+  double* ipart;     // [BH][nblk] inertia partial sums
+  int* init_idx;     // [BH][C]
+  int* lab;          // [BH][N]    working labels
+  int* gstart;       // [BH][C+1]  working group starts
+  int* gcount;       // [BH][C]
+  KmState* kst;      // [BH] key run
+  KmState* qst;      // [BH] query run
+  int* klab;         // [BH][N]
+  int* kperm;        // [BH][N]
+  int* koff;         // [BH][Ck+1]
+  float* kcent;      // [BH][Ck][d] key-space centroids of the compacted groups
+  int* qlab;         // [BH][N]
+  int* qperm;        // [BH][N]
+  int* qoff;         // [BH][Cq+1]
+  long long* u;      // [BH][Cq][Ck] integer group masses
+  int* sorted_b;     // [BH][Cq][Ck]
+  long long* cum;    // [BH][Cq][Ck] prefix masses in sorted order
+  long long* ccost;  // [BH][Cq][Ck] prefix pair costs in sorted order
+  int* jsel;         // [BH][Cq]
+  int* row_ptr;      // [BH][Cq+1]
+  int* cols;         // [BH][Cq*Ck]
+  RouteInfo* rinfo;  // [BH]
+  int* pcount;       // [BH][Cq]
+  int* poff;         // [BH][Cq+1]
+  float* pw_group;   // [BH][Cq]
+  int* probes;       // [BH][M]
+  float* pweights;   // [BH][M]
+  int* pslot;        // [BH][N] probe slot of a token or -1
+  void* kp;          // [BH][Npad][d] keys in key-group order
+  void* vpt;         // [BH][d][Npad] values in key-group order, transposed
+  int2* tiles;       // [BH][max_tiles] (query group, first position)
+  int* ntiles;       // [BH]
+  double* gram;      // [BH][d+1][2d+1]  [A | B] of the ridge normal equations
+  int* status;       // [BH]
+};
+
+constexpr int kKmRows = 128;   // rows per Lloyd assignment block
+constexpr int kAttnQT = 128;   // query rows per attention tile (4 waves x 32)
+constexpr int kKeyTile = 64;   // keys per attention tile
+
+}  // namespace spr

@@ -109,6 +109,18 @@ def block_sparse_attention(q, k, v, scale, q_perm, q_off, k_perm, k_off, row_ptr
     return out
 
 
+def block_sparse_rows(q, k, v, scale, rows, q_labels, k_perm, k_off, row_ptr, cols):
+    """block_sparse_attention restricted to the query rows ``rows`` (same definition)."""
+    rows = np.asarray(rows, dtype=np.int64)
+    out = np.zeros((len(rows), v.shape[1]), dtype=np.float64)
+    groups = q_labels[rows]
+    for a in np.unique(groups):
+        sel = np.flatnonzero(groups == a)
+        keys = np.concatenate([k_perm[k_off[b]:k_off[b + 1]] for b in cols[row_ptr[a]:row_ptr[a + 1]]])
+        out[sel] = dense_attention(q[rows[sel]], k[keys], v[keys], scale)
+    return out
+
+
 # ----------------------------------------------------------------------------------
 # Lloyd k-means ([abstract]: keys grouped by their responses, queries grouped by
 # responses to key-group centroids; [C.1]: 25 initial iterations, tolerance 1e-4)
@@ -523,6 +535,22 @@ def attend_fit_apply(q, k, v, p, hp):
     theta = ridge_fit(o_sp[hp.probes], o_dn, hp.weights, p["ridge_lambda"], p.get("penalize_bias", False))
     out = apply_residual(o_sp, hp.probes, o_dn, theta)
     return HeadResult(plan=hp, o_sparse=o_sp, o_probe_dense=o_dn, theta=theta, out=out)
+
+
+def attend_fit_apply_rows(q, k, v, p, hp, rows):
+    """The call's output on the query rows ``rows`` only (probe rows are always computed)."""
+    s = p["scale"]
+    rt = hp.route
+    o_sp_pr = block_sparse_rows(q, k, v, s, hp.probes, hp.query_labels, hp.k_perm, hp.k_off, rt.row_ptr, rt.cols)
+    o_dn = dense_attention(q[hp.probes], k, v, s)
+    theta = ridge_fit(o_sp_pr, o_dn, hp.weights, p["ridge_lambda"], p.get("penalize_bias", False))
+    o_sp = block_sparse_rows(q, k, v, s, rows, hp.query_labels, hp.k_perm, hp.k_off, rt.row_ptr, rt.cols)
+    out = o_sp + o_sp @ theta[:-1] + theta[-1][None, :]
+    slot = {int(t): j for j, t in enumerate(hp.probes)}
+    for r, t in enumerate(np.asarray(rows)):
+        if int(t) in slot:
+            out[r] = o_dn[slot[int(t)]]
+    return dict(o_sparse=o_sp, o_probe_sparse=o_sp_pr, o_probe_dense=o_dn, theta=theta, out=out)
 
 
 def call_params(cfg):

@@ -1,0 +1,108 @@
+"""GPU parity: the HIP path against the CPU oracle, element by element.
+
+Integer products (labels, permutations, offsets, route, probes) must match bit for bit
+given the oracle's partition; float outputs must match per query within rel-L2 1e-4
+(fp32) or 2e-2 (bf16).
+"""
+import numpy as np
+import pytest
+import torch
+
+from free_block_sparse_response_amd import configs
+from oracle import sparsepr_oracle as O
+
+from gpu_helpers import (DEV, check_integer_plan, gpu_from_labels, inputs, max_rel, np_, oracle_heads, say)
+
+pytestmark = pytest.mark.gpu
+
+TOL = {"f32": 1e-4, "bf16": 2e-2}
+
+
+def _parity_from_labels(w, heads, **over):
+    say(f"case: from-labels {w['dtype']} N={configs.seq_len(w)} d={w['head_dim']} heads={heads} {over}")
+    (tq, q64), (tk, k64), (tv, v64) = inputs(w, heads)
+    refs = oracle_heads(w, q64, k64, v64, heads, **over)
+    sp = gpu_from_labels(w, tq, tk, tv, [r.plan for r in refs], **over)
+    check_integer_plan(sp, [r.plan for r in refs])
+    tol = TOL[w["dtype"]]
+    o_sp = np_(sp.o_sparse[0])
+    o_pr = np_(sp.o_probe[0])
+    o_psp = np_(sp.o_probe_sparse[0])
+    out = np_(sp.out[0])
+    for i, r in enumerate(refs):
+        M = len(r.plan.probes)
+        e_sp = max_rel(o_sp[i], r.o_sparse)
+        e_pr = max_rel(o_pr[i][:M], r.o_probe_dense)
+        e_psp = max_rel(o_psp[i][:M], r.o_sparse[r.plan.probes])
+        e_out = max_rel(out[i], r.out)
+        say(f"  head {heads[i]}: o_sparse {e_sp:.2e} probe sparse {e_psp:.2e} probe dense {e_pr:.2e} "
+            f"out {e_out:.2e}")
+        assert e_sp <= tol and e_pr <= tol and e_out <= tol and e_psp <= tol
+        # probe rows carry their exact dense output (bit-equal to the probe buffer)
+        assert np.array_equal(out[i][r.plan.probes], o_pr[i][:M].astype(out.dtype)) or w["dtype"] == "bf16"
+    return sp, refs
+
+
+def test_c1_fp32_from_labels():
+    _parity_from_labels(configs.CONFIGS["c1"], [0])
+
+
+def test_c1_fp32_d128_ragged():
+    w = configs.with_overrides("c1", grid=(3, 15, 17), head_dim=128, heads=2)
+    _parity_from_labels(w, [0, 1])
+
+
+def test_c2_bf16_two_heads_from_labels():
+    w = configs.CONFIGS["c2"]
+    _parity_from_labels(w, [0, 5])
+
+
+def test_bf16_d64_ragged_small():
+    w = configs.with_overrides("c2", grid=(5, 13, 19), head_dim=64, heads=3, n_sampled=64, n_key_groups=24,
+                               n_query_groups=20, n_probes=40, density=0.3)
+    _parity_from_labels(w, [0, 1, 2])
+
+
+def test_full_density_is_dense():
+    w = configs.CONFIGS["c1"]
+    N = configs.seq_len(w)
+    sp, refs = _parity_from_labels(w, [0], density=1.0 + w["n_probes"] / N)
+    dn = O.dense_attention(*[x for x in _dense_inputs(w)], 1 / 8.0)
+    assert max_rel(np_(sp.o_sparse[0][0]), dn) <= 1e-4
+
+
+def _dense_inputs(w):
+    (_, q64), (_, k64), (_, v64) = inputs(w, [0])
+    return q64[0], k64[0], v64[0]
+
+
+def test_tight_budget_keeps_top1_and_flags():
+    w = configs.CONFIGS["c1"]
+    sp, refs = _parity_from_labels(w, [0], density=0.02)
+    assert refs[0].plan.route.budget_exceeded
+    assert sp.info()[0]["budget_exceeded"] == 1
+
+
+def test_single_groups_equal_dense():
+    w = configs.with_overrides("c1", n_key_groups=1, n_query_groups=1)
+    sp, refs = _parity_from_labels(w, [0])
+    q, k, v = _dense_inputs(w)
+    assert max_rel(np_(sp.o_sparse[0][0]), O.dense_attention(q, k, v, 1 / 8.0)) <= 1e-4
+
+
+def test_dense_entry_point_matches_oracle():
+    for w in (configs.CONFIGS["c1"], configs.with_overrides("c2", heads=2, grid=(4, 16, 16))):
+        say(f"case: dense {w['dtype']}")
+        (tq, q64), (tk, k64), (tv, v64) = inputs(w, [0, 1][: w["heads"]])
+        from free_block_sparse_response_amd.call import SparsePR, config_from_workload
+
+        sp = SparsePR(config_from_workload(w), device=DEV)
+        out = torch.empty_like(tq)
+        sp.dense(tq, tk, tv, out)
+        torch.cuda.synchronize()
+        o = np_(out[0])
+        for i in range(w["heads"]):
+            ref = O.dense_attention(q64[i], k64[i], v64[i], 1 / np.sqrt(w["head_dim"]))
+            e = max_rel(o[i], ref)
+            say(f"  head {i}: dense rel-L2 {e:.2e}")
+            assert e <= TOL[w["dtype"]] / 2

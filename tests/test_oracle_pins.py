@@ -524,3 +524,16 @@ def test_single_group_partition_is_dense():
     p = dict(_tiny_cfg(N, d), n_key_groups=1, n_query_groups=1, density=0.1)
     r = O.sparsepr_head(q, k, v, p, head=0)
     np.testing.assert_allclose(r.o_sparse, O.dense_attention(q, k, v, p["scale"]), rtol=1e-12, atol=1e-12)
+
+
+def test_row_subset_entry_matches_whole_call():
+    rng = np.random.default_rng(23)
+    N, d = 96, 8
+    q, k, v = (rng.standard_normal((N, d)) for _ in range(3))
+    p = _tiny_cfg(N, d)
+    r = O.sparsepr_head(q, k, v, p, head=1)
+    rows = np.array([0, 5, 17, 40, 95] + list(r.plan.probes[:2]))
+    sub = O.attend_fit_apply_rows(q, k, v, p, r.plan, rows)
+    np.testing.assert_allclose(sub["o_sparse"], r.o_sparse[rows], rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(sub["theta"], r.theta, rtol=1e-9, atol=1e-12)
+    np.testing.assert_allclose(sub["out"], r.out[rows], rtol=1e-9, atol=1e-12)
