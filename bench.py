@@ -1,0 +1,190 @@
+#!/usr/bin/env python3
+"""Benchmark of the SparsePR attention call on one MI355X.
+
+One step = one whole call (plan: key and query k-means, masses, routing, probes; attend:
+permutation, block-sparse attention, probe attention; ridge fit; apply) over all heads of
+the workload, on seeded synthetic inputs already resident in HBM. Prints ONE JSON line.
+
+  python bench.py [--steps K] [--warmup W] [--config c2] [--no-cpu-baseline]
+  python bench.py --copy-calibration      # plain device copy of a known size (for PMC scaling)
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "dense-equiv attention TFLOP/s + call latency at 22-26% density; mean rel-L2 err"
+HBM_PEAK_GBS = 8000.0
+BF16_MFMA_PEAK_TFLOPS = 2500.0
+FP32_VECTOR_PEAK_TFLOPS = 157.3
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--config", default="c2")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-sample-heads", type=int, default=2)
+    ap.add_argument("--copy-calibration", action="store_true")
+    return ap.parse_args()
+
+
+def copy_calibration():
+    """Copies 1 GiB device-to-device three times; FETCH_SIZE / WRITE_SIZE of that kernel
+    against the known 1 GiB give the counters' scale."""
+    import torch
+
+    n = 1 << 29  # bf16 elements = 1 GiB
+    src = torch.ones(n, dtype=torch.bfloat16, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes": 2 * n, "launches": 3}))
+
+
+def cpu_baseline(w, q64, k64, v64, heads):
+    """The oracle, untuned, on a bounded sample of the workload's heads (host cores)."""
+    from threadpoolctl import threadpool_info
+
+    from oracle import sparsepr_oracle as O
+
+    p = O.call_params(w)
+    t0 = time.perf_counter()
+    for i in range(heads):
+        O.sparsepr_head(q64[i], k64[i], v64[i], p, head=i)
+    dt = time.perf_counter() - t0
+    N, d = q64.shape[1], q64.shape[2]
+    threads = max([t.get("num_threads", 1) for t in threadpool_info()] or [1])
+    return {"value": 4.0 * N * N * d * heads / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads),
+            "kind": "oracle", "sample": f"{heads} of {w['batch'] * w['heads']} heads of the workload at full N "
+            f"(float64 NumPy; {dt:.1f} s, {dt / heads:.2f} s per head; the rate extrapolates per head)",
+            "seconds_per_head": dt / heads, "host_cpus": len(os.sched_getaffinity(0))}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only: the SparsePR call's heads are independent and this build "
+              f"measures one GPU's share; --gpus {args.gpus} is not supported.", file=sys.stderr)
+        sys.exit(2)
+    if args.copy_calibration:
+        copy_calibration()
+        return
+    import numpy as np
+    import torch
+
+    from free_block_sparse_response_amd import _lib as L
+    from free_block_sparse_response_amd import configs, synth
+    from free_block_sparse_response_amd.call import SparsePR, config_from_workload
+
+    w = configs.CONFIGS[args.config]
+    N, d, BH, M = configs.seq_len(w), w["head_dim"], w["batch"] * w["heads"], w["n_probes"]
+    dev = torch.device("cuda:0")
+    t0 = time.perf_counter()
+    q64, k64, v64 = synth.make_inputs(w)
+    tq, tk, tv = (synth.cast_to_dtype(x, w["dtype"])[0].reshape(w["batch"], w["heads"], N, d).to(dev)
+                  for x in (q64, k64, v64))
+    log(f"inputs {args.config}: B*H={BH} N={N} d={d} {w['dtype']} ({time.perf_counter() - t0:.1f} s)")
+
+    sp = SparsePR(config_from_workload(w), device=dev)
+    L.sparsepr_set_stage_timing(sp.plan_h, 1)
+    for _ in range(args.warmup):
+        sp(tq, tk, tv)
+    torch.cuda.synchronize()
+    L.sparsepr_stage_times(sp.plan_h)  # discard warm-up samples
+    stream = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for _ in range(args.steps):
+        sp(tq, tk, tv)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms_step = e0.elapsed_time(e1) / args.steps
+    stage = L.sparsepr_stage_times(sp.plan_h)
+    info = sp.info()
+
+    # dense attention with the same kernels, same inputs (baseline and error reference)
+    spd = SparsePR(config_from_workload(w), device=dev)
+    dense = torch.empty_like(tq)
+    spd.dense(tq, tk, tv, dense)
+    torch.cuda.synchronize()
+    d0, d1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    dsteps = max(3, args.steps // 2)
+    d0.record(stream)
+    for _ in range(dsteps):
+        spd.dense(tq, tk, tv, dense)
+    d1.record(stream)
+    torch.cuda.synchronize()
+    ms_dense = d0.elapsed_time(d1) / dsteps
+
+    # error of the call (and of the sparse output alone) against dense, unprobed rows
+    probes = sp.export("PROBES").long()
+    mask = torch.ones((BH, N), dtype=torch.bool, device=dev)
+    mask.scatter_(1, probes, False)
+    ref = dense.reshape(BH, N, d).float()
+
+    def err(x):
+        e = (x.reshape(BH, N, d).float() - ref).norm(dim=-1) / (ref.norm(dim=-1) + 1e-8)
+        e = e[mask].double()
+        return float(e.mean()), float(torch.quantile(e.float(), 0.99))
+
+    err_mean, err_p99 = err(sp.out)
+    sp_mean, sp_p99 = err(sp.o_sparse)
+
+    pairs = np.array([i["executed_pairs"] for i in info], dtype=np.float64)
+    cell_pairs = pairs - M * N
+    dense_flop = 4.0 * BH * N * N * d
+    value = dense_flop / (ms_step * 1e-3) / 1e12
+    # dominant kernel: block-sparse attention, logical executed pairs of the selected cells
+    bsfa_flop = 4.0 * d * cell_pairs.sum()
+    bsfa_ms = stage["sparse"]
+    bsfa_tflops = bsfa_flop / (bsfa_ms * 1e-3) / 1e12
+    roofline = {"kernel": "k_bsfa_bf16 (block-sparse attention)" if w["dtype"] == "bf16" else "k_bsfa_f32",
+                "bound": "mfma" if w["dtype"] == "bf16" else "alu", "achieved": round(bsfa_tflops, 2),
+                "peak": BF16_MFMA_PEAK_TFLOPS if w["dtype"] == "bf16" else FP32_VECTOR_PEAK_TFLOPS,
+                "unit": "TFLOP/s", "frac": None, "traffic": None,
+                "flop_per_launch": bsfa_flop, "ms_per_launch": round(bsfa_ms, 4)}
+    roofline["frac"] = round(roofline["achieved"] / roofline["peak"], 4)
+    probe_flop = 4.0 * d * M * N * BH
+    result = {
+        "metric": METRIC, "value": round(value, 3), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms_step, 4), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": w["dtype"],
+        "data": "synthetic (seeded clustered spatio-temporal mixture; stands in for video-model activations)",
+        "config": {"workload": f"{args.config}: B={w['batch']} H={w['heads']} N={N} d={d} S={w['n_sampled']} "
+                               f"C_k={w['n_key_groups']} C_q={w['n_query_groups']} M={M} rho={w['density']}",
+                   "batch": w["batch"], "heads": w["heads"], "seq_len": N, "head_dim": d, "density": w["density"],
+                   "parallelism": "single GPU (heads independent)"},
+        "call_latency_ms": round(ms_step, 4), "dense_ms": round(ms_dense, 4),
+        "speedup_vs_dense": round(ms_dense / ms_step, 3),
+        "realised_density": round(float(pairs.sum() / (BH * N * N)), 5),
+        "err_mean": round(err_mean, 5), "err_p99": round(err_p99, 5),
+        "sparse_only_err_mean": round(sp_mean, 5), "sparse_only_err_p99": round(sp_p99, 5),
+        "stage_ms": {k: round(v, 4) for k, v in stage.items()},
+        "probe_attention_tflops": round(probe_flop / max(stage["probes"], 1e-9) / 1e9, 2),
+        "kmeans_iters": [[i["key_iters"], i["query_iters"]] for i in info],
+        "roofline": roofline,
+    }
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(w, q64, k64, v64, min(args.cpu_sample_heads, BH))
+    print(json.dumps(result))
+
+
+if __name__ == "__main__":
+    main()

@@ -58,8 +58,11 @@ _SIGS = {
     "sparsepr_plan_info": (ctypes.c_int, [_P, ctypes.POINTER(sparsepr_head_info), ctypes.c_int32, _P]),
     "sparsepr_export_bytes": (_SZ, [_P, ctypes.c_int32]),
     "sparsepr_plan_export": (ctypes.c_int, [_P, ctypes.c_int32, _P, _SZ, _P]),
+    "sparsepr_set_stage_timing": (ctypes.c_int, [_P, ctypes.c_int32]),
+    "sparsepr_stage_times": (ctypes.c_int, [_P, ctypes.POINTER(ctypes.c_float), ctypes.c_int32]),
     "sparsepr_status_string": (ctypes.c_char_p, [ctypes.c_int]),
 }
+STAGES = ("plan", "permute", "sparse", "probes", "fit", "apply")
 SYMBOLS = tuple(_SIGS)
 
 
@@ -185,6 +188,16 @@ def sparsepr_plan_export(plan, which, dst, stream=None):
     w = EXPORT.get(which, which)
     _check("sparsepr_plan_export", lib().sparsepr_plan_export(plan, w, _ptr(dst), dst.numel() * dst.element_size(),
                                                               _stream(stream)))
+
+
+def sparsepr_set_stage_timing(plan, enable):
+    _check("sparsepr_set_stage_timing", lib().sparsepr_set_stage_timing(plan, int(enable)))
+
+
+def sparsepr_stage_times(plan):
+    arr = (ctypes.c_float * len(STAGES))()
+    _check("sparsepr_stage_times", lib().sparsepr_stage_times(plan, arr, len(STAGES)))
+    return dict(zip(STAGES, list(arr)))
 
 
 def sparsepr_status_string(status):

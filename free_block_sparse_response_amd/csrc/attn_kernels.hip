@@ -359,38 +359,35 @@ __global__ __launch_bounds__(128) void k_bsfa_f32(const float* __restrict__ q, D
   }
 }
 
-template <int DD>
-static void attend_bf16(const void* q, const Dims& D, const Bufs& B, void* o_sparse, float* o_psp, float* o_pdn,
-                        hipStream_t s) {
+void launch_attend_sparse(const void* q, const Dims& D, const Bufs& B, void* o_sparse, float* o_psp, hipStream_t s) {
   const int nb = D.BH * D.max_tiles;
-  hipLaunchKernelGGL((k_bsfa_bf16<DD, 0>), dim3(nb), dim3(256), 0, s, (const bf16*)q, D, B, o_sparse, o_psp);
-  if (D.M > 0 && o_pdn) {
-    const int nbp = D.BH * ((D.M + kAttnQT - 1) / kAttnQT);
-    hipLaunchKernelGGL((k_bsfa_bf16<DD, 1>), dim3(nbp), dim3(256), 0, s, (const bf16*)q, D, B, (void*)o_pdn,
-                       (float*)nullptr);
-  }
-}
-
-template <int DD>
-static void attend_f32(const void* q, const Dims& D, const Bufs& B, void* o_sparse, float* o_psp, float* o_pdn,
-                       hipStream_t s) {
-  const int nb = D.BH * D.max_tiles;
-  hipLaunchKernelGGL((k_bsfa_f32<DD, 0>), dim3(nb), dim3(128), 0, s, (const float*)q, D, B, o_sparse, o_psp);
-  if (D.M > 0 && o_pdn) {
-    const int nbp = D.BH * ((D.M + kAttnQT - 1) / kAttnQT);
-    hipLaunchKernelGGL((k_bsfa_f32<DD, 1>), dim3(nbp), dim3(128), 0, s, (const float*)q, D, B, (void*)o_pdn,
-                       (float*)nullptr);
-  }
-}
-
-void launch_attend(const void* q, const Dims& D, const Bufs& B, void* o_sparse, float* o_psp, float* o_pdn,
-                   hipStream_t s) {
   if (D.dtype == 1) {
-    if (D.d == 128) attend_bf16<128>(q, D, B, o_sparse, o_psp, o_pdn, s);
-    else attend_bf16<64>(q, D, B, o_sparse, o_psp, o_pdn, s);
+    if (D.d == 128)
+      hipLaunchKernelGGL((k_bsfa_bf16<128, 0>), dim3(nb), dim3(256), 0, s, (const bf16*)q, D, B, o_sparse, o_psp);
+    else
+      hipLaunchKernelGGL((k_bsfa_bf16<64, 0>), dim3(nb), dim3(256), 0, s, (const bf16*)q, D, B, o_sparse, o_psp);
   } else {
-    if (D.d == 128) attend_f32<128>(q, D, B, o_sparse, o_psp, o_pdn, s);
-    else attend_f32<64>(q, D, B, o_sparse, o_psp, o_pdn, s);
+    if (D.d == 128)
+      hipLaunchKernelGGL((k_bsfa_f32<128, 0>), dim3(nb), dim3(128), 0, s, (const float*)q, D, B, o_sparse, o_psp);
+    else
+      hipLaunchKernelGGL((k_bsfa_f32<64, 0>), dim3(nb), dim3(128), 0, s, (const float*)q, D, B, o_sparse, o_psp);
+  }
+}
+
+void launch_attend_probes(const void* q, const Dims& D, const Bufs& B, float* o_pdn, hipStream_t s) {
+  if (D.M == 0 || !o_pdn) return;
+  const int nb = D.BH * ((D.M + kAttnQT - 1) / kAttnQT);
+  float* none = nullptr;
+  if (D.dtype == 1) {
+    if (D.d == 128)
+      hipLaunchKernelGGL((k_bsfa_bf16<128, 1>), dim3(nb), dim3(256), 0, s, (const bf16*)q, D, B, (void*)o_pdn, none);
+    else
+      hipLaunchKernelGGL((k_bsfa_bf16<64, 1>), dim3(nb), dim3(256), 0, s, (const bf16*)q, D, B, (void*)o_pdn, none);
+  } else {
+    if (D.d == 128)
+      hipLaunchKernelGGL((k_bsfa_f32<128, 1>), dim3(nb), dim3(128), 0, s, (const float*)q, D, B, (void*)o_pdn, none);
+    else
+      hipLaunchKernelGGL((k_bsfa_f32<64, 1>), dim3(nb), dim3(128), 0, s, (const float*)q, D, B, (void*)o_pdn, none);
   }
 }
 

@@ -11,8 +11,9 @@ void launch_plan_from_labels(const void* q, const void* k, const int* klab, cons
 void launch_route_probes(const Dims& D, const Bufs& B, hipStream_t s);
 void launch_identity_plan(const Dims& D, const Bufs& B, hipStream_t s);
 void launch_permute_kv(const void* k, const void* v, const Dims& D, const Bufs& B, hipStream_t s);
-void launch_attend(const void* q, const Dims& D, const Bufs& B, void* o_sparse, float* o_probe_sparse,
-                   float* o_probe_dense, hipStream_t s);
+void launch_attend_sparse(const void* q, const Dims& D, const Bufs& B, void* o_sparse, float* o_probe_sparse,
+                          hipStream_t s);
+void launch_attend_probes(const void* q, const Dims& D, const Bufs& B, float* o_probe_dense, hipStream_t s);
 void launch_fit(const Dims& D, const Bufs& B, const float* o_psp, const float* o_dn, const float* w, float* coeffs,
                 hipStream_t s);
 void launch_apply(const Dims& D, const Bufs& B, const void* o_sp, const float* o_dn, const float* coeffs, void* out,

@@ -18,13 +18,38 @@ void launch_fill_i32(int* p, long long n, int v, hipStream_t s);
 using spr::Bufs;
 using spr::Dims;
 
+constexpr int kTimingRing = 64;
+
 struct sparsepr_plan_s {
   sparsepr_config cfg;
   Dims D;
   size_t ws_bytes;
   void* ws;
   int planned;  // 1 after sparsepr_plan / sparsepr_plan_from_labels on the bound workspace
+  int timing;   // stage events enabled
+  // ring of kTimingRing (begin, end) event pairs per stage; count = calls recorded since
+  // the last sparsepr_stage_times (the ring keeps the most recent kTimingRing of them)
+  hipEvent_t ev[SPARSEPR_NUM_STAGES][kTimingRing][2];
+  int count[SPARSEPR_NUM_STAGES];
 };
+
+namespace {
+// Stage timing guard: records the begin / end events of a stage when timing is on.
+struct StageTimer {
+  sparsepr_plan_s* p;
+  int st;
+  hipStream_t s;
+  StageTimer(sparsepr_plan_s* p_, int st_, hipStream_t s_) : p(p_), st(st_), s(s_) {
+    if (p->timing) (void)hipEventRecord(p->ev[st][p->count[st] % kTimingRing][0], s);
+  }
+  ~StageTimer() {
+    if (p->timing) {
+      (void)hipEventRecord(p->ev[st][p->count[st] % kTimingRing][1], s);
+      ++p->count[st];
+    }
+  }
+};
+}  // namespace
 
 namespace {
 
@@ -175,11 +200,60 @@ sparsepr_status sparsepr_plan_create(const sparsepr_config* cfg, sparsepr_plan_t
   carve(D, nullptr, &p->ws_bytes);
   p->ws = nullptr;
   p->planned = 0;
+  p->timing = 0;
   *out = p;
   return SPARSEPR_OK;
 }
 
-void sparsepr_plan_destroy(sparsepr_plan_t plan) { delete plan; }
+static void destroy_events(sparsepr_plan_t p, int upto) {
+  hipEvent_t* e = &p->ev[0][0][0];
+  for (int i = 0; i < upto; ++i) (void)hipEventDestroy(e[i]);
+}
+
+void sparsepr_plan_destroy(sparsepr_plan_t plan) {
+  if (!plan) return;
+  if (plan->timing) destroy_events(plan, SPARSEPR_NUM_STAGES * kTimingRing * 2);
+  delete plan;
+}
+
+sparsepr_status sparsepr_set_stage_timing(sparsepr_plan_t p, int32_t enable) {
+  if (!p) return SPARSEPR_ERR_INVALID_ARG;
+  if (enable && !p->timing) {
+    hipEvent_t* e = &p->ev[0][0][0];
+    const int n = SPARSEPR_NUM_STAGES * kTimingRing * 2;
+    for (int i = 0; i < n; ++i) {
+      if (hipEventCreate(&e[i]) != hipSuccess) {
+        destroy_events(p, i);
+        return SPARSEPR_ERR_HIP;
+      }
+    }
+    for (int i = 0; i < SPARSEPR_NUM_STAGES; ++i) p->count[i] = 0;
+    p->timing = 1;
+  } else if (!enable && p->timing) {
+    destroy_events(p, SPARSEPR_NUM_STAGES * kTimingRing * 2);
+    p->timing = 0;
+  }
+  return SPARSEPR_OK;
+}
+
+sparsepr_status sparsepr_stage_times(sparsepr_plan_t p, float* ms, int32_t n) {
+  if (!p || !ms || n < 1 || n > SPARSEPR_NUM_STAGES) return SPARSEPR_ERR_INVALID_ARG;
+  if (!p->timing) return SPARSEPR_ERR_STATE;
+  for (int i = 0; i < n; ++i) {
+    ms[i] = 0.f;
+    const int c = p->count[i] < kTimingRing ? p->count[i] : kTimingRing;
+    double tot = 0.0;
+    for (int j = 0; j < c; ++j) {
+      float t = 0.f;
+      if (hipEventSynchronize(p->ev[i][j][1]) != hipSuccess) return SPARSEPR_ERR_HIP;
+      if (hipEventElapsedTime(&t, p->ev[i][j][0], p->ev[i][j][1]) != hipSuccess) return SPARSEPR_ERR_HIP;
+      tot += t;
+    }
+    ms[i] = c ? (float)(tot / c) : 0.f;
+  }
+  for (int i = 0; i < SPARSEPR_NUM_STAGES; ++i) p->count[i] = 0;
+  return SPARSEPR_OK;
+}
 
 size_t sparsepr_workspace_bytes(sparsepr_plan_t plan) { return plan ? plan->ws_bytes : 0; }
 
@@ -200,8 +274,11 @@ sparsepr_status sparsepr_plan(sparsepr_plan_t p, const void* q, const void* k, v
   Bufs B;
   sparsepr_status st = begin_plan(p, ws, bytes, &B, s);
   if (st != SPARSEPR_OK) return st;
-  spr::launch_plan(q, k, p->D, B, s);
-  spr::launch_route_probes(p->D, B, s);
+  {
+    StageTimer t(p, SPARSEPR_STAGE_PLAN, s);
+    spr::launch_plan(q, k, p->D, B, s);
+    spr::launch_route_probes(p->D, B, s);
+  }
   st = hip_status();
   if (st == SPARSEPR_OK) p->planned = 1;
   return st;
@@ -215,8 +292,11 @@ sparsepr_status sparsepr_plan_from_labels(sparsepr_plan_t p, const void* q, cons
   Bufs B;
   sparsepr_status st = begin_plan(p, ws, bytes, &B, s);
   if (st != SPARSEPR_OK) return st;
-  spr::launch_plan_from_labels(q, k, key_labels, query_labels, (const long long*)group_mass, p->D, B, s);
-  spr::launch_route_probes(p->D, B, s);
+  {
+    StageTimer t(p, SPARSEPR_STAGE_PLAN, s);
+    spr::launch_plan_from_labels(q, k, key_labels, query_labels, (const long long*)group_mass, p->D, B, s);
+    spr::launch_route_probes(p->D, B, s);
+  }
   st = hip_status();
   if (st == SPARSEPR_OK) p->planned = 1;
   return st;
@@ -229,8 +309,18 @@ sparsepr_status sparsepr_attend(sparsepr_plan_t p, const void* q, const void* k,
   if (!p->planned) return SPARSEPR_ERR_STATE;
   hipStream_t s = (hipStream_t)stream;
   Bufs B = carve(p->D, p->ws, nullptr);
-  spr::launch_permute_kv(k, v, p->D, B, s);
-  spr::launch_attend(q, p->D, B, o_sparse, o_probe_sparse, o_probe_dense, s);
+  {
+    StageTimer t(p, SPARSEPR_STAGE_PERMUTE, s);
+    spr::launch_permute_kv(k, v, p->D, B, s);
+  }
+  {
+    StageTimer t(p, SPARSEPR_STAGE_SPARSE, s);
+    spr::launch_attend_sparse(q, p->D, B, o_sparse, o_probe_sparse, s);
+  }
+  {
+    StageTimer t(p, SPARSEPR_STAGE_PROBES, s);
+    spr::launch_attend_probes(q, p->D, B, o_probe_dense, s);
+  }
   return hip_status();
 }
 
@@ -241,6 +331,7 @@ sparsepr_status sparsepr_fit_residual(sparsepr_plan_t p, const float* o_probe_sp
   if (!p->planned) return SPARSEPR_ERR_STATE;
   hipStream_t s = (hipStream_t)stream;
   Bufs B = carve(p->D, p->ws, nullptr);
+  StageTimer t(p, SPARSEPR_STAGE_FIT, s);
   spr::launch_fit(p->D, B, o_probe_sparse, o_probe_dense, probe_weights, coeffs, s);
   return hip_status();
 }
@@ -252,6 +343,7 @@ sparsepr_status sparsepr_apply(sparsepr_plan_t p, const void* o_sparse, const fl
   if (!p->planned) return SPARSEPR_ERR_STATE;
   hipStream_t s = (hipStream_t)stream;
   Bufs B = carve(p->D, p->ws, nullptr);
+  StageTimer t(p, SPARSEPR_STAGE_APPLY, s);
   spr::launch_apply(p->D, B, o_sparse, o_probe_dense, coeffs, out, s);
   return hip_status();
 }
@@ -267,7 +359,7 @@ sparsepr_status sparsepr_dense_attention(sparsepr_plan_t p, const void* q, const
   Bufs B = carve(p->D, ws, nullptr);
   spr::launch_identity_plan(p->D, B, s);
   spr::launch_permute_kv(k, v, p->D, B, s);
-  spr::launch_attend(q, p->D, B, out, nullptr, nullptr, s);
+  spr::launch_attend_sparse(q, p->D, B, out, nullptr, s);
   return hip_status();
 }
 

@@ -173,6 +173,23 @@ size_t sparsepr_export_bytes(sparsepr_plan_t plan, int32_t which);
 sparsepr_status sparsepr_plan_export(sparsepr_plan_t plan, int32_t which, void* dst, size_t dst_bytes,
                                      void* stream);
 
+/* Per-stage timing (for benchmarks). When enabled, every later call records a pair of HIP
+ * events around each stage on its stream. sparsepr_stage_times waits for the recorded
+ * events and returns, per stage, the mean elapsed milliseconds over the calls since the
+ * previous sparsepr_stage_times (the most recent 64 of them), then starts a new count.
+ * Enabling creates HIP events (needs a device); disabling destroys them. */
+typedef enum {
+  SPARSEPR_STAGE_PLAN = 0,     /* sparsepr_plan / sparsepr_plan_from_labels                   */
+  SPARSEPR_STAGE_PERMUTE = 1,  /* group-contiguous K and transposed V                         */
+  SPARSEPR_STAGE_SPARSE = 2,   /* block-sparse attention kernel                               */
+  SPARSEPR_STAGE_PROBES = 3,   /* exact attention of the probe rows                           */
+  SPARSEPR_STAGE_FIT = 4,      /* ridge normal equations and Cholesky solve                   */
+  SPARSEPR_STAGE_APPLY = 5,    /* residual apply                                              */
+  SPARSEPR_NUM_STAGES = 6
+} sparsepr_stage;
+sparsepr_status sparsepr_set_stage_timing(sparsepr_plan_t plan, int32_t enable);
+sparsepr_status sparsepr_stage_times(sparsepr_plan_t plan, float* ms, int32_t n);
+
 const char* sparsepr_status_string(sparsepr_status s);
 
 #ifdef __cplusplus

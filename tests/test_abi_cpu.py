@@ -93,6 +93,10 @@ def test_workspace_size_and_host_side_errors(lib):
         assert lib.sparsepr_fit_residual(h, fake, fake, None, fake, None) == L.SPARSEPR_ERR_STATE
         assert lib.sparsepr_apply(h, fake, fake, fake, fake, None) == L.SPARSEPR_ERR_STATE
         assert lib.sparsepr_plan_export(h, 0, fake, 1 << 20, None) == L.SPARSEPR_ERR_STATE
+        ms = (ctypes.c_float * 6)()
+        assert lib.sparsepr_stage_times(h, ms, 6) == L.SPARSEPR_ERR_STATE
+        assert lib.sparsepr_stage_times(h, ms, 7) == L.SPARSEPR_ERR_INVALID_ARG
+        assert lib.sparsepr_set_stage_timing(None, 1) == L.SPARSEPR_ERR_INVALID_ARG
         info = (L.sparsepr_head_info * 2)()
         assert lib.sparsepr_plan_info(h, info, 2, None) == L.SPARSEPR_ERR_STATE
         assert lib.sparsepr_plan_info(h, info, 3, None) == L.SPARSEPR_ERR_INVALID_ARG
