@@ -14,6 +14,8 @@
 // G_k = C_k^T C_k. The assignment therefore needs score_b = m_b G m_b - 2 x.(G m_b) over
 // d-wide rows instead of S- or C_k-wide ones; the labels are those of Lloyd on the
 // response rows themselves.
+#include <type_traits>
+
 #include "common.h"
 #include "plan_state.h"
 #include "launch.h"
@@ -82,12 +84,33 @@ template <int BT, typename Cand>
 __device__ void select_smallest(int n, int m, Cand cand, uint64_t base, int* out) {
   __shared__ int hist[256];
   __shared__ uint64_t s_prefix;
-  __shared__ int s_k;
+  __shared__ int s_k, s_alleq;
   __shared__ int ws[BT / kWave];
+  __shared__ uint64_t ch[BT];
+  __shared__ int ci[BT];
   const int tid = threadIdx.x;
   if (m <= 0) return;
   if (m >= n) {
     for (int i = tid; i < n; i += BT) out[i] = cand(i);
+    return;
+  }
+  if (n <= BT) {
+    // direct ranks: candidate i is chosen iff fewer than m candidates precede it in (hash, id)
+    const bool valid = tid < n;
+    const int id = valid ? cand(tid) : 0;
+    const uint64_t h = valid ? splitmix64(base ^ (uint64_t)(uint32_t)id) : 0ull;
+    if (valid) {
+      ch[tid] = h;
+      ci[tid] = id;
+    }
+    __syncthreads();
+    int rank = 0;
+    if (valid)
+      for (int j = 0; j < n; ++j) rank += (ch[j] < h) || (ch[j] == h && ci[j] < id);
+    int tot;
+    const bool sel = valid && rank < m;
+    const int pos = block_excl_scan_bool<BT>(sel, &tot, ws);
+    if (sel) out[pos] = id;
     return;
   }
   uint64_t prefix = 0;
@@ -102,43 +125,61 @@ __device__ void select_smallest(int n, int m, Cand cand, uint64_t base, int* out
       if ((h & hi_mask) == prefix) atomicAdd(&hist[(h >> shift) & 255], 1);
     }
     __syncthreads();
-    if (tid == 0) {
-      int c = 0, dg = 0;
-      for (dg = 0; dg < 255; ++dg) {
-        if (c + hist[dg] >= k) break;
-        c += hist[dg];
+    if (tid < kWave) {
+      // the lane whose 4 bins hold the k-th candidate picks the digit
+      const int c0 = hist[4 * tid], c1 = hist[4 * tid + 1], c2 = hist[4 * tid + 2], c3 = hist[4 * tid + 3];
+      const int loc = c0 + c1 + c2 + c3;
+      const int inc = wave_incl_scan(loc), exc = inc - loc;
+      if (exc < k && inc >= k) {
+        int c = exc, dg, cnt;
+        if (c + c0 >= k) { dg = 4 * tid; cnt = c0; }
+        else if ((c += c0) + c1 >= k) { dg = 4 * tid + 1; cnt = c1; }
+        else if ((c += c1) + c2 >= k) { dg = 4 * tid + 2; cnt = c2; }
+        else { c += c2; dg = 4 * tid + 3; cnt = c3; }
+        s_prefix = prefix | ((uint64_t)dg << shift);
+        s_k = k - c;
+        s_alleq = (k - c) == cnt;
       }
-      s_prefix = prefix | ((uint64_t)dg << shift);
-      s_k = k - c;
     }
     __syncthreads();
     prefix = s_prefix;
     k = s_k;
     __syncthreads();
   }
+  // prefix = T, the m-th smallest hash; take every h < T and the first k ids with h == T
+  const bool alleq = s_alleq;
   int run_sel = 0, run_eq = 0;
   for (int c0 = 0; c0 < n; c0 += BT) {
     const int i = c0 + tid;
     const bool valid = i < n;
     const int id = valid ? cand(i) : 0;
     const uint64_t h = valid ? splitmix64(base ^ (uint64_t)(uint32_t)id) : 0ull;
-    const bool lt = valid && h < prefix;
-    const bool eq = valid && h == prefix;
-    int eq_tot, sel_tot;
-    const int eq_rank = block_excl_scan_bool<BT>(eq, &eq_tot, ws) + run_eq;
-    const bool sel = lt || (eq && eq_rank < k);
+    int sel_tot;
+    bool sel;
+    if (alleq) {
+      sel = valid && h <= prefix;
+    } else {
+      int eq_tot;
+      const bool eq = valid && h == prefix;
+      const int eq_rank = block_excl_scan_bool<BT>(eq, &eq_tot, ws) + run_eq;
+      sel = (valid && h < prefix) || (eq && eq_rank < k);
+      run_eq += eq_tot;
+    }
     const int pos = block_excl_scan_bool<BT>(sel, &sel_tot, ws) + run_sel;
     if (sel) out[pos] = id;
-    run_eq += eq_tot;
     run_sel += sel_tot;
   }
 }
 
-__global__ __launch_bounds__(1024) void k_select_all(int N, int m, uint64_t seed, uint64_t stream,
-                                                     int* out, int out_stride) {
-  const int bh = blockIdx.x;
-  const uint64_t base = head_hash_base(seed, stream, (uint64_t)bh);
-  select_smallest<1024>(N, m, [](int i) { return i; }, base, out + (size_t)bh * out_stride);
+// The three whole-sequence selections of a plan in one launch: blockIdx.y = 0 sampled
+// queries (stream 1), 1 key-group seeds (stream 2), 2 query-group seeds (stream 3).
+__global__ __launch_bounds__(1024) void k_select_all(Dims D, Bufs B) {
+  const int bh = blockIdx.x, which = blockIdx.y;
+  const int m = which == 0 ? D.S : (which == 1 ? D.Ck : D.Cq);
+  int* out = which == 0 ? B.sampled + (size_t)bh * D.S
+                        : (which == 1 ? B.init_k + (size_t)bh * D.Ck : B.init_q + (size_t)bh * D.Cq);
+  const uint64_t base = head_hash_base(D.seed, (uint64_t)(which + 1), (uint64_t)bh);
+  select_smallest<1024>(D.N, m, [](int i) { return i; }, base, out);
 }
 
 // Probe rows of query group a: m_a members with the smallest (hash, token id).
@@ -172,37 +213,37 @@ __global__ void k_gather_rows(const T* x, const int* idx, int N, int S, int d, f
   for (int i = threadIdx.x; i < d; i += blockDim.x) out[((size_t)bh * S + t) * d + i] = to_f32(src[i]);
 }
 
-// G = scale2 * sum_r rows_r^T rows_r over the first count rows (count from KmState when given).
+// G = scale2 * sum_r rows_r^T rows_r over the first count rows (count from KmState when
+// given). Block (gi, bh) owns G rows [RG*gi, RG*gi + RG): one entry per thread.
 template <int DD>
 __global__ __launch_bounds__(256) void k_gram(const float* rows, int R, const KmState* cnt_state, float scale2,
-                                              float* G) {
-  constexpr int E = DD * DD / 256;
+                                              float* G, bf16* Gh, bf16* Gl) {
+  constexpr int RG = 256 / DD;
   constexpr int CH = 32;
   __shared__ float sh[CH][DD];
-  const int bh = blockIdx.x;
+  const int gi = blockIdx.x, bh = blockIdx.y;
   const int n = cnt_state ? cnt_state[bh].c_final : R;
   const float* src = rows + (size_t)bh * R * DD;
-  float acc[E];
-#pragma unroll
-  for (int e = 0; e < E; ++e) acc[e] = 0.f;
+  const int i = gi * RG + threadIdx.x / DD, j = threadIdx.x % DD;
+  float acc = 0.f;
   for (int r0 = 0; r0 < n; r0 += CH) {
     __syncthreads();
-    for (int i = threadIdx.x; i < CH * DD; i += 256) {
-      const int r = i / DD, c = i % DD;
-      sh[r][c] = (r0 + r < n) ? src[(size_t)(r0 + r) * DD + c] : 0.f;
+    for (int e = threadIdx.x; e < CH * DD / 4; e += 256) {
+      const int r = e / (DD / 4), c4 = (e % (DD / 4)) * 4;
+      float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+      if (r0 + r < n) v = *reinterpret_cast<const float4*>(src + (size_t)(r0 + r) * DD + c4);
+      *reinterpret_cast<float4*>(&sh[r][c4]) = v;
     }
     __syncthreads();
     const int rmax = min(CH, n - r0);
-    for (int r = 0; r < rmax; ++r) {
-#pragma unroll
-      for (int e = 0; e < E; ++e) {
-        const int idx = threadIdx.x + 256 * e;
-        acc[e] += sh[r][idx / DD] * sh[r][idx % DD];
-      }
-    }
+    for (int r = 0; r < rmax; ++r) acc = fmaf(sh[r][i], sh[r][j], acc);
   }
-#pragma unroll
-  for (int e = 0; e < E; ++e) G[(size_t)bh * DD * DD + threadIdx.x + 256 * e] = scale2 * acc[e];
+  const float g = scale2 * acc;
+  const size_t o = (size_t)bh * DD * DD + (size_t)i * DD + j;
+  G[o] = g;
+  const bf16 gh = (bf16)g;
+  Gh[o] = gh;
+  Gl[o] = (bf16)(g - (float)gh);
 }
 
 // =====================================================================================
@@ -304,30 +345,42 @@ __global__ __launch_bounds__(256) void k_rowquad(const T* x, Dims D, const float
 // =====================================================================================
 // Lloyd iteration kernels (one run per head, all heads at once)
 // =====================================================================================
-// m_b = alpha x_{init_b}; also resets the run state.
+// m_b = alpha x_{init_b}; G m_b and m_b G m_b; item b = 0 also resets the run state.
+// Block of 256 threads; the first DD carry one coordinate each.
 template <typename T, int DD>
-__global__ __launch_bounds__(DD) void k_km_init(const T* x, Dims D, Bufs B, int C, KmState* st) {
-  const int b = blockIdx.x, bh = blockIdx.y, i = threadIdx.x;
+__device__ void km_init_item(const T* x, const Dims& D, const Bufs& B, int C, const int* init, KmState* st, int b,
+                             int bh) {
   __shared__ float m[DD];
-  __shared__ float red[DD / kWave];
-  const int row = B.init_idx[(size_t)bh * D.C + b];
-  float a = B.alpha ? B.alpha[(size_t)bh * D.N + row] : 1.f;
-  const float v = a * to_f32(x[((size_t)bh * D.N + row) * DD + i]);
-  m[i] = v;
+  __shared__ float red[4];
+  const int i = threadIdx.x;
+  const int row = init[(size_t)bh * C + b];
+  float v = 0.f;
+  if (i < DD) {
+    const float a = B.alpha ? B.alpha[(size_t)bh * D.N + row] : 1.f;
+    v = a * to_f32(x[((size_t)bh * D.N + row) * DD + i]);
+    m[i] = v;
+  }
   __syncthreads();
-  const float* G = B.metric + (size_t)bh * DD * DD;
-  float t = 0.f;
-  for (int k = 0; k < DD; ++k) t = fmaf(G[(size_t)k * DD + i], m[k], t);
-  const size_t o = ((size_t)bh * D.C + b) * DD + i;
-  B.cent[o] = v;
-  B.cent_t[o] = t;
-  float p = wave_sum(v * t);
+  float p = 0.f;
+  if (i < DD) {
+    const float* G = B.metric + (size_t)bh * DD * DD;
+    float t = 0.f;
+    for (int k = 0; k < DD; ++k) t = fmaf(G[(size_t)k * DD + i], m[k], t);
+    const size_t o = ((size_t)bh * D.C + b) * DD + i;
+    B.cent[o] = v;
+    B.cent_t[o] = t;
+    const bf16 th = (bf16)t;
+    B.cent_h[o] = th;
+    B.cent_l[o] = (bf16)(t - (float)th);
+    p = v * t;
+  }
+  p = wave_sum(p);
   if (lane_id() == 0) red[i / kWave] = p;
   __syncthreads();
   if (i == 0) {
-    float s = 0.f;
-    for (int w = 0; w < DD / kWave; ++w) s += red[w];
-    B.cnorm[(size_t)bh * D.C + b] = s;
+    float sum = 0.f;
+    for (int w = 0; w < DD / kWave; ++w) sum += red[w];
+    B.cnorm[(size_t)bh * D.C + b] = sum;
     if (b == 0) {
       st[bh].done_iter = 0x7fffffff;
       st[bh].iters = 0;
@@ -335,6 +388,79 @@ __global__ __launch_bounds__(DD) void k_km_init(const T* x, Dims D, Bufs B, int 
       st[bh].prev = 0.0;
     }
   }
+  __syncthreads();
+}
+
+template <typename T, int DD>
+__global__ __launch_bounds__(256) void k_km_init(const T* x, Dims D, Bufs B, int C, const int* init, KmState* st) {
+  km_init_item<T, DD>(x, D, B, C, init, st, blockIdx.x, blockIdx.y);
+}
+
+// Scatter offsets, split in two launches. Per (group b, head): one wave turns the block
+// counts tab[b][blk] into exclusive prefixes over the blocks and writes the group size.
+__global__ __launch_bounds__(64) void k_km_scan_groups(Dims D, Bufs B, int C, KmState* st, int t) {
+  const int b = blockIdx.x, bh = blockIdx.y;
+  if (st[bh].done_iter < t) return;
+  const int l = lane_id();
+  int* tab = B.tab + ((size_t)bh * D.C + b) * D.nblk;
+  int run = 0;
+  for (int i0 = 0; i0 < D.nblk; i0 += kWave) {
+    const int i = i0 + l;
+    const int c = i < D.nblk ? tab[i] : 0;
+    const int inc = wave_incl_scan(c);
+    if (i < D.nblk) tab[i] = run + inc - c;
+    run += __shfl(inc, kWave - 1, kWave);
+  }
+  if (l == 0) B.gcount[(size_t)bh * D.C + b] = run;
+}
+
+// Per head: the inertia of this assignment, the stopping rule, and the group starts.
+// Thread i owns groups [4i, 4i + 4).
+__global__ __launch_bounds__(256) void k_km_scan_head(Dims D, Bufs B, int C, KmState* st, int t) {
+  constexpr int LPT = kMaxGroups / 256;
+  __shared__ long long wsl[4];
+  const int bh = blockIdx.x;
+  if (st[bh].done_iter < t) return;
+  const int tid = threadIdx.x, w = tid / kWave, l = lane_id();
+  long long loc[LPT], run = 0;
+#pragma unroll
+  for (int j = 0; j < LPT; ++j) {
+    const int b = tid * LPT + j;
+    loc[j] = run;
+    run += b < C ? B.gcount[(size_t)bh * D.C + b] : 0;
+  }
+  long long tot;
+  const long long base = block_excl_scan<256, long long>(run, &tot, wsl);
+#pragma unroll
+  for (int j = 0; j < LPT; ++j) {
+    const int b = tid * LPT + j;
+    if (b < C) B.gstart[(size_t)bh * (D.C + 1) + b] = (int)(base + loc[j]);
+  }
+  if (tid == 0) B.gstart[(size_t)bh * (D.C + 1) + C] = (int)tot;
+  if (w == 0) {
+    double sum = 0.0;
+    for (int i = l; i < D.nblk; i += kWave) sum += B.ipart[(size_t)bh * D.nblk + i];
+    sum = wave_sum(sum);
+    if (l == 0) {
+      const double prev = st[bh].prev;
+      int done = st[bh].done_iter;
+      if (t > 1 && prev - sum <= (double)D.tol * prev) done = t;
+      if (t >= D.max_iter) done = t;
+      st[bh].done_iter = done;
+      st[bh].prev = sum;
+      st[bh].iters = t;
+    }
+  }
+}
+
+__device__ inline void km_scatter_item(const Dims& D, const Bufs& B, KmState* st, int t, int* perm, int blk, int bh) {
+  if (st[bh].done_iter < t) return;
+  const int row = blk * kKmRows + threadIdx.x;
+  if (threadIdx.x >= kKmRows || row >= D.N) return;
+  const int lab = B.lab[(size_t)bh * D.N + row];
+  const int pos = B.gstart[(size_t)bh * (D.C + 1) + lab] + B.tab[((size_t)bh * D.C + lab) * D.nblk + blk] +
+                  B.rank[(size_t)bh * D.N + row];
+  perm[(size_t)bh * D.N + pos] = row;
 }
 
 // Assignment of iteration t: nearest centroid (ties to the lower id) of 128 rows, the
@@ -421,98 +547,66 @@ __global__ __launch_bounds__(256) void k_km_assign(const T* x, Dims D, Bufs B, i
   for (int i = threadIdx.x; i < C; i += 256) tab[(size_t)i * D.nblk + blk] = hist[i];
 }
 
-// Per head: inertia, the stopping rule, group sizes and starts, per-(group, block)
-// scatter offsets.
-__global__ __launch_bounds__(1024) void k_km_scan(Dims D, Bufs B, int C, KmState* st, int t) {
-  __shared__ long long wsl[16];
-  __shared__ int gs[kMaxGroups];
-  const int bh = blockIdx.x;
-  if (st[bh].done_iter < t) return;
-  const int w = threadIdx.x / kWave, l = lane_id();
-  int* tab = B.tab + (size_t)bh * D.C * D.nblk;
-  if (w == 0) {
-    double s = 0.0;
-    for (int i = l; i < D.nblk; i += kWave) s += B.ipart[(size_t)bh * D.nblk + i];
-    s = wave_sum(s);
-    if (l == 0) {
-      const double prev = st[bh].prev;
-      int done = st[bh].done_iter;
-      if (t > 1 && prev - s <= (double)D.tol * prev) done = t;
-      if (t >= D.max_iter) done = t;
-      st[bh].done_iter = done;
-      st[bh].prev = s;
-      st[bh].iters = t;
-    }
-  }
-  for (int b = w; b < C; b += 16) {
-    int s = 0;
-    for (int i = l; i < D.nblk; i += kWave) s += tab[(size_t)b * D.nblk + i];
-    s = wave_sum_i(s);
-    if (l == 0) gs[b] = s;
-  }
-  __syncthreads();
-  long long tot;
-  const long long cnt = threadIdx.x < C ? gs[threadIdx.x] : 0;
-  const long long start = block_excl_scan<1024, long long>(cnt, &tot, wsl);
-  if (threadIdx.x < C) {
-    B.gcount[(size_t)bh * D.C + threadIdx.x] = (int)cnt;
-    B.gstart[(size_t)bh * (D.C + 1) + threadIdx.x] = (int)start;
-  }
-  if (threadIdx.x == 0) B.gstart[(size_t)bh * (D.C + 1) + C] = (int)tot;
-  __syncthreads();
-  if (threadIdx.x < C) gs[threadIdx.x] = (int)start;
-  __syncthreads();
-  for (int b = w; b < C; b += 16) {
-    int run = gs[b];
-    for (int i0 = 0; i0 < D.nblk; i0 += kWave) {
-      const int i = i0 + l;
-      const int c = i < D.nblk ? tab[(size_t)b * D.nblk + i] : 0;
-      const int inc = wave_incl_scan(c);
-      if (i < D.nblk) tab[(size_t)b * D.nblk + i] = run + inc - c;
-      run += __shfl(inc, kWave - 1, kWave);
-    }
-  }
-}
 
 __global__ __launch_bounds__(kKmRows) void k_km_scatter(Dims D, Bufs B, KmState* st, int t, int* perm) {
-  const int blk = blockIdx.x, bh = blockIdx.y;
-  if (st[bh].done_iter < t) return;
-  const int row = blk * kKmRows + threadIdx.x;
-  if (row >= D.N) return;
-  const int lab = B.lab[(size_t)bh * D.N + row];
-  const int pos = B.tab[((size_t)bh * D.C + lab) * D.nblk + blk] + B.rank[(size_t)bh * D.N + row];
-  perm[(size_t)bh * D.N + pos] = row;
+  km_scatter_item(D, B, st, t, perm, blockIdx.x, blockIdx.y);
 }
 
-// Mean of the rows alpha_j x_j of group b, summed in group order; optionally G m_b and m_b G m_b.
+// Mean of the rows alpha_j x_j of a group, listed by `members` (group order). 256 threads:
+// each 16-byte load covers EV elements, a row takes LPR lanes, RS rows are in flight per
+// pass. Row r always lands in slot r % RS and the slots are summed in a fixed order, so the
+// result does not depend on scheduling.
 template <typename T, int DD>
 __device__ void group_mean(const T* xb, const float* alpha, const int* members, int n, float* m_out,
-                           float* sh /* [256] */) {
-  constexpr int RL = 256 / DD;  // row lanes
-  const int c = threadIdx.x % DD, rl = threadIdx.x / DD;
-  float s = 0.f;
-  for (int r = rl; r < n; r += RL) {
-    const int row = members[r];
-    float v = to_f32(xb[(size_t)row * DD + c]);
-    if (alpha) v *= alpha[row];
-    s += v;
+                           float* sh /* [256 / (DD / (16 / sizeof(T)))][DD] */) {
+  constexpr int EV = 16 / sizeof(T);
+  constexpr int LPR = DD / EV;
+  constexpr int RS = 256 / LPR;
+  const int slot = threadIdx.x / LPR, c0 = (threadIdx.x % LPR) * EV;
+  float acc[EV];
+#pragma unroll
+  for (int e = 0; e < EV; ++e) acc[e] = 0.f;
+  auto add_row = [&](const uint4& raw, float a) {
+    const T* v = reinterpret_cast<const T*>(&raw);
+#pragma unroll
+    for (int e = 0; e < EV; ++e) acc[e] = fmaf(a, to_f32(v[e]), acc[e]);
+  };
+  int r = slot;
+  for (; r + 3 * RS < n; r += 4 * RS) {
+    int rows[4];
+    uint4 raw[4];
+    float al[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) rows[u] = members[r + u * RS];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      raw[u] = *reinterpret_cast<const uint4*>(xb + (size_t)rows[u] * DD + c0);
+      al[u] = alpha ? alpha[rows[u]] : 1.f;
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) add_row(raw[u], al[u]);
   }
-  sh[threadIdx.x] = s;
+  for (; r < n; r += RS) {
+    const int row = members[r];
+    add_row(*reinterpret_cast<const uint4*>(xb + (size_t)row * DD + c0), alpha ? alpha[row] : 1.f);
+  }
+#pragma unroll
+  for (int e = 0; e < EV; ++e) sh[slot * DD + c0 + e] = acc[e];
   __syncthreads();
   if (threadIdx.x < DD) {
     float tot = 0.f;
-    for (int q = 0; q < RL; ++q) tot += sh[q * DD + threadIdx.x];
+    for (int q = 0; q < RS; ++q) tot += sh[q * DD + threadIdx.x];
     m_out[threadIdx.x] = tot / (float)n;
   }
   __syncthreads();
 }
 
 template <typename T, int DD>
-__global__ __launch_bounds__(256) void k_km_update(const T* x, Dims D, Bufs B, KmState* st, int t, const int* perm) {
-  __shared__ float sh[256];
+__device__ void km_update_item(const T* x, const Dims& D, const Bufs& B, KmState* st, int t, const int* perm, int b,
+                               int bh) {
+  __shared__ float sh[2048];
   __shared__ float m[DD];
   __shared__ float red[4];
-  const int b = blockIdx.x, bh = blockIdx.y;
   if (st[bh].done_iter <= t) return;
   const int n = B.gcount[(size_t)bh * D.C + b];
   if (n == 0) return;  // empty cluster keeps its centroid
@@ -522,23 +616,44 @@ __global__ __launch_bounds__(256) void k_km_update(const T* x, Dims D, Bufs B, K
   group_mean<T, DD>(xb, alpha, perm + (size_t)bh * D.N + s0, n, m, sh);
   const float* G = B.metric + (size_t)bh * DD * DD;
   float p = 0.f;
-  if (threadIdx.x < DD) {
-    const int i = threadIdx.x;
+  {
+    // G m: threads i and i + DD (, ...) take interleaved parts of k; combined in order
+    constexpr int KH = 256 / DD;
+    const int i = threadIdx.x % DD, part = threadIdx.x / DD;
+    float gv[DD / KH];
+#pragma unroll
+    for (int kk = 0; kk < DD / KH; ++kk) gv[kk] = G[(size_t)(part + kk * KH) * DD + i];
     float tt = 0.f;
-    for (int k = 0; k < DD; ++k) tt = fmaf(G[(size_t)k * DD + i], m[k], tt);
-    const size_t o = ((size_t)bh * D.C + b) * DD + i;
-    B.cent[o] = m[i];
-    B.cent_t[o] = tt;
-    p = m[i] * tt;
+#pragma unroll
+    for (int kk = 0; kk < DD / KH; ++kk) tt = fmaf(gv[kk], m[part + kk * KH], tt);
+    sh[threadIdx.x] = tt;
+    __syncthreads();
+    if (threadIdx.x < DD) {
+      float tot = 0.f;
+      for (int q = 0; q < KH; ++q) tot += sh[q * DD + i];
+      const size_t o = ((size_t)bh * D.C + b) * DD + i;
+      B.cent[o] = m[i];
+      B.cent_t[o] = tot;
+      const bf16 th = (bf16)tot;
+      B.cent_h[o] = th;
+      B.cent_l[o] = (bf16)(tot - (float)th);
+      p = m[i] * tot;
+    }
   }
   p = wave_sum(p);
   if (lane_id() == 0) red[threadIdx.x / kWave] = p;
   __syncthreads();
   if (threadIdx.x == 0) {
-    float s = 0.f;
-    for (int w = 0; w < DD / kWave; ++w) s += red[w];
-    B.cnorm[(size_t)bh * D.C + b] = s;
+    float sum = 0.f;
+    for (int w = 0; w < DD / kWave; ++w) sum += red[w];
+    B.cnorm[(size_t)bh * D.C + b] = sum;
   }
+  __syncthreads();
+}
+
+template <typename T, int DD>
+__global__ __launch_bounds__(256) void k_km_update(const T* x, Dims D, Bufs B, KmState* st, int t, const int* perm) {
+  km_update_item<T, DD>(x, D, B, st, t, perm, blockIdx.x, blockIdx.y);
 }
 
 // Drop empty groups: compacted labels, offsets and the realised group count.
@@ -567,14 +682,344 @@ __global__ __launch_bounds__(1024) void k_km_compact(Dims D, Bufs B, int C, KmSt
 // Key-space centroid of each compacted key group (raw keys, group order).
 template <typename T, int DD>
 __global__ __launch_bounds__(256) void k_key_centroids(const T* k, Dims D, Bufs B) {
-  __shared__ float sh[256];
+  __shared__ float sh[2048];
   __shared__ float m[DD];
   const int b = blockIdx.x, bh = blockIdx.y;
   if (b >= B.kst[bh].c_final) return;
   const int* off = B.koff + (size_t)bh * (D.Ck + 1);
   const int s0 = off[b], n = off[b + 1] - off[b];
   group_mean<T, DD>(k + (size_t)bh * D.N * DD, nullptr, B.kperm + (size_t)bh * D.N + s0, n, m, sh);
-  if (threadIdx.x < DD) B.kcent[((size_t)bh * D.Ck + b) * DD + threadIdx.x] = m[threadIdx.x];
+  if (threadIdx.x < DD) {
+    const size_t o = ((size_t)bh * D.Ck + b) * DD + threadIdx.x;
+    const float v = m[threadIdx.x];
+    B.kcent[o] = v;
+    const bf16 vh = (bf16)v;
+    B.kcent_h[o] = vh;
+    B.kcent_l[o] = (bf16)(v - (float)vh);
+  }
+}
+
+// =====================================================================================
+// bf16 inputs: the same products on the matrix cores. A small float matrix Y (centroids,
+// metric, key centroids) is split as Y = hi + lo with hi, lo bf16, so hi.x + lo.x carries
+// ~16 significant bits of Y against the exact bf16 row x. Products are taken transposed,
+// acc = Y_block x^T with v_mfma_f32_32x32x16_bf16, so lane l owns row (l % 32) and holds
+// 16 of the 32 Y rows: Y row 8(v/4) + 4(l/32) + (v%4) in acc[v].
+// =====================================================================================
+template <int DD>
+__device__ inline void load_row_operand(const bf16* xrow, bf16x8* xr) {
+  const int h = lane_id() >> 5;
+#pragma unroll
+  for (int c = 0; c < DD / 16; ++c) xr[c] = *reinterpret_cast<const bf16x8*>(xrow + 16 * c + 8 * h);
+}
+
+// Y rows [r0, r0 + R) (float, row stride DD) -> Yh / Yl (bf16, row stride DD + 8); zero past nrows.
+template <int DD, int R>
+__device__ inline void stage_hilo(const float* Y, int r0, int nrows, bf16* Yh, bf16* Yl) {
+  constexpr int KS = DD + 8;
+  for (int e = threadIdx.x; e < R * DD / 4; e += blockDim.x) {
+    const int r = e / (DD / 4), c4 = (e % (DD / 4)) * 4;
+    float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (r0 + r < nrows) v = *reinterpret_cast<const float4*>(Y + (size_t)(r0 + r) * DD + c4);
+    const float f[4] = {v.x, v.y, v.z, v.w};
+    bf16x4 hv, lv;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const bf16 hb = (bf16)f[q];
+      hv[q] = hb;
+      lv[q] = (bf16)(f[q] - (float)hb);
+    }
+    *reinterpret_cast<bf16x4*>(&Yh[r * KS + c4]) = hv;
+    *reinterpret_cast<bf16x4*>(&Yl[r * KS + c4]) = lv;
+  }
+}
+
+// Rows [r0, r0 + R) of a bf16 hi/lo pair (row stride DD) -> Yh / Yl (row stride DD + 8); zero past nrows.
+template <int DD, int R>
+__device__ inline void copy_hilo(const bf16* Sh, const bf16* Sl, int r0, int nrows, bf16* Yh, bf16* Yl) {
+  constexpr int KS = DD + 8;
+  for (int e = threadIdx.x; e < R * DD / 8; e += blockDim.x) {
+    const int r = e / (DD / 8), c8 = (e % (DD / 8)) * 8;
+    bf16x8 hv, lv;
+    if (r0 + r < nrows) {
+      hv = *reinterpret_cast<const bf16x8*>(Sh + (size_t)(r0 + r) * DD + c8);
+      lv = *reinterpret_cast<const bf16x8*>(Sl + (size_t)(r0 + r) * DD + c8);
+    } else {
+#pragma unroll
+      for (int q = 0; q < 8; ++q) { hv[q] = (bf16)0.f; lv[q] = (bf16)0.f; }
+    }
+    *reinterpret_cast<bf16x8*>(&Yh[r * KS + c8]) = hv;
+    *reinterpret_cast<bf16x8*>(&Yl[r * KS + c8]) = lv;
+  }
+}
+
+template <int DD>
+__device__ inline f32x16 mfma_rows(const bf16* Yh, const bf16* Yl, int y0, const bf16x8* xr) {
+  constexpr int KS = DD + 8;
+  const int l32 = lane_id() & 31, h = lane_id() >> 5;
+  f32x16 acc;
+#pragma unroll
+  for (int v = 0; v < 16; ++v) acc[v] = 0.f;
+#pragma unroll
+  for (int c = 0; c < DD / 16; ++c) {
+    const bf16x8 ah = *reinterpret_cast<const bf16x8*>(&Yh[(y0 + l32) * KS + 16 * c + 8 * h]);
+    acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah, xr[c], acc, 0, 0, 0);
+    const bf16x8 al = *reinterpret_cast<const bf16x8*>(&Yl[(y0 + l32) * KS + 16 * c + 8 * h]);
+    acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(al, xr[c], acc, 0, 0, 0);
+  }
+  return acc;
+}
+
+__device__ inline int acc_row(int v) { return 8 * (v >> 2) + 4 * (lane_id() >> 5) + (v & 3); }
+
+// Stable in-block rank and histogram of the labels of one 128-row counting-sort block
+// (labels in lab_s[0..127]); run by threads 0..127, rows 0..63 in wave 0 and 64..127 in 1.
+__device__ inline void km_rank_block(const Dims& D, const Bufs& B, int C, int bh, int blk, const int* lab_s,
+                                     int* hist) {
+  const int tid = threadIdx.x, w = tid / kWave;
+  const int r0 = blk * kKmRows;
+  for (int i = tid; i < C; i += blockDim.x) hist[i] = 0;
+  __syncthreads();
+  const bool rvalid = tid < kKmRows && r0 + tid < D.N;
+  const int lab = tid < kKmRows ? lab_s[tid] : 0;
+  uint64_t mask = 0;
+  if (w < 2) mask = wave_match(lab, rvalid, 10);
+  const int rin = __popcll(mask & lanemask_lt());
+  const bool leader = rvalid && rin == 0;
+  if (w == 0 && leader) hist[lab] = __popcll(mask);
+  __syncthreads();
+  int rank = rin;
+  if (w == 1 && rvalid) rank += hist[lab];
+  __syncthreads();
+  if (w == 1 && leader) hist[lab] += __popcll(mask);
+  if (rvalid) B.rank[(size_t)bh * D.N + r0 + tid] = rank;
+  __syncthreads();
+  int* tab = B.tab + (size_t)bh * D.C * D.nblk;
+  for (int i = tid; i < C; i += blockDim.x) tab[(size_t)i * D.nblk + blk] = hist[i];
+  __syncthreads();
+}
+
+// Assignment of iteration t for 128*RS rows: each of the 4 waves owns RS sets of 32 rows, so
+// every centroid operand read from LDS feeds RS products. Centroid operands (G m_b as
+// bf16 hi + lo) are copied 64 at a time into LDS.
+template <int DD, int RS>
+__global__ __launch_bounds__(256) void k_km_assign_bf16(const bf16* x, Dims D, Bufs B, int C, KmState* st, int t) {
+  constexpr int CB = 64, KS = DD + 8, NB = kKmRows * RS;
+  __shared__ __attribute__((aligned(16))) bf16 Yh[CB * KS];
+  __shared__ __attribute__((aligned(16))) bf16 Yl[CB * KS];
+  __shared__ float cns[CB];
+  __shared__ int lab_s[NB];
+  __shared__ double dred[NB];
+  __shared__ int hist[kMaxGroups];
+  const int sb0 = blockIdx.x * RS, bh = blockIdx.y;  // first 128-row sort block
+  if (st[bh].done_iter < t) return;
+  const int tid = threadIdx.x, w = tid / kWave, l32 = lane_id() & 31, h = lane_id() >> 5;
+  const int r0 = sb0 * kKmRows;
+  bf16x8 xr[RS][DD / 16];
+  float a2[RS], best[RS];
+  int bidx[RS];
+#pragma unroll
+  for (int rs = 0; rs < RS; ++rs) {
+    const int row = r0 + 128 * rs + 32 * w + l32;
+    const bool valid = row < D.N;
+    load_row_operand<DD>(x + ((size_t)bh * D.N + (valid ? row : D.N - 1)) * DD, xr[rs]);
+    a2[rs] = 2.f * (B.alpha ? B.alpha[(size_t)bh * D.N + (valid ? row : 0)] : 1.f);
+    best[rs] = INFINITY;
+    bidx[rs] = 0x7fffffff;
+  }
+  const bf16* Ch = B.cent_h + (size_t)bh * D.C * DD;
+  const bf16* Cl = B.cent_l + (size_t)bh * D.C * DD;
+  const float* cn = B.cnorm + (size_t)bh * D.C;
+  for (int c0 = 0; c0 < C; c0 += CB) {
+    __syncthreads();
+    copy_hilo<DD, CB>(Ch, Cl, c0, C, Yh, Yl);
+    if (tid < CB) cns[tid] = c0 + tid < C ? cn[c0 + tid] : 0.f;
+    __syncthreads();
+#pragma unroll
+    for (int yb = 0; yb < CB; yb += 32) {
+      f32x16 acc[RS];
+#pragma unroll
+      for (int rs = 0; rs < RS; ++rs)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) acc[rs][v] = 0.f;
+#pragma unroll
+      for (int c = 0; c < DD / 16; ++c) {
+        const bf16x8 ah = *reinterpret_cast<const bf16x8*>(&Yh[(yb + l32) * KS + 16 * c + 8 * h]);
+        const bf16x8 al = *reinterpret_cast<const bf16x8*>(&Yl[(yb + l32) * KS + 16 * c + 8 * h]);
+#pragma unroll
+        for (int rs = 0; rs < RS; ++rs) {
+          acc[rs] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah, xr[rs][c], acc[rs], 0, 0, 0);
+          acc[rs] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(al, xr[rs][c], acc[rs], 0, 0, 0);
+        }
+      }
+#pragma unroll
+      for (int rs = 0; rs < RS; ++rs)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const int cl = yb + acc_row(v), col = c0 + cl;
+          const float sc = fmaf(-a2[rs], acc[rs][v], cns[cl]);
+          if (col < C && (sc < best[rs] || (sc == best[rs] && col < bidx[rs]))) { best[rs] = sc; bidx[rs] = col; }
+        }
+    }
+  }
+#pragma unroll
+  for (int rs = 0; rs < RS; ++rs) {
+    const float ob = __shfl_xor(best[rs], 32, kWave);
+    const int oi = __shfl_xor(bidx[rs], 32, kWave);
+    if (ob < best[rs] || (ob == best[rs] && oi < bidx[rs])) { best[rs] = ob; bidx[rs] = oi; }
+    const int lrow = 128 * rs + 32 * w + l32, row = r0 + lrow;
+    const bool valid = row < D.N;
+    if (h == 0) {
+      lab_s[lrow] = valid ? bidx[rs] : 0;
+      dred[lrow] = valid ? (double)B.rowconst[(size_t)bh * D.N + row] + (double)best[rs] : 0.0;
+      if (valid) B.lab[(size_t)bh * D.N + row] = bidx[rs];
+    }
+  }
+  __syncthreads();
+  for (int sb = 0; sb < RS && sb0 + sb < D.nblk; ++sb) {
+    double* dr = dred + 128 * sb;
+    for (int sz = kKmRows / 2; sz > 0; sz >>= 1) {
+      if (tid < sz) dr[tid] += dr[tid + sz];
+      __syncthreads();
+    }
+    if (tid == 0) B.ipart[(size_t)bh * D.nblk + sb0 + sb] = dr[0];
+    km_rank_block(D, B, C, bh, sb0 + sb, lab_s + 128 * sb, hist);
+  }
+}
+
+// Row constants (see k_rowquad) on the matrix cores: (G x)_i for 32 dims at a time, dotted
+// with x in the lane that owns the row.
+template <int DD>
+__global__ __launch_bounds__(256) void k_rowquad_bf16(const bf16* x, Dims D, const bf16* Gsh, const bf16* Gsl,
+                                                      float* rowconst, float* alpha_out, const KmState* kst_for_c) {
+  constexpr int KS = DD + 8;
+  __shared__ __attribute__((aligned(16))) bf16 Gh[DD * KS];
+  __shared__ __attribute__((aligned(16))) bf16 Gl[DD * KS];
+  const int blk = blockIdx.x, bh = blockIdx.y;
+  const int w = threadIdx.x / kWave, l32 = lane_id() & 31, h = lane_id() >> 5;
+  const int row = blk * kKmRows + 32 * w + l32;
+  const bool valid = row < D.N;
+  const bf16* xrow = x + ((size_t)bh * D.N + (valid ? row : D.N - 1)) * DD;
+  bf16x8 xr[DD / 16];
+  load_row_operand<DD>(xrow, xr);
+  copy_hilo<DD, DD>(Gsh + (size_t)bh * DD * DD, Gsl + (size_t)bh * DD * DD, 0, DD, Gh, Gl);
+  __syncthreads();
+  float part = 0.f;
+#pragma unroll
+  for (int ib = 0; ib < DD; ib += 32) {
+    const f32x16 acc = mfma_rows<DD>(Gh, Gl, ib, xr);
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const bf16x4 xv = *reinterpret_cast<const bf16x4*>(xrow + ib + 8 * g + 4 * h);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) part = fmaf(acc[4 * g + r], (float)xv[r], part);
+    }
+  }
+  part += __shfl_xor(part, 32, kWave);
+  if (h == 0 && valid) {
+    const size_t o = (size_t)bh * D.N + row;
+    if (alpha_out) {
+      const float cf = (float)kst_for_c[bh].c_final;
+      alpha_out[o] = part > 0.f ? sqrtf(cf / part) : 0.f;
+      rowconst[o] = part > 0.f ? cf : 0.f;
+    } else {
+      rowconst[o] = part;
+    }
+  }
+}
+
+// Group masses over one attention tile (128 rows of one query group): pass 1 finds each
+// row's softmax max and sum over the key groups, pass 2 adds the normalised masses into
+// per-tile column sums (rows reduced inside the wave, waves in a fixed order).
+template <int DD>
+__global__ __launch_bounds__(256) void k_group_mass_bf16(const bf16* q, Dims D, Bufs B) {
+  constexpr int CB = 64, KS = DD + 8;
+  __shared__ __attribute__((aligned(16))) bf16 Yh[CB * KS];
+  __shared__ __attribute__((aligned(16))) bf16 Yl[CB * KS];
+  __shared__ float lg[kMaxGroups];
+  __shared__ float colw[4][CB];
+  const int t = blockIdx.x, bh = blockIdx.y;
+  if (t >= B.ntiles[bh]) return;
+  const int2 tl = B.tiles[(size_t)bh * D.max_tiles + t];
+  const int a = tl.x, pos0 = tl.y;
+  const int rows = min(D.qt, B.qoff[(size_t)bh * (D.Cq + 1) + a + 1] - pos0);
+  const int tid = threadIdx.x, w = tid / kWave, l32 = lane_id() & 31;
+  const int lrow = 32 * w + l32;
+  const bool valid = lrow < rows;
+  const int tok = B.qperm[(size_t)bh * D.N + pos0 + (valid ? lrow : 0)];
+  bf16x8 xr[DD / 16];
+  load_row_operand<DD>(q + ((size_t)bh * D.N + tok) * DD, xr);
+  const int Ck = B.kst[bh].c_final;
+  const int* ko = B.koff + (size_t)bh * (D.Ck + 1);
+  for (int b = tid; b < Ck; b += 256) lg[b] = logf((float)(ko[b + 1] - ko[b]));
+  const bf16* Kh = B.kcent_h + (size_t)bh * D.Ck * DD;
+  const bf16* Kl = B.kcent_l + (size_t)bh * D.Ck * DD;
+  float m = -INFINITY, ssum = 0.f;
+  for (int c0 = 0; c0 < Ck; c0 += CB) {  // pass 1
+    __syncthreads();
+    copy_hilo<DD, CB>(Kh, Kl, c0, Ck, Yh, Yl);
+    __syncthreads();
+#pragma unroll
+    for (int yb = 0; yb < CB; yb += 32) {
+      const f32x16 acc = mfma_rows<DD>(Yh, Yl, yb, xr);
+      float z[16], mx = m;
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int col = c0 + yb + acc_row(v);
+        z[v] = col < Ck ? fmaf(D.scale, acc[v], lg[col]) : -INFINITY;
+        mx = fmaxf(mx, z[v]);
+      }
+      float add = 0.f;
+#pragma unroll
+      for (int v = 0; v < 16; ++v) add += expf(z[v] - mx);
+      ssum = ssum * expf(m - mx) + add;
+      m = mx;
+    }
+  }
+  {
+    const float mo = __shfl_xor(m, 32, kWave), so = __shfl_xor(ssum, 32, kWave);
+    const float mm = fmaxf(m, mo);
+    ssum = ssum * expf(m - mm) + so * expf(mo - mm);
+    m = mm;
+  }
+  const float inv = valid ? 1.f / ssum : 0.f;
+  float* part = B.mass_part + ((size_t)bh * D.max_tiles + t) * D.Ck;
+  for (int c0 = 0; c0 < Ck; c0 += CB) {  // pass 2
+    __syncthreads();
+    copy_hilo<DD, CB>(Kh, Kl, c0, Ck, Yh, Yl);
+    __syncthreads();
+#pragma unroll
+    for (int yb = 0; yb < CB; yb += 32) {
+      const f32x16 acc = mfma_rows<DD>(Yh, Yl, yb, xr);
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int col = c0 + yb + acc_row(v);
+        float p = col < Ck ? expf(fmaf(D.scale, acc[v], lg[col]) - m) * inv : 0.f;
+#pragma unroll
+        for (int o = 1; o < 32; o <<= 1) p += __shfl_xor(p, o, kWave);
+        if (l32 == 0) colw[w][yb + acc_row(v)] = p;
+      }
+    }
+    __syncthreads();
+    if (tid < CB && c0 + tid < Ck) part[c0 + tid] = ((colw[0][tid] + colw[1][tid]) + colw[2][tid]) + colw[3][tid];
+  }
+}
+
+// u[a][b] = rint(2^32 * mean over the group's rows of the masses), tiles summed in order.
+__global__ __launch_bounds__(256) void k_group_mass_final(Dims D, Bufs B) {
+  const int a = blockIdx.x, bh = blockIdx.y;
+  const int Cq = B.qst[bh].c_final, Ck = B.kst[bh].c_final;
+  if (a >= Cq) return;
+  const int* qo = B.qoff + (size_t)bh * (D.Cq + 1);
+  const int n = qo[a + 1] - qo[a];
+  const int t0 = B.tstart[(size_t)bh * (D.Cq + 1) + a], t1 = B.tstart[(size_t)bh * (D.Cq + 1) + a + 1];
+  const float* part = B.mass_part + (size_t)bh * D.max_tiles * D.Ck;
+  long long* u = B.u + ((size_t)bh * D.Cq + a) * D.Ck;
+  for (int b = threadIdx.x; b < Ck; b += 256) {
+    double sum = 0.0;
+    for (int t = t0; t < t1; ++t) sum += (double)part[(size_t)t * D.Ck + b];
+    u[b] = (long long)rint(sum / (double)n * 4294967296.0);
+  }
 }
 
 // =====================================================================================
@@ -883,6 +1328,8 @@ __global__ __launch_bounds__(1024) void k_build_tiles(Dims D, Bufs B) {
   int tot;
   const int s = block_excl_scan<1024, int>(nt, &tot, ws);
   tstart[a] = s;
+  if (a < Cq) B.tstart[(size_t)bh * (D.Cq + 1) + a] = s;
+  if (a == 0) B.tstart[(size_t)bh * (D.Cq + 1) + Cq] = tot;
   if (a == 0) {
     tstart[kMaxGroups] = tot;
     B.ntiles[bh] = tot;
@@ -903,29 +1350,40 @@ __global__ __launch_bounds__(1024) void k_build_tiles(Dims D, Bufs B) {
 template <typename T, int DD>
 __global__ __launch_bounds__(256) void k_permute_kv(const T* k, const T* v, const int* perm, int N, int Npad,
                                                     T* kp, T* vpt) {
-  __shared__ T vs[64][DD + 2];
+  constexpr int EV = 16 / sizeof(T);  // elements per 16-byte access
+  __shared__ T vs[64][DD + EV];
   const int p0 = blockIdx.x * 64, bh = blockIdx.y;
   const int* pb = perm + (size_t)bh * N;
   const T* kb = k + (size_t)bh * N * DD;
   const T* vb = v + (size_t)bh * N * DD;
   T* kpb = kp + (size_t)bh * Npad * DD;
   T* vtb = vpt + (size_t)bh * DD * Npad;
-  for (int i = threadIdx.x; i < 64 * DD; i += 256) {
-    const int r = i / DD, c = i % DD;
+  // rows: 64 positions x DD/EV chunks of 16 bytes
+  for (int e = threadIdx.x; e < 64 * DD / EV; e += 256) {
+    const int r = e / (DD / EV), c = (e % (DD / EV)) * EV;
     const int pos = p0 + r;
-    T kv = from_f32<T>(0.f), vv = from_f32<T>(0.f);
+    uint4 kv = make_uint4(0, 0, 0, 0), vv = make_uint4(0, 0, 0, 0);
     if (pos < N) {
       const int src = pb[pos];
-      kv = kb[(size_t)src * DD + c];
-      vv = vb[(size_t)src * DD + c];
+      kv = *reinterpret_cast<const uint4*>(kb + (size_t)src * DD + c);
+      vv = *reinterpret_cast<const uint4*>(vb + (size_t)src * DD + c);
     }
-    if (pos < Npad) kpb[(size_t)pos * DD + c] = kv;
-    vs[r][c] = vv;
+    if (pos < Npad) *reinterpret_cast<uint4*>(kpb + (size_t)pos * DD + c) = kv;
+    const T* vt = reinterpret_cast<const T*>(&vv);
+#pragma unroll
+    for (int q = 0; q < EV; ++q) vs[r][c + q] = vt[q];
   }
   __syncthreads();
-  for (int i = threadIdx.x; i < 64 * DD; i += 256) {
-    const int c = i / 64, r = i % 64;
-    if (p0 + r < Npad) vtb[(size_t)c * Npad + p0 + r] = vs[r][c];
+  // transposed: DD rows x 64 positions, EV consecutive positions per 16-byte store
+  for (int e = threadIdx.x; e < DD * 64 / EV; e += 256) {
+    const int c = e / (64 / EV), r = (e % (64 / EV)) * EV;
+    if (p0 + r < Npad) {
+      uint4 out;
+      T* ot = reinterpret_cast<T*>(&out);
+#pragma unroll
+      for (int q = 0; q < EV; ++q) ot[q] = vs[r + q][c];
+      *reinterpret_cast<uint4*>(vtb + (size_t)c * Npad + p0 + r) = out;
+    }
   }
 }
 
@@ -961,16 +1419,40 @@ __global__ void k_identity_plan(Dims D, Bufs B) {
   } while (0)
 
 template <typename T, int DD>
-static void run_lloyd(const void* xv, const Dims& D, const Bufs& B, int C, KmState* st, int* perm,
+static void run_lloyd(const void* xv, const Dims& D, const Bufs& B, int C, const int* init, KmState* st, int* perm,
                       hipStream_t s) {
   const T* x = (const T*)xv;
-  hipLaunchKernelGGL((k_km_init<T, DD>), dim3(C, D.BH), dim3(DD), 0, s, x, D, B, C, st);
+  hipLaunchKernelGGL((k_km_init<T, DD>), dim3(C, D.BH), dim3(256), 0, s, x, D, B, C, init, st);
   for (int t = 1; t <= D.max_iter; ++t) {
-    hipLaunchKernelGGL((k_km_assign<T, DD>), dim3(D.nblk, D.BH), dim3(256), 0, s, x, D, B, C, st, t);
-    hipLaunchKernelGGL(k_km_scan, dim3(D.BH), dim3(1024), 0, s, D, B, C, st, t);
+    if constexpr (std::is_same<T, bf16>::value)
+      hipLaunchKernelGGL((k_km_assign_bf16<DD, 2>), dim3((D.nblk + 1) / 2, D.BH), dim3(256), 0, s, x, D, B, C, st, t);
+    else
+      hipLaunchKernelGGL((k_km_assign<T, DD>), dim3(D.nblk, D.BH), dim3(256), 0, s, x, D, B, C, st, t);
+    hipLaunchKernelGGL(k_km_scan_groups, dim3(C, D.BH), dim3(64), 0, s, D, B, C, st, t);
+    hipLaunchKernelGGL(k_km_scan_head, dim3(D.BH), dim3(256), 0, s, D, B, C, st, t);
     hipLaunchKernelGGL(k_km_scatter, dim3(D.nblk, D.BH), dim3(kKmRows), 0, s, D, B, st, t, perm);
     if (t < D.max_iter)
       hipLaunchKernelGGL((k_km_update<T, DD>), dim3(C, D.BH), dim3(256), 0, s, x, D, B, st, t, perm);
+  }
+}
+
+template <typename T, int DD>
+static void rowquad(const T* x, const Dims& D, const Bufs& B, const float* G, float* rowconst, float* alpha_out,
+                    const KmState* kst, hipStream_t s) {
+  if constexpr (std::is_same<T, bf16>::value)
+    hipLaunchKernelGGL((k_rowquad_bf16<DD>), dim3(D.nblk, D.BH), dim3(256), 0, s, x, D, B.metric_h, B.metric_l,
+                       rowconst, alpha_out, kst);
+  else
+    hipLaunchKernelGGL((k_rowquad<T, DD>), dim3(D.nblk, D.BH), dim3(256), 0, s, x, D, G, rowconst, alpha_out, kst);
+}
+
+template <typename T, int DD>
+static void group_mass(const T* q, const Dims& D, const Bufs& B, hipStream_t s) {
+  if constexpr (std::is_same<T, bf16>::value) {
+    hipLaunchKernelGGL((k_group_mass_bf16<DD>), dim3(D.max_tiles, D.BH), dim3(256), 0, s, q, D, B);
+    hipLaunchKernelGGL(k_group_mass_final, dim3(D.Cq, D.BH), dim3(256), 0, s, D, B);
+  } else {
+    hipLaunchKernelGGL((k_group_mass<T, DD>), dim3(D.Cq, D.BH), dim3(256), 0, s, q, D, B);
   }
 }
 
@@ -979,32 +1461,26 @@ static void plan_impl(const void* qv, const void* kv, const Dims& D, const Bufs&
   const T* q = (const T*)qv;
   const T* k = (const T*)kv;
   // 01: sampled queries and their key-response metric
-  hipLaunchKernelGGL(k_select_all, dim3(D.BH), dim3(1024), 0, s, D.N, D.S, D.seed, (uint64_t)kStreamSampled,
-                     B.sampled, D.S);
+  hipLaunchKernelGGL(k_select_all, dim3(D.BH, 3), dim3(1024), 0, s, D, B);
   hipLaunchKernelGGL((k_gather_rows<T>), dim3(D.S, D.BH), dim3(DD), 0, s, q, B.sampled, D.N, D.S, DD, B.qs);
-  hipLaunchKernelGGL((k_gram<DD>), dim3(D.BH), dim3(256), 0, s, B.qs, D.S, (const KmState*)nullptr,
-                     D.scale * D.scale, B.metric);
+  hipLaunchKernelGGL((k_gram<DD>), dim3(DD * DD / 256, D.BH), dim3(256), 0, s, B.qs, D.S, (const KmState*)nullptr,
+                     D.scale * D.scale, B.metric, B.metric_h, B.metric_l);
   // 02a: paired K/V groups by Lloyd on the key responses
   Bufs Bk = B;
   Bk.alpha = nullptr;
-  hipLaunchKernelGGL((k_rowquad<T, DD>), dim3(D.nblk, D.BH), dim3(256), 0, s, k, D, B.metric, B.rowconst,
-                     (float*)nullptr, (const KmState*)nullptr);
-  hipLaunchKernelGGL(k_select_all, dim3(D.BH), dim3(1024), 0, s, D.N, D.Ck, D.seed, (uint64_t)kStreamKeyInit,
-                     B.init_idx, D.C);
-  run_lloyd<T, DD>(k, D, Bk, D.Ck, B.kst, B.kperm, s);
+  rowquad<T, DD>(k, D, B, B.metric, B.rowconst, (float*)nullptr, (const KmState*)nullptr, s);
+  run_lloyd<T, DD>(k, D, Bk, D.Ck, B.init_k, B.kst, B.kperm, s);
   hipLaunchKernelGGL(k_km_compact, dim3(D.BH), dim3(1024), 0, s, D, B, D.Ck, B.kst, B.klab, B.koff, D.Ck + 1);
   hipLaunchKernelGGL((k_key_centroids<T, DD>), dim3(D.Ck, D.BH), dim3(256), 0, s, k, D, B);
   // 02b: query-response coordinates (RMS-normalised) and query groups
-  hipLaunchKernelGGL((k_gram<DD>), dim3(D.BH), dim3(256), 0, s, B.kcent, D.Ck, (const KmState*)B.kst, 1.f,
-                     B.metric);
-  hipLaunchKernelGGL((k_rowquad<T, DD>), dim3(D.nblk, D.BH), dim3(256), 0, s, q, D, B.metric, B.rowconst, B.alpha,
-                     (const KmState*)B.kst);
-  hipLaunchKernelGGL(k_select_all, dim3(D.BH), dim3(1024), 0, s, D.N, D.Cq, D.seed, (uint64_t)kStreamQueryInit,
-                     B.init_idx, D.C);
-  run_lloyd<T, DD>(q, D, B, D.Cq, B.qst, B.qperm, s);
+  hipLaunchKernelGGL((k_gram<DD>), dim3(DD * DD / 256, D.BH), dim3(256), 0, s, B.kcent, D.Ck, (const KmState*)B.kst, 1.f,
+                     B.metric, B.metric_h, B.metric_l);
+  rowquad<T, DD>(q, D, B, B.metric, B.rowconst, B.alpha, (const KmState*)B.kst, s);
+  run_lloyd<T, DD>(q, D, B, D.Cq, B.init_q, B.qst, B.qperm, s);
   hipLaunchKernelGGL(k_km_compact, dim3(D.BH), dim3(1024), 0, s, D, B, D.Cq, B.qst, B.qlab, B.qoff, D.Cq + 1);
+  hipLaunchKernelGGL(k_build_tiles, dim3(D.BH), dim3(1024), 0, s, D, B);
   // 03: group masses
-  hipLaunchKernelGGL((k_group_mass<T, DD>), dim3(D.Cq, D.BH), dim3(256), 0, s, q, D, B);
+  group_mass<T, DD>(q, D, B, s);
 }
 
 template <typename T, int DD>
@@ -1015,20 +1491,23 @@ static void plan_labels_impl(const void* qv, const void* kv, const int* klab, co
   // key side
   hipLaunchKernelGGL(k_state_reset, dim3((D.BH + 63) / 64), dim3(64), 0, s, B.kst, D.BH, D.Ck, 1);
   hipLaunchKernelGGL(k_labels_given, dim3(D.nblk, D.BH), dim3(kKmRows), 0, s, klab, D, B, B.kst);
-  hipLaunchKernelGGL(k_km_scan, dim3(D.BH), dim3(1024), 0, s, D, B, D.Ck, B.kst, 1);
+  hipLaunchKernelGGL(k_km_scan_groups, dim3(D.Ck, D.BH), dim3(64), 0, s, D, B, D.Ck, B.kst, 1);
+  hipLaunchKernelGGL(k_km_scan_head, dim3(D.BH), dim3(256), 0, s, D, B, D.Ck, B.kst, 1);
   hipLaunchKernelGGL(k_km_scatter, dim3(D.nblk, D.BH), dim3(kKmRows), 0, s, D, B, B.kst, 1, B.kperm);
   hipLaunchKernelGGL(k_km_compact, dim3(D.BH), dim3(1024), 0, s, D, B, D.Ck, B.kst, B.klab, B.koff, D.Ck + 1);
   hipLaunchKernelGGL((k_key_centroids<T, DD>), dim3(D.Ck, D.BH), dim3(256), 0, s, k, D, B);
   // query side
   hipLaunchKernelGGL(k_state_reset, dim3((D.BH + 63) / 64), dim3(64), 0, s, B.qst, D.BH, D.Cq, 1);
   hipLaunchKernelGGL(k_labels_given, dim3(D.nblk, D.BH), dim3(kKmRows), 0, s, qlab, D, B, B.qst);
-  hipLaunchKernelGGL(k_km_scan, dim3(D.BH), dim3(1024), 0, s, D, B, D.Cq, B.qst, 1);
+  hipLaunchKernelGGL(k_km_scan_groups, dim3(D.Cq, D.BH), dim3(64), 0, s, D, B, D.Cq, B.qst, 1);
+  hipLaunchKernelGGL(k_km_scan_head, dim3(D.BH), dim3(256), 0, s, D, B, D.Cq, B.qst, 1);
   hipLaunchKernelGGL(k_km_scatter, dim3(D.nblk, D.BH), dim3(kKmRows), 0, s, D, B, B.qst, 1, B.qperm);
   hipLaunchKernelGGL(k_km_compact, dim3(D.BH), dim3(1024), 0, s, D, B, D.Cq, B.qst, B.qlab, B.qoff, D.Cq + 1);
+  hipLaunchKernelGGL(k_build_tiles, dim3(D.BH), dim3(1024), 0, s, D, B);
   if (mass) {
     (void)hipMemcpyAsync(B.u, mass, sizeof(long long) * (size_t)D.BH * D.Cq * D.Ck, hipMemcpyDeviceToDevice, s);
   } else {
-    hipLaunchKernelGGL((k_group_mass<T, DD>), dim3(D.Cq, D.BH), dim3(256), 0, s, q, D, B);
+    group_mass<T, DD>(q, D, B, s);
   }
 }
 
@@ -1051,7 +1530,6 @@ void launch_route_probes(const Dims& D, const Bufs& B, hipStream_t s) {
     hipLaunchKernelGGL(k_probe_alloc, dim3(D.BH), dim3(1024), 0, s, D, B);
     hipLaunchKernelGGL(k_select_probes, dim3(D.Cq, D.BH), dim3(256), 0, s, D, B);
   }
-  hipLaunchKernelGGL(k_build_tiles, dim3(D.BH), dim3(1024), 0, s, D, B);
 }
 
 template <typename T, int DD>

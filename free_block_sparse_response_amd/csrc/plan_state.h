@@ -4,6 +4,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "common.h"
+
 namespace spr {
 
 // Lloyd bookkeeping of one head (one k-means run).
@@ -31,6 +33,8 @@ struct Dims {
   int Npad;       // padded key count of the permuted K / transposed V
   int qt;         // query rows per attention tile
   int max_tiles;  // attention tiles per head, upper bound
+  int pch;        // key chunks of the probe attention (split over keys)
+  int pkc;        // keys per probe chunk (multiple of the key tile)
   int dtype;      // 0 f32, 1 bf16
   float scale;
   float log2_scale;  // scale * log2(e)
@@ -47,15 +51,20 @@ struct Bufs {
   int* sampled;      // [BH][S]
   float* qs;         // [BH][S][d] gathered sampled queries
   float* metric;     // [BH][d][d] Lloyd metric G
+  bf16* metric_h;    // [BH][d][d] G rounded to bf16
+  bf16* metric_l;    // [BH][d][d] G minus its bf16 rounding
   float* cent;       // [BH][C][d] Lloyd centroids (row space of X = alpha x)
   float* cent_t;     // [BH][C][d] G m_b
   float* cnorm;      // [BH][C]    m_b G m_b
+  bf16* cent_h;      // [BH][C][d] G m_b rounded to bf16
+  bf16* cent_l;      // [BH][C][d] G m_b minus its bf16 rounding, in bf16
   float* alpha;      // [BH][N]    row scales of the query features
   float* rowconst;   // [BH][N]    alpha^2 x G x
   int* rank;         // [BH][N]    stable rank inside a Lloyd row block
   int* tab;          // [BH][C][nblk] block counts -> scatter offsets
   double* ipart;     // [BH][nblk] inertia partial sums
-  int* init_idx;     // [BH][C]
+  int* init_k;       // [BH][Ck] key-group seed rows
+  int* init_q;       // [BH][Cq] query-group seed rows
   int* lab;          // [BH][N]    working labels
   int* gstart;       // [BH][C+1]  working group starts
   int* gcount;       // [BH][C]
@@ -65,6 +74,8 @@ struct Bufs {
   int* kperm;        // [BH][N]
   int* koff;         // [BH][Ck+1]
   float* kcent;      // [BH][Ck][d] key-space centroids of the compacted groups
+  bf16* kcent_h;     // [BH][Ck][d] key centroids rounded to bf16
+  bf16* kcent_l;     // [BH][Ck][d] key centroids minus their bf16 rounding
   int* qlab;         // [BH][N]
   int* qperm;        // [BH][N]
   int* qoff;         // [BH][Cq+1]
@@ -86,7 +97,13 @@ struct Bufs {
   void* vpt;         // [BH][d][Npad] values in key-group order, transposed
   int2* tiles;       // [BH][max_tiles] (query group, first position)
   int* ntiles;       // [BH]
+  int* tstart;       // [BH][Cq+1] first tile of each query group
+  float* mass_part;  // [BH][max_tiles][Ck] per-tile column sums of the group masses
+  float* pp_o;       // [BH][M][pch][d] probe attention partial outputs (unnormalised)
+  float2* pp_ml;     // [BH][M][pch] probe attention partial (max, sum), log2 domain
   double* gram;      // [BH][d+1][2d+1]  [A | B] of the ridge normal equations
+  bf16* theta_h;     // [BH][d][d] Theta^T (output dim major) rounded to bf16, for the apply
+  bf16* theta_l;     // [BH][d][d] Theta^T minus its bf16 rounding
   int* status;       // [BH]
 };
 

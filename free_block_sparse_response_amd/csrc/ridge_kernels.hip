@@ -8,6 +8,8 @@
 // built as one bordered matrix [A | B] (A (d+1)x(d+1), B (d+1)xd), then solved by a
 // Cholesky factorisation held packed in LDS. A pivot at or below 1e-12 x max diag(A)
 // marks the head numerically singular.
+#include <type_traits>
+
 #include "common.h"
 #include "plan_state.h"
 #include "launch.h"
@@ -68,35 +70,56 @@ __global__ __launch_bounds__(256) void k_ridge_gram(Dims D, Bufs B, const float*
   }
 }
 
-// One block per (head, 64 right-hand-side columns): packed Cholesky of A in LDS (redone
-// per column block), then forward and back substitution of the block's columns.
+// Orders the LDS accesses of one wave (its lanes run in lockstep): waits for this wave's
+// outstanding LDS operations and keeps the compiler from moving memory operations across.
+__device__ inline void wave_lds_sync() {
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  __builtin_amdgcn_wave_barrier();
+}
+
+// One block per (head, 32 right-hand-side columns); each block redoes the elimination of A
+// in LDS (lower triangle, packed). A = L1 Dg L1^T (unit lower L1, pivots Dg) is formed by
+// Gaussian elimination without pivoting -- the Cholesky factorisation up to the scaling
+// sqrt(Dg), stable for symmetric positive definite A -- with the same row operations on
+// the right-hand side, Z = L1^-1 B, then L1^T X = Dg^-1 Z. Blocked by 8-column panels: one
+// wave factors a panel (its columns in order, lockstep, no block barrier), then all threads
+// apply the panel's rank-8 update to the trailing matrix and right-hand side; the back
+// substitution is blocked the same way. A pivot at or below 1e-12 x max diag(A) (the
+// squared Cholesky diagonal) fails the head.
 template <int DD>
-__global__ __launch_bounds__(1024) void k_ridge_solve(Dims D, Bufs B, float* coeffs) {
+__global__ __launch_bounds__(256) void k_ridge_solve(Dims D, Bufs B, float* coeffs) {
   constexpr int n = DD + 1;
   constexpr int W = n + DD;
   constexpr int NP = n * (n + 1) / 2;
-  constexpr int CB = 64;
+  constexpr int CB = 32;
+  constexpr int PB = 8;
   __shared__ double Lp[NP];
   __shared__ double Bs[n][CB];
+  __shared__ double pan[n][PB];   // multipliers L1(i, j0 + jj) of the current panel
+  __shared__ double panU[n][PB];  // the same column entries before scaling (A(i, j0 + jj))
+  __shared__ double piv_s[n];
   __shared__ double s_floor;
   __shared__ int s_fail;
   const int cb = blockIdx.x, bh = blockIdx.y, tid = threadIdx.x;
+  const int ty = tid / 16, tx = tid % 16, lane = tid & 63;
+  const bool wave0 = tid < 64;
   const int c0 = cb * CB;
   float* Th = coeffs + (size_t)bh * n * DD;
-  if (D.M == 0) {
-    for (int e = tid; e < n * CB; e += 1024) {
+  auto write_zero = [&]() {
+    for (int e = tid; e < n * CB; e += 256) {
       const int i = e / CB, c = e % CB;
       if (c0 + c < DD) Th[(size_t)i * DD + c0 + c] = 0.f;
     }
+  };
+  if (D.M == 0) {
+    write_zero();
     return;
   }
   const double* G = B.gram + (size_t)bh * n * W;
   auto pk = [](int i, int k) { return i * (i + 1) / 2 + k; };
-  for (int e = tid; e < n * n; e += 1024) {
-    const int i = e / n, k = e % n;
-    if (k <= i) Lp[pk(i, k)] = G[(size_t)i * W + k];
-  }
-  for (int e = tid; e < n * CB; e += 1024) {
+  for (int i = ty; i < n; i += 16)
+    for (int k = tx; k <= i; k += 16) Lp[pk(i, k)] = G[(size_t)i * W + k];
+  for (int e = tid; e < n * CB; e += 256) {
     const int i = e / CB, c = e % CB;
     Bs[i][c] = (c0 + c < DD) ? G[(size_t)i * W + n + c0 + c] : 0.0;
   }
@@ -107,56 +130,98 @@ __global__ __launch_bounds__(1024) void k_ridge_solve(Dims D, Bufs B, float* coe
     s_fail = 0;
   }
   __syncthreads();
-  for (int j = 0; j < n; ++j) {
-    if (tid == 0) {
-      const double piv = Lp[pk(j, j)];
-      if (!(piv > s_floor)) s_fail = 1;
-      else Lp[pk(j, j)] = sqrt(piv);
+  for (int j0 = 0; j0 < n; j0 += PB) {
+    const int w = min(PB, n - j0), je = j0 + w;
+    if (wave0) {
+      // ---- panel factorisation by one wave: columns j0 .. je-1 in order
+      for (int jj = j0; jj < je; ++jj) {
+        wave_lds_sync();
+        const double piv = Lp[pk(jj, jj)];
+        if (!(piv > s_floor)) {
+          if (lane == 0) s_fail = 1;
+          break;
+        }
+        if (lane == 0) piv_s[jj] = piv;
+        const double ipiv = 1.0 / piv;
+        for (int i = jj + 1 + lane; i < n; i += 64) {
+          const double u = Lp[pk(i, jj)];
+          const double lv = u * ipiv;
+          panU[i][jj - j0] = u;
+          pan[i][jj - j0] = lv;
+          Lp[pk(i, jj)] = lv;
+        }
+        wave_lds_sync();
+        // panel-local update: rows i > jj, panel columns k in (jj, min(i, je - 1)]
+        for (int i = jj + 1 + lane; i < n; i += 64) {
+          const double lv = pan[i][jj - j0];
+          const int kmax = min(i, je - 1);
+          for (int k = jj + 1; k <= kmax; ++k) Lp[pk(i, k)] -= lv * panU[k][jj - j0];
+        }
+        // right-hand side rows inside the panel
+        for (int e = lane; e < (je - jj - 1) * CB; e += 64) {
+          const int i = jj + 1 + e / CB, c = e % CB;
+          Bs[i][c] -= pan[i][jj - j0] * Bs[jj][c];
+        }
+      }
     }
     __syncthreads();
     if (s_fail) break;
-    const double djj = Lp[pk(j, j)];
-    for (int i = j + 1 + tid; i < n; i += 1024) Lp[pk(i, j)] /= djj;
-    __syncthreads();
-    const int m = n - j - 1;
-    for (int e = tid; e < m * m; e += 1024) {
-      const int ii = e / m, kk = e % m;
-      if (kk <= ii) {
-        const int i = j + 1 + ii, k = j + 1 + kk;
-        Lp[pk(i, k)] -= Lp[pk(i, j)] * Lp[pk(k, j)];
+    // ---- rank-w update of the trailing rows i >= je (matrix and right-hand side)
+    for (int i = je + ty; i < n; i += 16) {
+      double li[PB];
+#pragma unroll
+      for (int q = 0; q < PB; ++q) li[q] = q < w ? pan[i][q] : 0.0;
+      for (int k = je + tx; k <= i; k += 16) {
+        double acc = Lp[pk(i, k)];
+#pragma unroll
+        for (int q = 0; q < PB; ++q) acc -= li[q] * panU[k][q];
+        Lp[pk(i, k)] = acc;
+      }
+      for (int c = tx; c < CB; c += 16) {
+        double acc = Bs[i][c];
+#pragma unroll
+        for (int q = 0; q < PB; ++q)
+          if (q < w) acc -= li[q] * Bs[j0 + q][c];
+        Bs[i][c] = acc;
       }
     }
     __syncthreads();
   }
   if (s_fail) {
-    for (int e = tid; e < n * CB; e += 1024) {
-      const int i = e / CB, c = e % CB;
-      if (c0 + c < DD) Th[(size_t)i * DD + c0 + c] = 0.f;
-    }
+    write_zero();
     if (tid == 0) B.status[bh] = 5;  // SPARSEPR_ERR_NUMERICAL
     return;
   }
-  // L Y = B
-  for (int i = 0; i < n; ++i) {
-    if (tid < CB) Bs[i][tid] /= Lp[pk(i, i)];
+  for (int e = tid; e < n * CB; e += 256) {
+    const int i = e / CB, c = e % CB;
+    Bs[i][c] /= piv_s[i];
+  }
+  __syncthreads();
+  // ---- L1^T X = Dg^-1 Z, panels from the last: one wave solves inside the panel, then all
+  //      threads remove the panel's unknowns from the rows above it
+  const int np = (n + PB - 1) / PB;
+  for (int p = np - 1; p >= 0; --p) {
+    const int j0 = p * PB, je = min(n, j0 + PB);
+    if (wave0) {
+      for (int jj = je - 1; jj > j0; --jj) {
+        wave_lds_sync();
+        for (int e = lane; e < (jj - j0) * CB; e += 64) {
+          const int k = j0 + e / CB, c = e % CB;
+          Bs[k][c] -= Lp[pk(jj, k)] * Bs[jj][c];
+        }
+      }
+    }
     __syncthreads();
-    for (int e = tid; e < (n - i - 1) * CB; e += 1024) {
-      const int k = i + 1 + e / CB, c = e % CB;
-      Bs[k][c] -= Lp[pk(k, i)] * Bs[i][c];
+    for (int k = ty; k < j0; k += 16) {
+      for (int c = tx; c < CB; c += 16) {
+        double acc = Bs[k][c];
+        for (int jj = j0; jj < je; ++jj) acc -= Lp[pk(jj, k)] * Bs[jj][c];
+        Bs[k][c] = acc;
+      }
     }
     __syncthreads();
   }
-  // L^T X = Y
-  for (int i = n - 1; i >= 0; --i) {
-    if (tid < CB) Bs[i][tid] /= Lp[pk(i, i)];
-    __syncthreads();
-    for (int e = tid; e < i * CB; e += 1024) {
-      const int k = e / CB, c = e % CB;
-      Bs[k][c] -= Lp[pk(i, k)] * Bs[i][c];
-    }
-    __syncthreads();
-  }
-  for (int e = tid; e < n * CB; e += 1024) {
+  for (int e = tid; e < n * CB; e += 256) {
     const int i = e / CB, c = e % CB;
     if (c0 + c < DD) Th[(size_t)i * DD + c0 + c] = (float)Bs[i][c];
   }
@@ -211,6 +276,91 @@ __global__ __launch_bounds__(256) void k_apply(Dims D, Bufs B, const T* o_sp, co
   }
 }
 
+// Theta^T split as bf16 hi + lo (row j = output dim, column k = input dim), once per head.
+template <int DD>
+__global__ __launch_bounds__(256) void k_theta_split(Dims D, Bufs B, const float* coeffs) {
+  const int j0 = blockIdx.x * (256 / DD), bh = blockIdx.y;
+  const int j = j0 + threadIdx.x / DD, k = threadIdx.x % DD;  // one Theta^T entry per thread
+  const float v = coeffs[(size_t)bh * (DD + 1) * DD + (size_t)k * DD + j];
+  const bf16 hb = (bf16)v;
+  const size_t o = (size_t)bh * DD * DD + (size_t)j * DD + k;
+  B.theta_h[o] = hb;
+  B.theta_l[o] = (bf16)(v - (float)hb);
+}
+
+// bf16 apply on the matrix cores: Theta^T (hi + lo bf16, copied into LDS) times the exact
+// bf16 row of o (transposed product: lane l owns row l % 32 of a 32-row set and 16 output
+// dims per 32-dim block); each wave owns RS row sets so every operand read feeds RS
+// products. The epilogue adds o and the bias; probe rows take o_dense.
+template <int DD, int RS>
+__global__ __launch_bounds__(256) void k_apply_bf16(Dims D, Bufs B, const bf16* o_sp, const float* o_dn,
+                                                    const float* coeffs, bf16* out) {
+  constexpr int KS = DD + 8;
+  __shared__ __attribute__((aligned(16))) bf16 Th[DD * KS];
+  __shared__ __attribute__((aligned(16))) bf16 Tl[DD * KS];
+  __shared__ float bias[DD];
+  const int blk = blockIdx.x, bh = blockIdx.y;
+  const int tid = threadIdx.x, w = tid / kWave, l32 = lane_id() & 31, h = lane_id() >> 5;
+  const bf16* sh = B.theta_h + (size_t)bh * DD * DD;
+  const bf16* sl = B.theta_l + (size_t)bh * DD * DD;
+  for (int e = tid; e < DD * DD / 8; e += 256) {
+    const int r = e / (DD / 8), c8 = (e % (DD / 8)) * 8;
+    *reinterpret_cast<bf16x8*>(&Th[r * KS + c8]) = *reinterpret_cast<const bf16x8*>(sh + (size_t)r * DD + c8);
+    *reinterpret_cast<bf16x8*>(&Tl[r * KS + c8]) = *reinterpret_cast<const bf16x8*>(sl + (size_t)r * DD + c8);
+  }
+  if (tid < DD) bias[tid] = coeffs[(size_t)bh * (DD + 1) * DD + (size_t)DD * DD + tid];
+  int row[RS], slot[RS];
+  bf16x8 xr[RS][DD / 16];
+#pragma unroll
+  for (int rs = 0; rs < RS; ++rs) {
+    row[rs] = blk * 128 * RS + 128 * rs + 32 * w + l32;
+    const bool valid = row[rs] < D.N;
+    const bf16* orow = o_sp + ((size_t)bh * D.N + (valid ? row[rs] : D.N - 1)) * DD;
+#pragma unroll
+    for (int c = 0; c < DD / 16; ++c) xr[rs][c] = *reinterpret_cast<const bf16x8*>(orow + 16 * c + 8 * h);
+    slot[rs] = (valid && D.M > 0) ? B.pslot[(size_t)bh * D.N + row[rs]] : -1;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int jb = 0; jb < DD; jb += 32) {
+    f32x16 acc[RS];
+#pragma unroll
+    for (int rs = 0; rs < RS; ++rs)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[rs][v] = 0.f;
+#pragma unroll
+    for (int c = 0; c < DD / 16; ++c) {
+      const bf16x8 ah = *reinterpret_cast<const bf16x8*>(&Th[(jb + l32) * KS + 16 * c + 8 * h]);
+      const bf16x8 al = *reinterpret_cast<const bf16x8*>(&Tl[(jb + l32) * KS + 16 * c + 8 * h]);
+#pragma unroll
+      for (int rs = 0; rs < RS; ++rs) {
+        acc[rs] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah, xr[rs][c], acc[rs], 0, 0, 0);
+        acc[rs] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(al, xr[rs][c], acc[rs], 0, 0, 0);
+      }
+    }
+#pragma unroll
+    for (int rs = 0; rs < RS; ++rs) {
+      if (row[rs] >= D.N) continue;
+      const bf16* orow = o_sp + ((size_t)bh * D.N + row[rs]) * DD;
+      bf16* dst = out + ((size_t)bh * D.N + row[rs]) * DD;
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int j = jb + 8 * g + 4 * h;
+        bf16x4 ov;
+        if (slot[rs] >= 0) {
+          const float4 dv = *reinterpret_cast<const float4*>(o_dn + ((size_t)bh * D.M + slot[rs]) * DD + j);
+          ov[0] = (bf16)dv.x; ov[1] = (bf16)dv.y; ov[2] = (bf16)dv.z; ov[3] = (bf16)dv.w;
+        } else {
+          const bf16x4 xv = *reinterpret_cast<const bf16x4*>(orow + j);
+#pragma unroll
+          for (int r = 0; r < 4; ++r) ov[r] = (bf16)((float)xv[r] + acc[rs][4 * g + r] + bias[j + r]);
+        }
+        *reinterpret_cast<bf16x4*>(dst + j) = ov;
+      }
+    }
+  }
+}
+
 template <int DD>
 static void fit_impl(const Dims& D, const Bufs& B, const float* o_psp, const float* o_dn, const float* w, float* coeffs,
                      hipStream_t s) {
@@ -219,14 +369,21 @@ static void fit_impl(const Dims& D, const Bufs& B, const float* o_psp, const flo
     dim3 g((n + 31) / 32, (n + DD + 31) / 32, D.BH);
     hipLaunchKernelGGL((k_ridge_gram<DD>), g, dim3(256), 0, s, D, B, o_psp, o_dn, w);
   }
-  hipLaunchKernelGGL((k_ridge_solve<DD>), dim3((DD + 63) / 64, D.BH), dim3(1024), 0, s, D, B, coeffs);
+  hipLaunchKernelGGL((k_ridge_solve<DD>), dim3((DD + 31) / 32, D.BH), dim3(256), 0, s, D, B, coeffs);
 }
 
 template <typename T, int DD>
 static void apply_impl(const Dims& D, const Bufs& B, const void* o_sp, const float* o_dn, const float* coeffs, void* out,
                        hipStream_t s) {
-  hipLaunchKernelGGL((k_apply<T, DD>), dim3((D.N + 63) / 64, D.BH), dim3(256), 0, s, D, B, (const T*)o_sp, o_dn,
-                     coeffs, (T*)out);
+  if constexpr (std::is_same<T, bf16>::value) {
+    constexpr int RS = 2;
+    hipLaunchKernelGGL((k_theta_split<DD>), dim3(DD * DD / 256, D.BH), dim3(256), 0, s, D, B, coeffs);
+    hipLaunchKernelGGL((k_apply_bf16<DD, RS>), dim3((D.N + 128 * RS - 1) / (128 * RS), D.BH), dim3(256), 0, s, D, B,
+                       (const bf16*)o_sp, o_dn, coeffs, (bf16*)out);
+  }
+  else
+    hipLaunchKernelGGL((k_apply<T, DD>), dim3((D.N + 63) / 64, D.BH), dim3(256), 0, s, D, B, (const T*)o_sp, o_dn,
+                       coeffs, (T*)out);
 }
 
 #define SPR_DISPATCH2(dtype, d, FN, ...)                                  \

@@ -75,15 +75,20 @@ Bufs carve(const Dims& D, void* base, size_t* total) {
   B.sampled = c.take<int>(BH * D.S);
   B.qs = c.take<float>(BH * D.S * d);
   B.metric = c.take<float>(BH * d * d);
+  B.metric_h = c.take<spr::bf16>(BH * d * d);
+  B.metric_l = c.take<spr::bf16>(BH * d * d);
   B.cent = c.take<float>(BH * C * d);
   B.cent_t = c.take<float>(BH * C * d);
   B.cnorm = c.take<float>(BH * C);
+  B.cent_h = c.take<spr::bf16>(BH * C * d);
+  B.cent_l = c.take<spr::bf16>(BH * C * d);
   B.alpha = c.take<float>(BH * N);
   B.rowconst = c.take<float>(BH * N);
   B.rank = c.take<int>(BH * N);
   B.tab = c.take<int>(BH * C * D.nblk);
   B.ipart = c.take<double>(BH * D.nblk);
-  B.init_idx = c.take<int>(BH * C);
+  B.init_k = c.take<int>(BH * D.Ck);
+  B.init_q = c.take<int>(BH * D.Cq);
   B.lab = c.take<int>(BH * N);
   B.gstart = c.take<int>(BH * (C + 1));
   B.gcount = c.take<int>(BH * C);
@@ -93,6 +98,8 @@ Bufs carve(const Dims& D, void* base, size_t* total) {
   B.kperm = c.take<int>(BH * N);
   B.koff = c.take<int>(BH * (D.Ck + 1));
   B.kcent = c.take<float>(BH * D.Ck * d);
+  B.kcent_h = c.take<spr::bf16>(BH * D.Ck * d);
+  B.kcent_l = c.take<spr::bf16>(BH * D.Ck * d);
   B.qlab = c.take<int>(BH * N);
   B.qperm = c.take<int>(BH * N);
   B.qoff = c.take<int>(BH * (D.Cq + 1));
@@ -114,7 +121,13 @@ Bufs carve(const Dims& D, void* base, size_t* total) {
   B.vpt = c.take<char>(BH * D.Npad * d * esz);
   B.tiles = c.take<int2>(BH * D.max_tiles);
   B.ntiles = c.take<int>(BH);
+  B.tstart = c.take<int>(BH * (D.Cq + 1));
+  B.mass_part = c.take<float>(BH * D.max_tiles * D.Ck);
+  B.pp_o = c.take<float>(BH * D.M * D.pch * d);
+  B.pp_ml = c.take<float2>(BH * D.M * D.pch);
   B.gram = c.take<double>(BH * (d + 1) * (2 * d + 1));
+  B.theta_h = c.take<spr::bf16>(BH * d * d);
+  B.theta_l = c.take<spr::bf16>(BH * d * d);
   B.status = c.take<int>(BH);
   if (total) *total = align_up(c.off, 256);
   return B;
@@ -187,6 +200,16 @@ sparsepr_status sparsepr_plan_create(const sparsepr_config* cfg, sparsepr_plan_t
   D.Npad = (N + 63) / 64 * 64 + 64;
   D.qt = spr::kAttnQT;
   D.max_tiles = (N + spr::kAttnQT - 1) / spr::kAttnQT + D.Cq;
+  {
+    // split the probe rows' keys so that about 1024 workgroups share the probe attention
+    const int ptiles = (D.M + spr::kAttnQT - 1) / spr::kAttnQT;
+    const long long want = ptiles > 0 ? (1024 + (long long)D.BH * ptiles - 1) / ((long long)D.BH * ptiles) : 1;
+    const int maxch = (N + 511) / 512;
+    int pch = (int)(want < 1 ? 1 : (want > maxch ? maxch : want));
+    if (pch < 1) pch = 1;
+    D.pkc = ((N + pch - 1) / pch + spr::kKeyTile - 1) / spr::kKeyTile * spr::kKeyTile;
+    D.pch = (N + D.pkc - 1) / D.pkc;
+  }
   D.dtype = c.dtype;
   D.scale = c.softmax_scale > 0.f ? c.softmax_scale : (float)(1.0 / sqrt((double)c.head_dim));
   D.log2_scale = (float)((double)D.scale * 1.4426950408889634);
