@@ -19,7 +19,7 @@ class SparsePR:
 
     ``cfg`` keys: batch, heads, seq_len, head_dim, dtype ("f32" / "bf16"), n_sampled,
     n_key_groups, n_query_groups, n_probes, density, ridge_lambda, seed and optionally
-    kmeans_max_iter, kmeans_tol, penalize_bias, softmax_scale.
+    kmeans_max_iter, kmeans_tol, penalize_bias, softmax_scale, assign_precision.
     """
 
     def __init__(self, cfg, device="cuda"):
@@ -31,7 +31,8 @@ class SparsePR:
         self._cc = L.make_config(c["batch"], c["heads"], c["seq_len"], c["head_dim"], c["dtype"], c["n_sampled"],
                                  c["n_key_groups"], c["n_query_groups"], c["n_probes"], c["density"],
                                  c.get("kmeans_max_iter", 25), c.get("kmeans_tol", 1e-4), c.get("ridge_lambda", 1e-3),
-                                 c.get("penalize_bias", 0), c.get("seed", 0), c.get("softmax_scale", 0.0))
+                                 c.get("penalize_bias", 0), c.get("seed", 0), c.get("softmax_scale", 0.0),
+                                 c.get("assign_precision", 0))
         self.plan_h = L.sparsepr_plan_create(self._cc)
         self.ws = torch.empty(L.sparsepr_workspace_bytes(self.plan_h), dtype=torch.uint8, device=device)
         shape = (c["batch"], c["heads"], self.N, self.d)

@@ -124,6 +124,7 @@ __global__ __launch_bounds__(256, 2) void k_bsfa_bf16(const bf16* __restrict__ q
   // ---- Q^T operand in registers: query (32w + l32), d-slots 16c + 8h .. +7
   const int qr = 32 * w + l32;
   const bool qvalid = qr < rows;
+  const bool wave_active = 32 * w < rows;  // a wave past the tile's last row only stages K / V
   int tok;
   if (MODE == 0) tok = B.qperm[(size_t)bh * D.N + pos0 + (qvalid ? qr : 0)];
   else tok = B.probes[(size_t)bh * D.M + pos0 + (qvalid ? qr : 0)];
@@ -187,6 +188,7 @@ __global__ __launch_bounds__(256, 2) void k_bsfa_bf16(const bf16* __restrict__ q
     const int k0 = ts.k0, lo = ts.lo, hi = ts.hi;
     const bool more = ts.next();
     if (more) load_tile(ts.k0);
+    if (wave_active) {
     // ---- S^T = K Q^T for two 32-key blocks
     const bf16* Kc = Ks[cur];
     f32x16 s[2];
@@ -218,7 +220,7 @@ __global__ __launch_bounds__(256, 2) void k_bsfa_bf16(const bf16* __restrict__ q
       for (int v = 0; v < 16; ++v) mt = fmaxf(mt, s[kb][v]);
     mt = fmaxf(mt, __shfl_xor(mt, 32, kWave)) * c2;
     if (mt > m_run + 8.f) {
-      const float alpha = exp2f(m_run - mt);
+      const float alpha = __builtin_amdgcn_exp2f(m_run - mt);
       m_run = mt;
       l_half *= alpha;
 #pragma unroll
@@ -231,7 +233,7 @@ __global__ __launch_bounds__(256, 2) void k_bsfa_bf16(const bf16* __restrict__ q
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
-        const float p = exp2f(fmaf(s[kb][v], c2, -m_run));
+        const float p = __builtin_amdgcn_exp2f(fmaf(s[kb][v], c2, -m_run));
         s[kb][v] = p;
         ps += p;
       }
@@ -256,6 +258,7 @@ __global__ __launch_bounds__(256, 2) void k_bsfa_bf16(const bf16* __restrict__ q
         o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, pb, o[db], 0, 0, 0);
       }
     }
+    }  // wave_active
     if (more) store_tile(cur ^ 1);
     __syncthreads();
     cur ^= 1;

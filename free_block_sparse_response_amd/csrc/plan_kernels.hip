@@ -800,14 +800,16 @@ __device__ inline void km_rank_block(const Dims& D, const Bufs& B, int C, int bh
 }
 
 // Assignment of iteration t for 128*RS rows: each of the 4 waves owns RS sets of 32 rows, so
-// every centroid operand read from LDS feeds RS products. Centroid operands (G m_b as
-// bf16 hi + lo) are copied 64 at a time into LDS.
-template <int DD, int RS>
+// every centroid operand read from LDS feeds RS products. Centroid operands (G m_b in
+// bf16, plus its bf16 remainder when LO) are double-buffered in LDS 64 centroids at a time:
+// the next chunk's global loads are issued before the current chunk's products.
+template <int DD, int RS, bool LO>
 __global__ __launch_bounds__(256) void k_km_assign_bf16(const bf16* x, Dims D, Bufs B, int C, KmState* st, int t) {
   constexpr int CB = 64, KS = DD + 8, NB = kKmRows * RS;
-  __shared__ __attribute__((aligned(16))) bf16 Yh[CB * KS];
-  __shared__ __attribute__((aligned(16))) bf16 Yl[CB * KS];
-  __shared__ float cns[CB];
+  constexpr int NL = CB * DD / 8 / 256;  // 16-byte loads per thread per chunk and operand
+  constexpr int NO = LO ? 2 : 1;
+  __shared__ __attribute__((aligned(16))) bf16 Y[2][NO][CB * KS];
+  __shared__ float cns[2][CB];
   __shared__ int lab_s[NB];
   __shared__ double dred[NB];
   __shared__ int hist[kMaxGroups];
@@ -827,14 +829,42 @@ __global__ __launch_bounds__(256) void k_km_assign_bf16(const bf16* x, Dims D, B
     best[rs] = INFINITY;
     bidx[rs] = 0x7fffffff;
   }
-  const bf16* Ch = B.cent_h + (size_t)bh * D.C * DD;
-  const bf16* Cl = B.cent_l + (size_t)bh * D.C * DD;
+  const bf16* Cop[2] = {B.cent_h + (size_t)bh * D.C * DD, B.cent_l + (size_t)bh * D.C * DD};
   const float* cn = B.cnorm + (size_t)bh * D.C;
+  bf16x8 pre[NO][NL];
+  float pcn = 0.f;
+  auto load_chunk = [&](int c0) {
+#pragma unroll
+    for (int o = 0; o < NO; ++o)
+#pragma unroll
+      for (int i = 0; i < NL; ++i) {
+        const int e = tid + 256 * i, r = e / (DD / 8), c8 = (e % (DD / 8)) * 8;
+        if (c0 + r < C) {
+          pre[o][i] = *reinterpret_cast<const bf16x8*>(Cop[o] + (size_t)(c0 + r) * DD + c8);
+        } else {
+#pragma unroll
+          for (int q = 0; q < 8; ++q) pre[o][i][q] = (bf16)0.f;
+        }
+      }
+    pcn = (tid < CB && c0 + tid < C) ? cn[c0 + tid] : 0.f;
+  };
+  auto store_chunk = [&](int buf) {
+#pragma unroll
+    for (int o = 0; o < NO; ++o)
+#pragma unroll
+      for (int i = 0; i < NL; ++i) {
+        const int e = tid + 256 * i, r = e / (DD / 8), c8 = (e % (DD / 8)) * 8;
+        *reinterpret_cast<bf16x8*>(&Y[buf][o][r * KS + c8]) = pre[o][i];
+      }
+    if (tid < CB) cns[buf][tid] = pcn;
+  };
+  load_chunk(0);
+  store_chunk(0);
+  __syncthreads();
+  int cur = 0;
   for (int c0 = 0; c0 < C; c0 += CB) {
-    __syncthreads();
-    copy_hilo<DD, CB>(Ch, Cl, c0, C, Yh, Yl);
-    if (tid < CB) cns[tid] = c0 + tid < C ? cn[c0 + tid] : 0.f;
-    __syncthreads();
+    const bool more = c0 + CB < C;
+    if (more) load_chunk(c0 + CB);
 #pragma unroll
     for (int yb = 0; yb < CB; yb += 32) {
       f32x16 acc[RS];
@@ -844,12 +874,12 @@ __global__ __launch_bounds__(256) void k_km_assign_bf16(const bf16* x, Dims D, B
         for (int v = 0; v < 16; ++v) acc[rs][v] = 0.f;
 #pragma unroll
       for (int c = 0; c < DD / 16; ++c) {
-        const bf16x8 ah = *reinterpret_cast<const bf16x8*>(&Yh[(yb + l32) * KS + 16 * c + 8 * h]);
-        const bf16x8 al = *reinterpret_cast<const bf16x8*>(&Yl[(yb + l32) * KS + 16 * c + 8 * h]);
 #pragma unroll
-        for (int rs = 0; rs < RS; ++rs) {
-          acc[rs] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah, xr[rs][c], acc[rs], 0, 0, 0);
-          acc[rs] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(al, xr[rs][c], acc[rs], 0, 0, 0);
+        for (int o = 0; o < NO; ++o) {
+          const bf16x8 av = *reinterpret_cast<const bf16x8*>(&Y[cur][o][(yb + l32) * KS + 16 * c + 8 * h]);
+#pragma unroll
+          for (int rs = 0; rs < RS; ++rs)
+            acc[rs] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, xr[rs][c], acc[rs], 0, 0, 0);
         }
       }
 #pragma unroll
@@ -857,10 +887,13 @@ __global__ __launch_bounds__(256) void k_km_assign_bf16(const bf16* x, Dims D, B
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
           const int cl = yb + acc_row(v), col = c0 + cl;
-          const float sc = fmaf(-a2[rs], acc[rs][v], cns[cl]);
+          const float sc = fmaf(-a2[rs], acc[rs][v], cns[cur][cl]);
           if (col < C && (sc < best[rs] || (sc == best[rs] && col < bidx[rs]))) { best[rs] = sc; bidx[rs] = col; }
         }
     }
+    if (more) store_chunk(cur ^ 1);
+    __syncthreads();
+    cur ^= 1;
   }
 #pragma unroll
   for (int rs = 0; rs < RS; ++rs) {
@@ -1425,7 +1458,12 @@ static void run_lloyd(const void* xv, const Dims& D, const Bufs& B, int C, const
   hipLaunchKernelGGL((k_km_init<T, DD>), dim3(C, D.BH), dim3(256), 0, s, x, D, B, C, init, st);
   for (int t = 1; t <= D.max_iter; ++t) {
     if constexpr (std::is_same<T, bf16>::value)
-      hipLaunchKernelGGL((k_km_assign_bf16<DD, 2>), dim3((D.nblk + 1) / 2, D.BH), dim3(256), 0, s, x, D, B, C, st, t);
+      if (D.assign_lo)
+        hipLaunchKernelGGL((k_km_assign_bf16<DD, 2, true>), dim3((D.nblk + 1) / 2, D.BH), dim3(256), 0, s, x, D, B, C,
+                           st, t);
+      else
+        hipLaunchKernelGGL((k_km_assign_bf16<DD, 2, false>), dim3((D.nblk + 1) / 2, D.BH), dim3(256), 0, s, x, D, B, C,
+                           st, t);
     else
       hipLaunchKernelGGL((k_km_assign<T, DD>), dim3(D.nblk, D.BH), dim3(256), 0, s, x, D, B, C, st, t);
     hipLaunchKernelGGL(k_km_scan_groups, dim3(C, D.BH), dim3(64), 0, s, D, B, C, st, t);

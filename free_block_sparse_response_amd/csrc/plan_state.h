@@ -44,6 +44,7 @@ struct Dims {
   float tol;
   float lambda;
   int pen_bias;
+  int assign_lo;  // Lloyd assignment with the bf16 remainder of the centroid operand
   uint64_t seed;
 };
 

@@ -183,6 +183,7 @@ sparsepr_status sparsepr_plan_create(const sparsepr_config* cfg, sparsepr_plan_t
   if (!finite_d(c.kmeans_tol) || c.kmeans_tol < 0.f) return SPARSEPR_ERR_INVALID_ARG;
   if (!finite_d(c.ridge_lambda) || c.ridge_lambda < 0.f) return SPARSEPR_ERR_INVALID_ARG;
   if (!finite_d(c.softmax_scale) || c.softmax_scale < 0.f) return SPARSEPR_ERR_INVALID_ARG;
+  if (c.assign_precision != 0 && c.assign_precision != 1) return SPARSEPR_ERR_INVALID_ARG;
 
   sparsepr_plan_s* p = new (std::nothrow) sparsepr_plan_s();
   if (!p) return SPARSEPR_ERR_INVALID_ARG;
@@ -219,6 +220,7 @@ sparsepr_status sparsepr_plan_create(const sparsepr_config* cfg, sparsepr_plan_t
   D.tol = c.kmeans_tol;
   D.lambda = c.ridge_lambda;
   D.pen_bias = c.penalize_bias ? 1 : 0;
+  D.assign_lo = c.assign_precision ? 1 : 0;
   D.seed = c.seed;
   carve(D, nullptr, &p->ws_bytes);
   p->ws = nullptr;

@@ -76,6 +76,9 @@ typedef struct {
   float ridge_lambda;                      /* lambda >= 0 on the linear part of the map   */
   int32_t penalize_bias;                   /* nonzero: lambda on the bias row too         */
   uint64_t seed;                           /* seeds the counter-based selection hash      */
+  int32_t assign_precision;                /* bf16 inputs, Lloyd assignment products:     */
+                                           /*   0 centroid operand rounded to bf16,       */
+                                           /*   1 bf16 + bf16 remainder (~16-bit operand) */
 } sparsepr_config;
 
 typedef struct sparsepr_plan_s* sparsepr_plan_t;

@@ -61,6 +61,7 @@ def _create(lib, cfg):
     (dict(kmeans_tol=-1e-3), L.SPARSEPR_ERR_INVALID_ARG),
     (dict(seq_len=0), L.SPARSEPR_ERR_INVALID_ARG),
     (dict(batch=0), L.SPARSEPR_ERR_INVALID_ARG),
+    (dict(assign_precision=2), L.SPARSEPR_ERR_INVALID_ARG),
 ])
 def test_plan_create_rejects(lib, over, want):
     st, h = _create(lib, _cfg(**over))

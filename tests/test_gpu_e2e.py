@@ -63,10 +63,10 @@ def check_plan_invariants(sp, N, M, rho):
     return info, ex
 
 
-def _error_stats_vs_oracle(w, heads, rows_per_head=None):
-    say(f"case: e2e {w['dtype']} N={configs.seq_len(w)} heads={heads}")
+def _error_stats_vs_oracle(w, heads, rows_per_head=None, **over):
+    say(f"case: e2e {w['dtype']} N={configs.seq_len(w)} heads={heads} {over}")
     (tq, q64), (tk, k64), (tv, v64) = inputs(w, heads)
-    sp = gpu_call(w, tq, tk, tv, heads=len(heads))
+    sp = gpu_call(w, tq, tk, tv, heads=len(heads), **over)
     N, M = configs.seq_len(w), w["n_probes"]
     info, ex = check_plan_invariants(sp, N, M, w["density"])
     refs = oracle_heads(w, q64, k64, v64, heads)
@@ -102,10 +102,11 @@ def test_c1_full_call_error_matches_oracle():
     _error_stats_vs_oracle(configs.CONFIGS["c1"], [0])
 
 
-def test_c2_full_call_error_matches_oracle():
+@pytest.mark.parametrize("assign_precision", [0, 1])
+def test_c2_full_call_error_matches_oracle(assign_precision):
     # the benchmark's workload and launch configuration: all 8 heads, 2048 sampled rows per head
     w = configs.CONFIGS["c2"]
-    _error_stats_vs_oracle(w, list(range(w["heads"])), rows_per_head=2048)
+    _error_stats_vs_oracle(w, list(range(w["heads"])), rows_per_head=2048, assign_precision=assign_precision)
 
 
 def test_c2_deterministic_bitwise():
