@@ -27,6 +27,28 @@ BF16_MFMA_PEAK_TFLOPS = 2500.0
 FP32_VECTOR_PEAK_TFLOPS = 157.3
 
 
+ATTN_SRC = os.path.join(ROOT, "free_block_sparse_response_amd", "csrc", "attn_kernels.hip")
+
+
+def recorded_traffic(config):
+    """HBM bytes per launch of the block-sparse kernel from the committed counter summary
+    profiles/bsfa_<config>_traffic.md, or None when that summary is missing or was taken on
+    a different version of the kernel source (its sha256 is recorded beside the figure)."""
+    import hashlib
+    import re
+
+    path = os.path.join(ROOT, "profiles", f"bsfa_{config}_traffic.md")
+    if not os.path.exists(path):
+        return None
+    text = open(path).read()
+    m = re.search(r"traffic_bytes_per_launch:\s*(\d+)", text)
+    h = re.search(r"kernel_source_sha256:\s*([0-9a-f]{64})", text)
+    if not m or not h:
+        return None
+    cur = hashlib.sha256(open(ATTN_SRC, "rb").read()).hexdigest()
+    return int(m.group(1)) if cur == h.group(1) else None
+
+
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
@@ -158,7 +180,7 @@ def main():
     roofline = {"kernel": "k_bsfa_bf16 (block-sparse attention)" if w["dtype"] == "bf16" else "k_bsfa_f32",
                 "bound": "mfma" if w["dtype"] == "bf16" else "alu", "achieved": round(bsfa_tflops, 2),
                 "peak": BF16_MFMA_PEAK_TFLOPS if w["dtype"] == "bf16" else FP32_VECTOR_PEAK_TFLOPS,
-                "unit": "TFLOP/s", "frac": None, "traffic": None,
+                "unit": "TFLOP/s", "frac": None, "traffic": recorded_traffic(args.config),
                 "flop_per_launch": bsfa_flop, "ms_per_launch": round(bsfa_ms, 4)}
     roofline["frac"] = round(roofline["achieved"] / roofline["peak"], 4)
     probe_flop = 4.0 * d * M * N * BH

@@ -81,7 +81,8 @@ struct TileSeq {
 // -------------------------------------------------------------------------------------
 // bf16 MFMA kernel. MODE 0: block-sparse tiles from the tile table, bf16 output in token
 // order (plus float rows for probes). MODE 1: probe rows (128 per block) over one chunk of
-// all keys, partial outputs for the chunk combine.
+// all keys, partial outputs for the chunk combine. MODE 2: the same code as MODE 0 under its
+// own symbol, used by the dense reference call so that traces keep the two apart.
 // K and V^T tiles are double-buffered in LDS: the global loads of tile j+1 are issued
 // before the products of tile j and land in the other buffer afterwards, one barrier per
 // tile. The accumulator is rescaled only when a query's running max grows by more than
@@ -101,7 +102,7 @@ __global__ __launch_bounds__(256, 2) void k_bsfa_bf16(const bf16* __restrict__ q
   const int nb = gridDim.x;
   const int bid = xcd_remap(blockIdx.x, nb);
   int bh, rows, a = 0, pos0 = 0;
-  if (MODE == 0) {
+  if (MODE != 1) {
     bh = bid / D.max_tiles;
     const int t = bid % D.max_tiles;
     if (t >= B.ntiles[bh]) return;
@@ -126,7 +127,7 @@ __global__ __launch_bounds__(256, 2) void k_bsfa_bf16(const bf16* __restrict__ q
   const bool qvalid = qr < rows;
   const bool wave_active = 32 * w < rows;  // a wave past the tile's last row only stages K / V
   int tok;
-  if (MODE == 0) tok = B.qperm[(size_t)bh * D.N + pos0 + (qvalid ? qr : 0)];
+  if (MODE != 1) tok = B.qperm[(size_t)bh * D.N + pos0 + (qvalid ? qr : 0)];
   else tok = B.probes[(size_t)bh * D.M + pos0 + (qvalid ? qr : 0)];
   const bf16* qrow = q + ((size_t)bh * D.N + tok) * DD;
   bf16x8 qreg[NC];
@@ -146,7 +147,7 @@ __global__ __launch_bounds__(256, 2) void k_bsfa_bf16(const bf16* __restrict__ q
   TileSeq ts;
   ts.single = MODE == 1;
   ts.used = false;
-  if (MODE == 0) {
+  if (MODE != 1) {
     ts.it.cols = B.cols + (size_t)bh * D.Cq * D.Ck;
     ts.it.koff = B.koff + (size_t)bh * (D.Ck + 1);
     const int* rp = B.row_ptr + (size_t)bh * (D.Cq + 1);
@@ -218,7 +219,7 @@ __global__ __launch_bounds__(256, 2) void k_bsfa_bf16(const bf16* __restrict__ q
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int v = 0; v < 16; ++v) mt = fmaxf(mt, s[kb][v]);
-    mt = fmaxf(mt, __shfl_xor(mt, 32, kWave)) * c2;
+    mt = fmaxf(mt, xor32(mt)) * c2;
     if (mt > m_run + 8.f) {
       const float alpha = __builtin_amdgcn_exp2f(m_run - mt);
       m_run = mt;
@@ -265,10 +266,10 @@ __global__ __launch_bounds__(256, 2) void k_bsfa_bf16(const bf16* __restrict__ q
     have = more;
   }
   // ---- normalise and store query l32's row: d = 32db + 8g + 4h + r
-  const float lsum = l_half + __shfl_xor(l_half, 32, kWave);
+  const float lsum = l_half + xor32(l_half);
   const float inv = 1.f / lsum;
   if (!qvalid) return;
-  if (MODE == 0) {
+  if (MODE != 1) {
     bf16* orow = (bf16*)out + ((size_t)bh * D.N + tok) * DD;
 #pragma unroll
     for (int db = 0; db < ND; ++db)
@@ -439,13 +440,21 @@ __global__ __launch_bounds__(128) void k_bsfa_f32(const float* __restrict__ q, D
   }
 }
 
-void launch_attend_sparse(const void* q, const Dims& D, const Bufs& B, void* o_sparse, float* o_psp, hipStream_t s) {
+void launch_attend_sparse(const void* q, const Dims& D, const Bufs& B, void* o_sparse, float* o_psp, hipStream_t s,
+                          bool dense) {
   const int nb = D.BH * D.max_tiles;
   if (D.dtype == 1) {
-    if (D.d == 128)
-      hipLaunchKernelGGL((k_bsfa_bf16<128, 0>), dim3(nb), dim3(256), 0, s, (const bf16*)q, D, B, o_sparse, o_psp);
-    else
-      hipLaunchKernelGGL((k_bsfa_bf16<64, 0>), dim3(nb), dim3(256), 0, s, (const bf16*)q, D, B, o_sparse, o_psp);
+    if (D.d == 128) {
+      if (dense)
+        hipLaunchKernelGGL((k_bsfa_bf16<128, 2>), dim3(nb), dim3(256), 0, s, (const bf16*)q, D, B, o_sparse, o_psp);
+      else
+        hipLaunchKernelGGL((k_bsfa_bf16<128, 0>), dim3(nb), dim3(256), 0, s, (const bf16*)q, D, B, o_sparse, o_psp);
+    } else {
+      if (dense)
+        hipLaunchKernelGGL((k_bsfa_bf16<64, 2>), dim3(nb), dim3(256), 0, s, (const bf16*)q, D, B, o_sparse, o_psp);
+      else
+        hipLaunchKernelGGL((k_bsfa_bf16<64, 0>), dim3(nb), dim3(256), 0, s, (const bf16*)q, D, B, o_sparse, o_psp);
+    }
   } else {
     if (D.d == 128)
       hipLaunchKernelGGL((k_bsfa_f32<128, 0>), dim3(nb), dim3(128), 0, s, (const float*)q, D, B, o_sparse, o_psp);

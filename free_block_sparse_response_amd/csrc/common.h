@@ -92,4 +92,12 @@ __device__ inline uint64_t wave_match(int key, bool valid, int bits) {
 
 __device__ inline int ceil_div(int a, int b) { return (a + b - 1) / b; }
 
+// Value of lane l ^ 32 (the other half of the wave), by gfx950's v_permlane32_swap (a VALU
+// swap of the two 32-lane halves, no LDS round trip).
+__device__ inline float xor32(float v) {
+  const unsigned u = __float_as_uint(v);
+  const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  return __uint_as_float(lane_id() < 32 ? r[1] : r[0]);
+}
+
 }  // namespace spr

@@ -12,7 +12,7 @@ void launch_route_probes(const Dims& D, const Bufs& B, hipStream_t s);
 void launch_identity_plan(const Dims& D, const Bufs& B, hipStream_t s);
 void launch_permute_kv(const void* k, const void* v, const Dims& D, const Bufs& B, hipStream_t s);
 void launch_attend_sparse(const void* q, const Dims& D, const Bufs& B, void* o_sparse, float* o_probe_sparse,
-                          hipStream_t s);
+                          hipStream_t s, bool dense = false);
 void launch_attend_probes(const void* q, const Dims& D, const Bufs& B, float* o_probe_dense, hipStream_t s);
 void launch_fit(const Dims& D, const Bufs& B, const float* o_psp, const float* o_dn, const float* w, float* coeffs,
                 hipStream_t s);

@@ -384,7 +384,7 @@ sparsepr_status sparsepr_dense_attention(sparsepr_plan_t p, const void* q, const
   Bufs B = carve(p->D, ws, nullptr);
   spr::launch_identity_plan(p->D, B, s);
   spr::launch_permute_kv(k, v, p->D, B, s);
-  spr::launch_attend_sparse(q, p->D, B, out, nullptr, s);
+  spr::launch_attend_sparse(q, p->D, B, out, nullptr, s, true);
   return hip_status();
 }
 
