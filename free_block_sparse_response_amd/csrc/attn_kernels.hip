@@ -78,26 +78,90 @@ struct TileSeq {
   }
 };
 
+// Walks the 64-key tiles of one work item over its key runs (the plan lists each query
+// group's runs). The runs are held one per lane, 64 at a time, and read out with v_readlane,
+// so stepping from tile to tile touches no memory. A run [lo, hi) starts its first tile at lo
+// rounded down to 8 keys (16-byte aligned rows of the transposed V); keys outside [lo, hi)
+// are masked.
+struct TileWalk {
+  const int2* runs;
+  int nr, r;      // runs of the item, current run
+  int rlo, rhi;   // this lane's run of the current batch of 64
+  int lo, hi, k0;
+  __device__ void load_batch(int base) {
+    const int i = base + lane_id();
+    const int2 v = i < nr ? runs[i] : make_int2(0, 0);
+    rlo = v.x;
+    rhi = v.y;
+  }
+  __device__ void set_run() {
+    if (r > 0 && (r & 63) == 0) load_batch(r);
+    lo = __builtin_amdgcn_readlane(rlo, r & 63);
+    hi = __builtin_amdgcn_readlane(rhi, r & 63);
+    k0 = lo & ~7;
+  }
+  __device__ bool first() {
+    r = 0;
+    if (nr <= 0) return false;
+    load_batch(0);
+    set_run();
+    return true;
+  }
+  __device__ bool first_single(int a, int b) {  // one run [a, b), no run list
+    r = 0;
+    nr = a < b ? 1 : 0;
+    rlo = a;
+    rhi = b;
+    lo = a;
+    hi = b;
+    k0 = a & ~7;
+    return nr > 0;
+  }
+  __device__ bool next() {
+    k0 += kKeyTile;
+    if (k0 < hi) return true;
+    if (++r >= nr) return false;
+    set_run();
+    return true;
+  }
+};
+
 // -------------------------------------------------------------------------------------
 // bf16 MFMA kernel. MODE 0: block-sparse tiles from the tile table, bf16 output in token
 // order (plus float rows for probes). MODE 1: probe rows (128 per block) over one chunk of
 // all keys, partial outputs for the chunk combine. MODE 2: the same code as MODE 0 under its
 // own symbol, used by the dense reference call so that traces keep the two apart.
-// K and V^T tiles are double-buffered in LDS: the global loads of tile j+1 are issued
-// before the products of tile j and land in the other buffer afterwards, one barrier per
-// tile. The accumulator is rescaled only when a query's running max grows by more than
-// 2^8 (the stale max keeps every exponent <= 2^8, exact enough in fp32 and bf16).
+//
+// Tiles move HBM -> LDS with direct-to-LDS loads (global_load_lds_dwordx4: lane i of a wave
+// lands 16 bytes at base + 16 i), so no registers stage them. Rows carry an XOR swizzle of
+// their 16-byte chunks so that the operand reads are bank-conflict free without padding.
+//
+// Pipeline per 64-key tile j (one barrier per tile):
+//   barrier: K(j+1) and V(j) have landed; everyone is done with K(j) and V(j-1)
+//   issue loads K(j+2) -> K buffer of j, V(j+1) -> V buffer of j-1
+//   S(j+1) = K(j+1) Q^T  (MFMA)   interleaved with   softmax of S(j) (VALU)
+//   O += V(j) P(j)       (MFMA)
+// The K rows of a 32-key block are read in the order pi (bits 2 and 3 of the row swapped),
+// which makes the eight scores a lane holds for one 16-key chunk eight consecutive keys, so
+// the V^T operand is a single 16-byte read per MFMA.
+// The accumulator is rescaled only when a query's running max grows by more than 2^8 (the
+// stale max keeps every exponent <= 2^8, exact enough in fp32 and bf16).
 // -------------------------------------------------------------------------------------
+__device__ inline int swap_bits23(int x) { return (x & ~12) | ((x & 4) << 1) | ((x & 8) >> 1); }
+
 template <int DD, int MODE>
 __global__ __launch_bounds__(256, 2) void k_bsfa_bf16(const bf16* __restrict__ q, Dims D, Bufs B, void* out,
                                                         float* psp) {
-  constexpr int KS = DD + 8;          // K row stride in LDS (elements)
-  constexpr int VS = kKeyTile + 8;    // V^T row stride in LDS (elements)
-  constexpr int NC = DD / 16;         // k-chunks of the QK^T product
-  constexpr int ND = DD / 32;         // 32-wide d blocks of the output
-  constexpr int KL = (kKeyTile * DD / 8) / 256;  // 16-byte loads per thread per tile (K and V each)
-  __shared__ __attribute__((aligned(16))) bf16 Ks[2][kKeyTile * KS];
-  __shared__ __attribute__((aligned(16))) bf16 Vs[2][DD * VS];
+  constexpr int KT = kKeyTile;          // keys per tile
+  constexpr int KRB = DD * 2;           // K row bytes (256 or 128)
+  constexpr int KW = KRB / 16;          // 16-byte slots per K row
+  constexpr int KR = 64 / KW;           // K rows per wave-wide direct load
+  constexpr int KI = KT * KRB / 4096;   // direct loads per wave per K tile (4 waves, 1 KB each)
+  constexpr int VI = DD * KT * 2 / 4096;  // and per V^T tile (rows of 128 bytes)
+  constexpr int NC = DD / 16;           // k-chunks of the QK^T product
+  constexpr int ND = DD / 32;           // 32-wide d blocks of the output
+  static_assert(KT == 64 && (DD == 64 || DD == 128), "tile shape");
+  __shared__ __attribute__((aligned(1024))) bf16 Kb0[KT * DD], Kb1[KT * DD], Vb0[DD * KT], Vb1[DD * KT];
 
   const int nb = gridDim.x;
   const int bid = xcd_remap(blockIdx.x, nb);
@@ -120,12 +184,13 @@ __global__ __launch_bounds__(256, 2) void k_bsfa_bf16(const bf16* __restrict__ q
     a = rem % D.pch;  // key chunk
     rows = min(kAttnQT, D.M - pos0);
   }
-  const int tid = threadIdx.x, w = tid / kWave, l = lane_id(), h = l >> 5, l32 = l & 31;
+  const int tid = threadIdx.x, l = lane_id(), h = l >> 5, l32 = l & 31;
+  const int w = __builtin_amdgcn_readfirstlane(tid / kWave);
 
   // ---- Q^T operand in registers: query (32w + l32), d-slots 16c + 8h .. +7
   const int qr = 32 * w + l32;
   const bool qvalid = qr < rows;
-  const bool wave_active = 32 * w < rows;  // a wave past the tile's last row only stages K / V
+  const bool wave_active = 32 * w < rows;  // a wave past the tile's last row only loads K / V
   int tok;
   if (MODE != 1) tok = B.qperm[(size_t)bh * D.N + pos0 + (qvalid ? qr : 0)];
   else tok = B.probes[(size_t)bh * D.M + pos0 + (qvalid ? qr : 0)];
@@ -144,127 +209,192 @@ __global__ __launch_bounds__(256, 2) void k_bsfa_bf16(const bf16* __restrict__ q
 
   const bf16* kpb = (const bf16*)B.kp + (size_t)bh * D.Npad * DD;
   const bf16* vtb = (const bf16*)B.vpt + (size_t)bh * DD * D.Npad;
-  TileSeq ts;
-  ts.single = MODE == 1;
-  ts.used = false;
-  if (MODE != 1) {
-    ts.it.cols = B.cols + (size_t)bh * D.Cq * D.Ck;
-    ts.it.koff = B.koff + (size_t)bh * (D.Ck + 1);
-    const int* rp = B.row_ptr + (size_t)bh * (D.Cq + 1);
-    ts.it.c = rp[a];
-    ts.it.cend = rp[a + 1];
-  }
-  const int clo = MODE == 1 ? a * D.pkc : 0;
-  bool have = ts.first(clo, MODE == 1 ? min(D.N, clo + D.pkc) : 0);
 
-  // thread's share of a tile: K rows r = c / (DD/8), 16-byte column c8; V^T rows / columns
-  bf16x8 kreg[KL], vreg[KL];
-  auto load_tile = [&](int k0) {
-#pragma unroll
-    for (int i = 0; i < KL; ++i) {
-      const int c = tid + 256 * i;
-      const int r = c / (DD / 8), c8 = c % (DD / 8);
-      kreg[i] = *reinterpret_cast<const bf16x8*>(kpb + (size_t)(k0 + r) * DD + c8 * 8);
-      const int rv = c / (kKeyTile / 8), cv = c % (kKeyTile / 8);
-      vreg[i] = *reinterpret_cast<const bf16x8*>(vtb + (size_t)rv * D.Npad + k0 + cv * 8);
-    }
-  };
-  auto store_tile = [&](int buf) {
-#pragma unroll
-    for (int i = 0; i < KL; ++i) {
-      const int c = tid + 256 * i;
-      const int r = c / (DD / 8), c8 = c % (DD / 8);
-      *reinterpret_cast<bf16x8*>(&Ks[buf][r * KS + c8 * 8]) = kreg[i];
-      const int rv = c / (kKeyTile / 8), cv = c % (kKeyTile / 8);
-      *reinterpret_cast<bf16x8*>(&Vs[buf][rv * VS + cv * 8]) = vreg[i];
-    }
-  };
-  int cur = 0;
-  if (have) {
-    load_tile(ts.k0);
-    store_tile(0);
+  // Tile layout in LDS, no padding: 16-byte slot s of row r holds chunk s ^ swz(r), with
+  // swz(r) = r & 15 for 16-slot rows and (r >> 1) & 7 for 8-slot rows, so the 16 rows one
+  // operand read touches fall on 16 distinct bank groups. Wave-wide direct load g fills
+  // rows [64g / slots, ...) contiguously; the chunk a lane fetches depends on its lane and
+  // wave only, so its source is one lane offset plus a per-load scalar.
+  auto swz = [](int r, int slots) { return slots == 16 ? (r & 15) : ((r >> 1) & 7); };
+  unsigned klane, vlane;
+  {
+    const int r = KR * w + l / KW;  // row within the wave's first load (load g = 4 i + w)
+    klane = (unsigned)(r * KRB + 16 * ((l % KW) ^ swz(r, KW)));
+    const int rv = 8 * w + l / 8;
+    vlane = (unsigned)(rv * 2 * D.Npad + 16 * ((l % 8) ^ swz(rv, 8)));
   }
-  __syncthreads();
-  while (have) {
-    const int k0 = ts.k0, lo = ts.lo, hi = ts.hi;
-    const bool more = ts.next();
-    if (more) load_tile(ts.k0);
-    if (wave_active) {
-    // ---- S^T = K Q^T for two 32-key blocks
-    const bf16* Kc = Ks[cur];
-    f32x16 s[2];
+  auto issue_k = [&](bf16* dst, int k0) {
+    const char* src = (const char*)(kpb + (size_t)k0 * DD);
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
+    for (int i = 0; i < KI; ++i)
+      __builtin_amdgcn_global_load_lds(src + (size_t)i * 4 * KR * KRB + klane, dst + (4 * i + w) * 512, 16, 0, 0);
+  };
+  auto issue_v = [&](bf16* dst, int k0) {
+    const char* src = (const char*)(vtb + k0);
 #pragma unroll
-      for (int v = 0; v < 16; ++v) s[kb][v] = 0.f;
-#pragma unroll
-      for (int c = 0; c < NC; ++c) {
-        const bf16x8 av = *reinterpret_cast<const bf16x8*>(&Kc[(kb * 32 + l32) * KS + 16 * c + 8 * h]);
-        s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, qreg[c], s[kb], 0, 0, 0);
-      }
-    }
-    // ---- online softmax (scores of query l32; key = k0 + 32kb + 8(v/4) + 4h + v%4)
-    if (k0 < lo || k0 + kKeyTile > hi) {
-      const int vlo = lo - k0, vhi = hi - k0;
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          const int kk = 32 * kb + 8 * (v >> 2) + 4 * h + (v & 3);
-          if (kk < vlo || kk >= vhi) s[kb][v] = -INFINITY;
-        }
-    }
-    float mt = s[0][0];
+    for (int i = 0; i < VI; ++i)
+      __builtin_amdgcn_global_load_lds(src + (size_t)i * 32 * 2 * D.Npad + vlane, dst + (4 * i + w) * 512, 16, 0, 0);
+  };
+
+  // operand reads. K: row 32 kb + pi(l32), chunk 2c + h -> byte (kaddr ^ 32c) + kb * 32 rows;
+  // V^T: row 32 db + l32, chunk 2cc + h -> byte (vaddr ^ 32cc) + db * 32 rows.
+  const int prow = swap_bits23(l32);
+  const unsigned kaddr = (unsigned)(prow * KRB + 16 * (h ^ swz(prow, KW)));
+  const unsigned vaddr = (unsigned)(l32 * 128 + 16 * (h ^ swz(l32, 8)));
+  auto qk = [&](const bf16* Kc, f32x16 (&s)[2]) {
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int v = 0; v < 16; ++v) mt = fmaxf(mt, s[kb][v]);
+      for (int v = 0; v < 16; ++v) s[kb][v] = 0.f;
+#pragma unroll
+    for (int c = 0; c < NC; ++c)
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        const bf16x8 av = *reinterpret_cast<const bf16x8*>((const char*)Kc + kb * 32 * KRB + (kaddr ^ (32u * c)));
+        s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, qreg[c], s[kb], 0, 0, 0);
+      }
+  };
+  // keys outside [lo, hi) of an edge tile get score -inf
+  auto mask = [&](f32x16 (&s)[2], int k0, int lo, int hi) {
+    const int vlo = lo - k0, vhi = hi - k0;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int kk = 32 * kb + 16 * (v >> 3) + 8 * h + (v & 7);  // key of score v (pi order)
+        if (kk < vlo || kk >= vhi) s[kb][v] = -INFINITY;
+      }
+  };
+  // exponentials of one tile against the running max, raised lazily: mu is the max this tile
+  // uses (the tile max when it exceeds the running one by more than 2^8, else the running
+  // max). Returns the P^T operands (chunk cc = 2 kb + sub) and the tile's share of the row sum.
+  auto expo = [&](f32x16 (&s)[2], bf16x8 (&pb)[4], float& ps, float& mu) {
+    float mx[4];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      const int kb = t >> 1, b = 8 * (t & 1);
+      mx[t] = fmaxf(fmaxf(fmaxf(s[kb][b], s[kb][b + 1]), fmaxf(s[kb][b + 2], s[kb][b + 3])),
+                    fmaxf(fmaxf(s[kb][b + 4], s[kb][b + 5]), fmaxf(s[kb][b + 6], s[kb][b + 7])));
+    }
+    float mt = fmaxf(fmaxf(mx[0], mx[1]), fmaxf(mx[2], mx[3]));
     mt = fmaxf(mt, xor32(mt)) * c2;
-    if (mt > m_run + 8.f) {
-      const float alpha = __builtin_amdgcn_exp2f(m_run - mt);
-      m_run = mt;
+    mu = mt > m_run + 8.f ? mt : m_run;
+    float pt[4];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      const int kb = t >> 1, b = 8 * (t & 1);
+      float e[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) e[u] = __builtin_amdgcn_exp2f(fmaf(s[kb][b + u], c2, -mu));
+      pt[t] = ((e[0] + e[1]) + (e[2] + e[3])) + ((e[4] + e[5]) + (e[6] + e[7]));
+#pragma unroll
+      for (int u = 0; u < 8; ++u) pb[t][u] = (bf16)e[u];
+    }
+    ps = (pt[0] + pt[1]) + (pt[2] + pt[3]);
+  };
+  // moves the accumulator to the new max when any lane of the wave raised it
+  auto rescale = [&](float mu, float ps) {
+    if (__builtin_amdgcn_ballot_w64(mu != m_run)) {
+      const float alpha = __builtin_amdgcn_exp2f(m_run - mu);
+      m_run = mu;
       l_half *= alpha;
 #pragma unroll
       for (int i = 0; i < ND; ++i)
 #pragma unroll
         for (int v = 0; v < 16; ++v) o[i][v] *= alpha;
     }
-    float ps = 0.f;
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const float p = __builtin_amdgcn_exp2f(fmaf(s[kb][v], c2, -m_run));
-        s[kb][v] = p;
-        ps += p;
-      }
     l_half += ps;
-    // ---- O^T += V^T P^T over four 16-key chunks
-    const bf16* Vc = Vs[cur];
+  };
+  auto pv = [&](const bf16* Vc, const bf16x8 (&pb)[4]) {
 #pragma unroll
-    for (int cc = 0; cc < 4; ++cc) {
-      const int kb = cc >> 1, sub = cc & 1;
-      bf16x8 pb;
-#pragma unroll
-      for (int t = 0; t < 8; ++t) pb[t] = (bf16)s[kb][8 * sub + t];
-      const int key0 = 32 * kb + 16 * sub + 4 * h;
+    for (int cc = 0; cc < 4; ++cc)
 #pragma unroll
       for (int db = 0; db < ND; ++db) {
-        const bf16* vr = &Vc[(32 * db + l32) * VS + key0];
-        const bf16x4 v0 = *reinterpret_cast<const bf16x4*>(vr);
-        const bf16x4 v1 = *reinterpret_cast<const bf16x4*>(vr + 8);
-        bf16x8 av;
-        av[0] = v0[0]; av[1] = v0[1]; av[2] = v0[2]; av[3] = v0[3];
-        av[4] = v1[0]; av[5] = v1[1]; av[6] = v1[2]; av[7] = v1[3];
-        o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, pb, o[db], 0, 0, 0);
+        const bf16x8 av = *reinterpret_cast<const bf16x8*>((const char*)Vc + db * 32 * 128 + (vaddr ^ (32u * cc)));
+        o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, pb[cc], o[db], 0, 0, 0);
+      }
+  };
+
+  TileWalk ts;
+  bool hasc;
+  if (MODE != 1) {
+    ts.runs = B.runs + (size_t)bh * D.Cq * D.Ck + B.row_ptr[(size_t)bh * (D.Cq + 1) + a];
+    ts.nr = B.nruns[(size_t)bh * D.Cq + a];
+    hasc = ts.first();
+  } else {
+    const int clo = a * D.pkc;
+    hasc = ts.first_single(clo, min(D.N, clo + D.pkc));
+  }
+  // tile descriptors: current (j), next (j+1), after next (j+2)
+  int k0c = 0, loc = 0, hic = 0, k0n = 0, lon = 0, hin = 0;
+  f32x16 sa[2], sb[2];
+  if (hasc) {
+    k0c = ts.k0; loc = ts.lo; hic = ts.hi;
+    issue_k(Kb0, k0c);
+    issue_v(Vb0, k0c);
+  }
+  bool hasn = hasc && ts.next();
+  if (hasn) {
+    k0n = ts.k0; lon = ts.lo; hin = ts.hi;
+    issue_k(Kb1, k0n);
+  }
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  if (hasc && wave_active) qk(Kb0, sa);
+
+  // one tile: Kn = K buffer of tile j+1, Kc = K buffer of tile j (refilled with j+2),
+  // Vc = V buffer of tile j, Vn = V buffer of tile j+1
+  auto step = [&](f32x16 (&scur)[2], f32x16 (&snext)[2], bf16* Kc, const bf16* Kn, const bf16* Vc, bf16* Vn) {
+    __builtin_amdgcn_s_waitcnt(0);  // this wave's direct-to-LDS loads have landed
+    __syncthreads();
+    bool hasnn = false;
+    int k0nn = 0, lonn = 0, hinn = 0;
+    if (hasn) {
+      hasnn = ts.next();
+      if (hasnn) {
+        k0nn = ts.k0; lonn = ts.lo; hinn = ts.hi;
+        issue_k(Kc, k0nn);
+      }
+      issue_v(Vn, k0n);
+    }
+    if (wave_active) {
+      if (k0c < loc || k0c + KT > hic) mask(scur, k0c, loc, hic);
+      bf16x8 pb[4];
+      float ps, mu;
+      if (hasn) {
+        // S(j+1) on the matrix cores while the vector units exponentiate S(j)
+        qk(Kn, snext);
+        expo(scur, pb, ps, mu);
+        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+#pragma unroll
+        for (int i = 0; i < 2 * NC; ++i) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          if (i + 2 < 2 * NC) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x002, 128 / (2 * NC), 0);
+        }
+      } else {
+        expo(scur, pb, ps, mu);
+      }
+      rescale(mu, ps);
+      pv(Vc, pb);
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+#pragma unroll
+      for (int i = 0; i < 4 * ND; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        if (i + 2 < 4 * ND) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
       }
     }
-    }  // wave_active
-    if (more) store_tile(cur ^ 1);
-    __syncthreads();
-    cur ^= 1;
-    have = more;
+    hasc = hasn;
+    k0c = k0n; loc = lon; hic = hin;
+    hasn = hasnn;
+    k0n = k0nn; lon = lonn; hin = hinn;
+  };
+  while (hasc) {
+    step(sa, sb, Kb0, Kb1, Vb0, Vb1);
+    if (!hasc) break;
+    step(sb, sa, Kb1, Kb0, Vb1, Vb0);
   }
+
   // ---- normalise and store query l32's row: d = 32db + 8g + 4h + r
   const float lsum = l_half + xor32(l_half);
   const float inv = 1.f / lsum;

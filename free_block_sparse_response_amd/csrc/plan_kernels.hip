@@ -1300,7 +1300,19 @@ __global__ __launch_bounds__(1024) void k_route_emit(Dims D, Bufs B) {
   int tot;
   const bool f = tid < Ck && flag[tid];
   const int pos = block_excl_scan_bool<1024>(f, &tot, ws);
-  if (f) B.cols[(size_t)bh * D.Cq * D.Ck + B.row_ptr[(size_t)bh * (D.Cq + 1) + a] + pos] = tid;
+  const int rp = B.row_ptr[(size_t)bh * (D.Cq + 1) + a];
+  if (f) B.cols[(size_t)bh * D.Cq * D.Ck + rp + pos] = tid;
+  // key runs: maximal stretches of consecutive selected groups, whose keys are contiguous
+  // after the permutation, as [koff[first], koff[last + 1])
+  const bool st = f && (tid == 0 || !flag[tid - 1]);
+  const bool en = f && (tid + 1 == Ck || !flag[tid + 1]);
+  int nr;
+  const int rs = block_excl_scan_bool<1024>(st, &nr, ws);
+  const int* ko = B.koff + (size_t)bh * (D.Ck + 1);
+  int2* runs = B.runs + (size_t)bh * D.Cq * D.Ck + rp;
+  if (st) runs[rs].x = ko[tid];
+  if (en) runs[rs + (st ? 1 : 0) - 1].y = ko[tid + 1];
+  if (tid == 0) B.nruns[(size_t)bh * D.Cq + a] = nr;
 }
 
 // =====================================================================================
@@ -1435,6 +1447,8 @@ __global__ void k_identity_plan(Dims D, Bufs B) {
     B.row_ptr[(size_t)bh * (D.Cq + 1)] = 0;
     B.row_ptr[(size_t)bh * (D.Cq + 1) + 1] = 1;
     B.cols[(size_t)bh * D.Cq * D.Ck] = 0;
+    B.runs[(size_t)bh * D.Cq * D.Ck] = make_int2(0, D.N);
+    B.nruns[(size_t)bh * D.Cq] = 1;
     B.qst[bh].c_final = 1;
     B.kst[bh].c_final = 1;
   }

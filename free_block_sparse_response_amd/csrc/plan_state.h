@@ -87,6 +87,8 @@ struct Bufs {
   int* jsel;         // [BH][Cq]
   int* row_ptr;      // [BH][Cq+1]
   int* cols;         // [BH][Cq*Ck]
+  int2* runs;        // [BH][Cq*Ck] key runs [lo, hi) of merged consecutive selected groups (CSR as cols)
+  int* nruns;        // [BH][Cq]
   RouteInfo* rinfo;  // [BH]
   int* pcount;       // [BH][Cq]
   int* poff;         // [BH][Cq+1]

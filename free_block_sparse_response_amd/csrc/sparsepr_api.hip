@@ -110,6 +110,8 @@ Bufs carve(const Dims& D, void* base, size_t* total) {
   B.jsel = c.take<int>(BH * D.Cq);
   B.row_ptr = c.take<int>(BH * (D.Cq + 1));
   B.cols = c.take<int>(BH * D.Cq * D.Ck);
+  B.runs = c.take<int2>(BH * D.Cq * D.Ck);
+  B.nruns = c.take<int>(BH * D.Cq);
   B.rinfo = c.take<spr::RouteInfo>(BH);
   B.pcount = c.take<int>(BH * D.Cq);
   B.poff = c.take<int>(BH * (D.Cq + 1));
