@@ -5,17 +5,16 @@
 // Query rows of one query group are taken 128 at a time (one tile); the keys are the
 // union of the selected key groups, which the permutation made contiguous per group, so
 // consecutive selected groups merge into one key run. Softmax is renormalised over the
-// retained keys only (online softmax across 64-key tiles).
+// retained keys only (online softmax across key tiles).
 //
 // bf16 path, per workgroup of 4 waves (32 query rows each):
 //   S^T = K Q^T   with v_mfma_f32_32x32x16_bf16: A = K tile rows from LDS, B = Q^T kept in
-//                 registers; each lane then holds the scores of ONE query (lane % 32) for 32
+//                 registers; each lane then holds the scores of ONE query (lane % 32) for 16
 //                 keys, so the row max / sum are in-lane plus one cross-half exchange.
 //   O^T = V^T P^T with the same MFMA: B = P^T is the score registers converted to bf16 in
 //                 place (no shuffles); A = V^T comes from the transposed V layout that the
-//                 permutation pass writes, read as two 8-byte LDS loads per operand.
-// K rows are 16 B-padded in LDS and V^T rows 16 B-padded so both operand reads are
-// bank-conflict free; exp2 with the log2(e) factor folded into the score scale.
+//                 permutation pass writes, one 16-byte LDS read per operand.
+// exp2 with the log2(e) factor folded into the score scale.
 #include "common.h"
 #include "plan_state.h"
 #include "launch.h"
@@ -78,11 +77,12 @@ struct TileSeq {
   }
 };
 
-// Walks the 64-key tiles of one work item over its key runs (the plan lists each query
+// Walks the KT-key tiles of one work item over its key runs (the plan lists each query
 // group's runs). The runs are held one per lane, 64 at a time, and read out with v_readlane,
 // so stepping from tile to tile touches no memory. A run [lo, hi) starts its first tile at lo
 // rounded down to 8 keys (16-byte aligned rows of the transposed V); keys outside [lo, hi)
 // are masked.
+template <int KT>
 struct TileWalk {
   const int2* runs;
   int nr, r;      // runs of the item, current run
@@ -118,7 +118,7 @@ struct TileWalk {
     return nr > 0;
   }
   __device__ bool next() {
-    k0 += kKeyTile;
+    k0 += KT;
     if (k0 < hi) return true;
     if (++r >= nr) return false;
     set_run();
@@ -132,35 +132,35 @@ struct TileWalk {
 // all keys, partial outputs for the chunk combine. MODE 2: the same code as MODE 0 under its
 // own symbol, used by the dense reference call so that traces keep the two apart.
 //
-// Tiles move HBM -> LDS with direct-to-LDS loads (global_load_lds_dwordx4: lane i of a wave
-// lands 16 bytes at base + 16 i), so no registers stage them. Rows carry an XOR swizzle of
-// their 16-byte chunks so that the operand reads are bank-conflict free without padding.
+// Tiles of 32 keys move HBM -> registers -> LDS, two steps ahead: a step issues the global
+// loads of K(j+2) and V(j+1) and stores K(j+1) and V(j), loaded a step earlier, at its end
+// (direct-to-LDS loads were tried: while they are in flight the operand reads of every wave
+// on the CU stall). Rows carry an XOR swizzle of their 16-byte chunks so that the operand
+// reads are bank-conflict free without padding.
 //
-// Pipeline per 64-key tile j (one barrier per tile):
-//   barrier: K(j+1) and V(j) have landed; everyone is done with K(j) and V(j-1)
-//   issue loads K(j+2) -> K buffer of j, V(j+1) -> V buffer of j-1
-//   S(j+1) = K(j+1) Q^T  (MFMA)   interleaved with   softmax of S(j) (VALU)
-//   O += V(j) P(j)       (MFMA)
-// The K rows of a 32-key block are read in the order pi (bits 2 and 3 of the row swapped),
-// which makes the eight scores a lane holds for one 16-key chunk eight consecutive keys, so
-// the V^T operand is a single 16-byte read per MFMA.
-// The accumulator is rescaled only when a query's running max grows by more than 2^8 (the
-// stale max keeps every exponent <= 2^8, exact enough in fp32 and bf16).
+// Step j (one barrier): S(j) = K(j) Q^T on the matrix cores; then O += V(j-1) P(j-1), each
+// MFMA followed by a slice of the softmax that turns S(j) into P(j) (P is double-buffered in
+// registers). The K rows of a 32-key block are read in the order pi (bits 2 and 3 of the row
+// swapped), which makes the eight scores a lane holds for one 16-key chunk eight consecutive
+// keys, so the V^T operand is a single 16-byte read per MFMA.
+// The accumulator is rescaled only when a query's running max grows by more than 2^16 (the
+// stale max keeps every exponential <= 2^16: far from overflow in fp32, and bf16 keeps its
+// relative precision at any magnitude).
 // -------------------------------------------------------------------------------------
 __device__ inline int swap_bits23(int x) { return (x & ~12) | ((x & 4) << 1) | ((x & 8) >> 1); }
 
 template <int DD, int MODE>
 __global__ __launch_bounds__(256, 2) void k_bsfa_bf16(const bf16* __restrict__ q, Dims D, Bufs B, void* out,
                                                         float* psp) {
-  constexpr int KT = kKeyTile;          // keys per tile
+  constexpr int KT = 32;                // keys per tile
   constexpr int KRB = DD * 2;           // K row bytes (256 or 128)
-  constexpr int KW = KRB / 16;          // 16-byte slots per K row
-  constexpr int KR = 64 / KW;           // K rows per wave-wide direct load
-  constexpr int KI = KT * KRB / 4096;   // direct loads per wave per K tile (4 waves, 1 KB each)
-  constexpr int VI = DD * KT * 2 / 4096;  // and per V^T tile (rows of 128 bytes)
+  constexpr int KW = KRB / 16;          // 16-byte slots per K row (16 or 8)
+  constexpr int KR = 64 / KW;           // K rows per wave-wide 1 KB load
+  constexpr int KI = KT * KRB / 4096;   // 1 KB loads per wave per K tile (4 waves)
+  constexpr int VI = DD * KT * 2 / 4096;  // and per V^T tile (rows of 64 bytes)
   constexpr int NC = DD / 16;           // k-chunks of the QK^T product
   constexpr int ND = DD / 32;           // 32-wide d blocks of the output
-  static_assert(KT == 64 && (DD == 64 || DD == 128), "tile shape");
+  static_assert((DD == 64 || DD == 128) && KI >= 1 && VI >= 1, "tile shape");
   __shared__ __attribute__((aligned(1024))) bf16 Kb0[KT * DD], Kb1[KT * DD], Vb0[DD * KT], Vb1[DD * KT];
 
   const int nb = gridDim.x;
@@ -190,7 +190,7 @@ __global__ __launch_bounds__(256, 2) void k_bsfa_bf16(const bf16* __restrict__ q
   // ---- Q^T operand in registers: query (32w + l32), d-slots 16c + 8h .. +7
   const int qr = 32 * w + l32;
   const bool qvalid = qr < rows;
-  const bool wave_active = 32 * w < rows;  // a wave past the tile's last row only loads K / V
+  const bool wave_active = 32 * w < rows;  // a wave past the tile's last row only stages K / V
   int tok;
   if (MODE != 1) tok = B.qperm[(size_t)bh * D.N + pos0 + (qvalid ? qr : 0)];
   else tok = B.probes[(size_t)bh * D.M + pos0 + (qvalid ? qr : 0)];
@@ -211,89 +211,97 @@ __global__ __launch_bounds__(256, 2) void k_bsfa_bf16(const bf16* __restrict__ q
   const bf16* vtb = (const bf16*)B.vpt + (size_t)bh * DD * D.Npad;
 
   // Tile layout in LDS, no padding: 16-byte slot s of row r holds chunk s ^ swz(r), with
-  // swz(r) = r & 15 for 16-slot rows and (r >> 1) & 7 for 8-slot rows, so the 16 rows one
-  // operand read touches fall on 16 distinct bank groups. Wave-wide direct load g fills
-  // rows [64g / slots, ...) contiguously; the chunk a lane fetches depends on its lane and
+  // swz(r) = r & 15 for 16-slot K rows, (r >> 1) & 7 for 8-slot K rows and (r >> 2) & 3 for
+  // the 4-slot V^T rows, so the 16 rows one operand read touches fall on distinct bank groups.
+  // Each wave stages whole 1 KB row blocks; the chunk a lane fetches depends on its lane and
   // wave only, so its source is one lane offset plus a per-load scalar.
-  auto swz = [](int r, int slots) { return slots == 16 ? (r & 15) : ((r >> 1) & 7); };
+  auto kswz = [](int r) { return KW == 16 ? (r & 15) : ((r >> 1) & 7); };
+  auto vswz = [](int r) { return (r >> 2) & 3; };
   unsigned klane, vlane;
   {
-    const int r = KR * w + l / KW;  // row within the wave's first load (load g = 4 i + w)
-    klane = (unsigned)(r * KRB + 16 * ((l % KW) ^ swz(r, KW)));
-    const int rv = 8 * w + l / 8;
-    vlane = (unsigned)(rv * 2 * D.Npad + 16 * ((l % 8) ^ swz(rv, 8)));
+    const int r = KR * w + l / KW;  // row of this lane in the wave's first load (load g = 4 i + w)
+    klane = (unsigned)(r * KRB + 16 * ((l % KW) ^ kswz(r)));
+    const int rv = 16 * w + l / 4;
+    vlane = (unsigned)(rv * 2 * D.Npad + 16 * ((l % 4) ^ vswz(rv)));
   }
-  auto issue_k = [&](bf16* dst, int k0) {
+  // Tile staging through registers, two steps deep: the global loads issued in one step are
+  // stored to LDS at the end of the next, so a load has about two steps to arrive.
+  struct Stage {
+    bf16x8 k[KI], v[VI];
+  };
+  auto load_k = [&](Stage& st, int k0) {
     const char* src = (const char*)(kpb + (size_t)k0 * DD);
 #pragma unroll
-    for (int i = 0; i < KI; ++i)
-      __builtin_amdgcn_global_load_lds(src + (size_t)i * 4 * KR * KRB + klane, dst + (4 * i + w) * 512, 16, 0, 0);
+    for (int i = 0; i < KI; ++i) st.k[i] = *reinterpret_cast<const bf16x8*>(src + i * 4 * KR * KRB + klane);
   };
-  auto issue_v = [&](bf16* dst, int k0) {
+  auto load_v = [&](Stage& st, int k0) {
     const char* src = (const char*)(vtb + k0);
 #pragma unroll
-    for (int i = 0; i < VI; ++i)
-      __builtin_amdgcn_global_load_lds(src + (size_t)i * 32 * 2 * D.Npad + vlane, dst + (4 * i + w) * 512, 16, 0, 0);
+    for (int i = 0; i < VI; ++i) st.v[i] = *reinterpret_cast<const bf16x8*>(src + (size_t)i * 128 * D.Npad + vlane);
+  };
+  auto store_k = [&](const Stage& st, bf16* dst) {
+#pragma unroll
+    for (int i = 0; i < KI; ++i) *reinterpret_cast<bf16x8*>(dst + (4 * i + w) * 512 + 8 * l) = st.k[i];
+  };
+  auto store_v = [&](const Stage& st, bf16* dst) {
+#pragma unroll
+    for (int i = 0; i < VI; ++i) *reinterpret_cast<bf16x8*>(dst + (4 * i + w) * 512 + 8 * l) = st.v[i];
   };
 
-  // operand reads. K: row 32 kb + pi(l32), chunk 2c + h -> byte (kaddr ^ 32c) + kb * 32 rows;
+  // operand reads. K: row pi(l32), chunk 2c + h -> byte kaddr ^ 32c;
   // V^T: row 32 db + l32, chunk 2cc + h -> byte (vaddr ^ 32cc) + db * 32 rows.
   const int prow = swap_bits23(l32);
-  const unsigned kaddr = (unsigned)(prow * KRB + 16 * (h ^ swz(prow, KW)));
-  const unsigned vaddr = (unsigned)(l32 * 128 + 16 * (h ^ swz(l32, 8)));
-  auto qk = [&](const bf16* Kc, f32x16 (&s)[2]) {
+  const unsigned kaddr = (unsigned)(prow * KRB + 16 * (h ^ kswz(prow)));
+  const unsigned vaddr = (unsigned)(l32 * 64 + 16 * (h ^ vswz(l32)));
+  // The per-chunk addresses are formed where they are used (one v_xor each): an empty asm
+  // makes the base opaque so that the compiler does not keep all of them live across the loop.
+  auto kread = [&](const bf16* Kc, unsigned kb, int c) {
+    return *reinterpret_cast<const bf16x8*>((const char*)Kc + (kb ^ (32u * c)));
+  };
+  auto vread = [&](const bf16* Vc, unsigned vb, int i) {  // i = cc * ND + db
+    const int cc = i / ND, db = i % ND;
+    return *reinterpret_cast<const bf16x8*>((const char*)Vc + db * 32 * 64 + (vb ^ (32u * cc)));
+  };
+  // S^T = K Q^T of one tile; K operands read two k-chunks ahead
+  auto qk = [&](const bf16* Kc, f32x16& s) {
+    unsigned kb = kaddr;
+    asm volatile("" : "+v"(kb));
+    bf16x8 ka[NC];
+    ka[0] = kread(Kc, kb, 0);
+    ka[1] = kread(Kc, kb, 1);
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int v = 0; v < 16; ++v) s[kb][v] = 0.f;
-#pragma unroll
-    for (int c = 0; c < NC; ++c)
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        const bf16x8 av = *reinterpret_cast<const bf16x8*>((const char*)Kc + kb * 32 * KRB + (kaddr ^ (32u * c)));
-        s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, qreg[c], s[kb], 0, 0, 0);
+    for (int c = 0; c < NC; ++c) {
+      if (c == 0) {
+        const f32x16 z = {};
+        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[0], qreg[0], z, 0, 0, 0);
+      } else {
+        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[c], qreg[c], s, 0, 0, 0);
       }
-  };
-  // keys outside [lo, hi) of an edge tile get score -inf
-  auto mask = [&](f32x16 (&s)[2], int k0, int lo, int hi) {
-    const int vlo = lo - k0, vhi = hi - k0;
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const int kk = 32 * kb + 16 * (v >> 3) + 8 * h + (v & 7);  // key of score v (pi order)
-        if (kk < vlo || kk >= vhi) s[kb][v] = -INFINITY;
-      }
-  };
-  // exponentials of one tile against the running max, raised lazily: mu is the max this tile
-  // uses (the tile max when it exceeds the running one by more than 2^8, else the running
-  // max). Returns the P^T operands (chunk cc = 2 kb + sub) and the tile's share of the row sum.
-  auto expo = [&](f32x16 (&s)[2], bf16x8 (&pb)[4], float& ps, float& mu) {
-    float mx[4];
-#pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      const int kb = t >> 1, b = 8 * (t & 1);
-      mx[t] = fmaxf(fmaxf(fmaxf(s[kb][b], s[kb][b + 1]), fmaxf(s[kb][b + 2], s[kb][b + 3])),
-                    fmaxf(fmaxf(s[kb][b + 4], s[kb][b + 5]), fmaxf(s[kb][b + 6], s[kb][b + 7])));
+      if (c + 2 < NC) ka[c + 2] = kread(Kc, kb, c + 2);
+      __builtin_amdgcn_sched_barrier(0);
     }
-    float mt = fmaxf(fmaxf(mx[0], mx[1]), fmaxf(mx[2], mx[3]));
-    mt = fmaxf(mt, xor32(mt)) * c2;
-    mu = mt > m_run + 8.f ? mt : m_run;
-    float pt[4];
-#pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      const int kb = t >> 1, b = 8 * (t & 1);
-      float e[8];
-#pragma unroll
-      for (int u = 0; u < 8; ++u) e[u] = __builtin_amdgcn_exp2f(fmaf(s[kb][b + u], c2, -mu));
-      pt[t] = ((e[0] + e[1]) + (e[2] + e[3])) + ((e[4] + e[5]) + (e[6] + e[7]));
-#pragma unroll
-      for (int u = 0; u < 8; ++u) pb[t][u] = (bf16)e[u];
-    }
-    ps = (pt[0] + pt[1]) + (pt[2] + pt[3]);
   };
-  // moves the accumulator to the new max when any lane of the wave raised it
-  auto rescale = [&](float mu, float ps) {
+  // keys outside [lo, hi) of an edge tile get score -inf; score v is key
+  // 16 (v >> 3) + 8 h + (v & 7) of the tile (pi order)
+  auto mask = [&](f32x16& s, int k0, int lo, int hi) {
+    const int vlo = lo - k0 - 8 * h, vhi = hi - k0 - 8 * h;
+    if (lo > k0) {
+#pragma unroll
+      for (int v = 0; v < 16; ++v)
+        if (16 * (v >> 3) + (v & 7) < vlo) s[v] = -INFINITY;
+    }
+    if (hi < k0 + KT) {
+#pragma unroll
+      for (int v = 0; v < 16; ++v)
+        if (16 * (v >> 3) + (v & 7) >= vhi) s[v] = -INFINITY;
+    }
+  };
+  auto max8 = [&](const f32x16& s, int b) {  // max of scores b .. b+7
+    return fmaxf(fmaxf(fmaxf(s[b], s[b + 1]), fmaxf(s[b + 2], s[b + 3])),
+                 fmaxf(fmaxf(s[b + 4], s[b + 5]), fmaxf(s[b + 6], s[b + 7])));
+  };
+  // moves the accumulator and row sum to max mu when any lane of the wave raised its max
+  auto rescale = [&](float mu) {
     if (__builtin_amdgcn_ballot_w64(mu != m_run)) {
       const float alpha = __builtin_amdgcn_exp2f(m_run - mu);
       m_run = mu;
@@ -303,96 +311,170 @@ __global__ __launch_bounds__(256, 2) void k_bsfa_bf16(const bf16* __restrict__ q
 #pragma unroll
         for (int v = 0; v < 16; ++v) o[i][v] *= alpha;
     }
-    l_half += ps;
   };
-  auto pv = [&](const bf16* Vc, const bf16x8 (&pb)[4]) {
+  // Softmax numerators of one tile, spread over 8 slices (each after one MFMA of the previous
+  // tile's PV product). Slices 0-1 take the tile max and the lazily raised reference max mu
+  // (the tile max when it exceeds the running max by more than 2^16, else the running max).
+  // The 16 scores then go in groups of four through a three-slice pipeline: scale and shift
+  // in slice 2+g, exponentiate in 3+g, sum and pack into the P^T operands in 4+g.
+  auto soft_slice = [&](const f32x16& s, int i, float (&mx)[2], float& mu, float& ps, float (&xe)[16],
+                        bf16x8 (&pn)[2]) {
+    if (i == 0) {
+      mx[0] = max8(s, 0);
+      mx[1] = max8(s, 8);
+    }
+    if (i == 1) {
+      const float mt = fmaxf(mx[0], mx[1]);
+      const float m2 = fmaxf(mt, xor32(mt)) * c2;
+      mu = m2 > m_run + 16.f ? m2 : m_run;
+      ps = 0.f;
+    }
+    const int ga = i - 4, ge = i - 3, gf = i - 2;
+    if (ga >= 0 && ga < 4) {
+      const int t = 4 * ga;
+      ps += (xe[t] + xe[t + 1]) + (xe[t + 2] + xe[t + 3]);
 #pragma unroll
-    for (int cc = 0; cc < 4; ++cc)
+      for (int u = 0; u < 4; ++u) pn[t >> 3][(t & 7) + u] = (bf16)xe[t + u];
+    }
+    if (ge >= 0 && ge < 4) {
 #pragma unroll
-      for (int db = 0; db < ND; ++db) {
-        const bf16x8 av = *reinterpret_cast<const bf16x8*>((const char*)Vc + db * 32 * 128 + (vaddr ^ (32u * cc)));
-        o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, pb[cc], o[db], 0, 0, 0);
+      for (int u = 0; u < 4; ++u) xe[4 * ge + u] = __builtin_amdgcn_exp2f(xe[4 * ge + u]);
+    }
+    if (gf >= 0 && gf < 4) {
+#pragma unroll
+      for (int u = 0; u < 4; ++u) xe[4 * gf + u] = fmaf(s[4 * gf + u], c2, -mu);
+    }
+  };
+  // O^T += V^T P^T of the previous tile (V operands two MFMAs ahead) interleaved with the
+  // softmax numerators of the current tile
+  auto pv_soft = [&](const bf16* Vp, const bf16x8 (&pp)[2], const f32x16& s, float& mu, float& ps,
+                     bf16x8 (&pn)[2]) {
+    constexpr int NI = 2 * ND;
+    unsigned vb = vaddr;
+    asm volatile("" : "+v"(vb));
+    bf16x8 va[NI];
+    va[0] = vread(Vp, vb, 0);
+    va[1] = vread(Vp, vb, 1);
+    float mx[2], xe[16];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      if (i < NI) {
+        const int cc = i / ND, db = i % ND;
+        o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[i], pp[cc], o[db], 0, 0, 0);
+        if (i + 2 < NI) va[i + 2] = vread(Vp, vb, i + 2);
       }
+      soft_slice(s, i, mx, mu, ps, xe, pn);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+  auto pv = [&](const bf16* Vp, const bf16x8 (&pp)[2]) {
+    constexpr int NI = 2 * ND;
+    unsigned vb = vaddr;
+    asm volatile("" : "+v"(vb));
+    bf16x8 va[NI];
+    va[0] = vread(Vp, vb, 0);
+    va[1] = vread(Vp, vb, 1);
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+      const int cc = i / ND, db = i % ND;
+      o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[i], pp[cc], o[db], 0, 0, 0);
+      if (i + 2 < NI) va[i + 2] = vread(Vp, vb, i + 2);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+  auto soft = [&](const f32x16& s, float& mu, float& ps, bf16x8 (&pn)[2]) {
+    float mx[2], xe[16];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) soft_slice(s, i, mx, mu, ps, xe, pn);
   };
 
-  TileWalk ts;
-  bool hasc;
+  TileWalk<KT> ts;
+  bool has;  // the next tile exists
   if (MODE != 1) {
     ts.runs = B.runs + (size_t)bh * D.Cq * D.Ck + B.row_ptr[(size_t)bh * (D.Cq + 1) + a];
     ts.nr = B.nruns[(size_t)bh * D.Cq + a];
-    hasc = ts.first();
+    has = ts.first();
   } else {
     const int clo = a * D.pkc;
-    hasc = ts.first_single(clo, min(D.N, clo + D.pkc));
+    has = ts.first_single(clo, min(D.N, clo + D.pkc));
   }
-  // tile descriptors: current (j), next (j+1), after next (j+2)
-  int k0c = 0, loc = 0, hic = 0, k0n = 0, lon = 0, hin = 0;
-  f32x16 sa[2], sb[2];
-  if (hasc) {
-    k0c = ts.k0; loc = ts.lo; hic = ts.hi;
-    issue_k(Kb0, k0c);
-    issue_v(Vb0, k0c);
-  }
-  bool hasn = hasc && ts.next();
-  if (hasn) {
-    k0n = ts.k0; lon = ts.lo; hin = ts.hi;
-    issue_k(Kb1, k0n);
-  }
-  __builtin_amdgcn_s_waitcnt(0);
-  __syncthreads();
-  if (hasc && wave_active) qk(Kb0, sa);
-
-  // one tile: Kn = K buffer of tile j+1, Kc = K buffer of tile j (refilled with j+2),
-  // Vc = V buffer of tile j, Vn = V buffer of tile j+1
-  auto step = [&](f32x16 (&scur)[2], f32x16 (&snext)[2], bf16* Kc, const bf16* Kn, const bf16* Vc, bf16* Vn) {
-    __builtin_amdgcn_s_waitcnt(0);  // this wave's direct-to-LDS loads have landed
+  // Tile j: K(j) sits in K buffer j%2 and V(j) in V buffer j%2. Step j (j >= 1) loads K(j+1)
+  // and V(j) into registers, forms S(j), runs O += V(j-1) P(j-1) while it turns S(j) into
+  // P(j), and stores the loaded tiles at its end. P is double-buffered in registers (pa, pb
+  // by parity); the max and row sum of P(j) are applied (rescale, sum) at the start of step
+  // j+1, after P(j-1) has entered O. Tile 0 is handled before the loop and the last PV after
+  // it, so every step runs the same code and O never changes registers.
+  bf16x8 pp[2];  // P^T operands of the pending tile
+  float mu = -INFINITY, ps = 0.f;
+  if (has) {
+    // tile descriptors: j (current), j+1, j+2
+    int k0c = ts.k0, loc = ts.lo, hic = ts.hi;
+    bool has1 = ts.next();
+    int k01 = ts.k0, lo1 = ts.lo, hi1 = ts.hi;
+    bool has2 = has1 && ts.next();
+    int k02 = ts.k0;
+    Stage sa, sb;  // sa: K(j+1), V(j) (stored at the end of step j); sb: K(j+2), V(j+1)
+    load_k(sa, k0c);
+    store_k(sa, Kb0);
+    if (has1) load_k(sa, k01);
+    load_v(sa, k0c);
+    // Step j: K(j) is in K buffer j%2, V(j-1) in V buffer (j-1)%2. Load K(j+2) and V(j+1);
+    // S(j) = K(j) Q^T; O += V(j-1) P(j-1) while S(j) turns into P(j); store K(j+1) and V(j).
+    // Step 0 has no PV; one loop body serves both parities, so O keeps its registers.
     __syncthreads();
-    bool hasnn = false;
-    int k0nn = 0, lonn = 0, hinn = 0;
-    if (hasn) {
-      hasnn = ts.next();
-      if (hasnn) {
-        k0nn = ts.k0; lonn = ts.lo; hinn = ts.hi;
-        issue_k(Kc, k0nn);
-      }
-      issue_v(Vn, k0n);
-    }
+    if (has2) load_k(sb, k02);
+    if (has1) load_v(sb, k01);
     if (wave_active) {
-      if (k0c < loc || k0c + KT > hic) mask(scur, k0c, loc, hic);
-      bf16x8 pb[4];
-      float ps, mu;
-      if (hasn) {
-        // S(j+1) on the matrix cores while the vector units exponentiate S(j)
-        qk(Kn, snext);
-        expo(scur, pb, ps, mu);
-        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-#pragma unroll
-        for (int i = 0; i < 2 * NC; ++i) {
-          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-          if (i + 2 < 2 * NC) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-          __builtin_amdgcn_sched_group_barrier(0x002, 128 / (2 * NC), 0);
-        }
-      } else {
-        expo(scur, pb, ps, mu);
-      }
-      rescale(mu, ps);
-      pv(Vc, pb);
-      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-#pragma unroll
-      for (int i = 0; i < 4 * ND; ++i) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        if (i + 2 < 4 * ND) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-      }
+      f32x16 s;
+      qk(Kb0, s);
+      if (loc > k0c || hic < k0c + KT) mask(s, k0c, loc, hic);
+      soft(s, mu, ps, pp);
     }
-    hasc = hasn;
-    k0c = k0n; loc = lon; hic = hin;
-    hasn = hasnn;
-    k0n = k0nn; lon = lonn; hin = hinn;
-  };
-  while (hasc) {
-    step(sa, sb, Kb0, Kb1, Vb0, Vb1);
-    if (!hasc) break;
-    step(sb, sa, Kb1, Kb0, Vb1, Vb0);
+    if (has1) store_k(sa, Kb1);
+    store_v(sa, Vb0);
+    int par = 0;  // parity of the last tile
+    // step of tile j; `cur` holds K(j+1), V(j) (loaded a step ago), `nxt` receives K(j+2), V(j+1)
+    auto step = [&](Stage& cur, Stage& nxt) {
+      k0c = k01; loc = lo1; hic = hi1;
+      has1 = has2;
+      k01 = k02; lo1 = ts.lo; hi1 = ts.hi;
+      has2 = has2 && ts.next();
+      k02 = ts.k0;
+      par ^= 1;
+      const bf16* Kc = par ? Kb1 : Kb0;
+      bf16* Kn = par ? Kb0 : Kb1;
+      const bf16* Vp = par ? Vb0 : Vb1;
+      bf16* Vc = par ? Vb1 : Vb0;
+      __syncthreads();
+      if (has2) load_k(nxt, k02);
+      if (has1) load_v(nxt, k01);
+      if (wave_active) {
+        rescale(mu);
+        l_half += ps;
+        f32x16 s;
+        qk(Kc, s);
+        if (loc > k0c || hic < k0c + KT) mask(s, k0c, loc, hic);
+        bf16x8 pn[2];
+        pv_soft(Vp, pp, s, mu, ps, pn);
+        pp[0] = pn[0];
+        pp[1] = pn[1];
+      }
+      if (has1) store_k(cur, Kn);
+      store_v(cur, Vc);
+    };
+    // whole pairs of steps (stages swap roles twice), then at most one more step
+    while (has1 && has2) {
+      step(sb, sa);
+      step(sa, sb);
+    }
+    if (has1) step(sb, sa);
+    // O += V(T-1) P(T-1), V(T-1) in V buffer par
+    __syncthreads();
+    if (wave_active) {
+      rescale(mu);
+      l_half += ps;
+      pv(par ? Vb1 : Vb0, pp);
+    }
   }
 
   // ---- normalise and store query l32's row: d = 32db + 8g + 4h + r
