@@ -804,7 +804,7 @@ __device__ inline void km_rank_block(const Dims& D, const Bufs& B, int C, int bh
 // bf16, plus its bf16 remainder when LO) are double-buffered in LDS 64 centroids at a time:
 // the next chunk's global loads are issued before the current chunk's products.
 template <int DD, int RS, bool LO>
-__global__ __launch_bounds__(256) void k_km_assign_bf16(const bf16* x, Dims D, Bufs B, int C, KmState* st, int t) {
+__global__ __launch_bounds__(256, 2) void k_km_assign_bf16(const bf16* x, Dims D, Bufs B, int C, KmState* st, int t) {
   constexpr int CB = 64, KS = DD + 8, NB = kKmRows * RS;
   constexpr int NL = CB * DD / 8 / 256;  // 16-byte loads per thread per chunk and operand
   constexpr int NO = LO ? 2 : 1;
@@ -846,7 +846,8 @@ __global__ __launch_bounds__(256) void k_km_assign_bf16(const bf16* x, Dims D, B
           for (int q = 0; q < 8; ++q) pre[o][i][q] = (bf16)0.f;
         }
       }
-    pcn = (tid < CB && c0 + tid < C) ? cn[c0 + tid] : 0.f;
+    // a centroid past the last one scores +inf and never wins the strict comparison below
+    pcn = (tid < CB && c0 + tid < C) ? cn[c0 + tid] : INFINITY;
   };
   auto store_chunk = [&](int buf) {
 #pragma unroll
@@ -882,13 +883,15 @@ __global__ __launch_bounds__(256) void k_km_assign_bf16(const bf16* x, Dims D, B
             acc[rs] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, xr[rs][c], acc[rs], 0, 0, 0);
         }
       }
+      // A lane visits its centroids in increasing index order, so a strict comparison keeps
+      // the lowest index among equal scores; the two lane halves merge with the full rule.
 #pragma unroll
       for (int rs = 0; rs < RS; ++rs)
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
-          const int cl = yb + acc_row(v), col = c0 + cl;
+          const int cl = yb + acc_row(v);
           const float sc = fmaf(-a2[rs], acc[rs][v], cns[cur][cl]);
-          if (col < C && (sc < best[rs] || (sc == best[rs] && col < bidx[rs]))) { best[rs] = sc; bidx[rs] = col; }
+          if (sc < best[rs]) { best[rs] = sc; bidx[rs] = c0 + cl; }
         }
     }
     if (more) store_chunk(cur ^ 1);
