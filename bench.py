@@ -141,6 +141,25 @@ def main():
     stage = L.sparsepr_stage_times(sp.plan_h)
     info = sp.info()
 
+    # warm-started calls (paper Table C.1: k-means limit 2 for subsequent calls), each from
+    # the groups the previous call left; the headline stays the cold call
+    sp_w = SparsePR(config_from_workload(w), device=dev)
+    L.sparsepr_set_stage_timing(sp_w.plan_h, 1)
+    sp_w(tq, tk, tv)
+    for _ in range(max(1, args.warmup)):
+        sp_w(tq, tk, tv, warm=True)
+    torch.cuda.synchronize()
+    L.sparsepr_stage_times(sp_w.plan_h)
+    w0, w1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    w0.record(stream)
+    for _ in range(args.steps):
+        sp_w(tq, tk, tv, warm=True)
+    w1.record(stream)
+    torch.cuda.synchronize()
+    ms_warm = w0.elapsed_time(w1) / args.steps
+    stage_w = L.sparsepr_stage_times(sp_w.plan_h)
+    info_w = sp_w.info()
+
     # dense attention with the same kernels, same inputs (baseline and error reference)
     spd = SparsePR(config_from_workload(w), device=dev)
     dense = torch.empty_like(tq)
@@ -168,6 +187,11 @@ def main():
 
     err_mean, err_p99 = err(sp.out)
     sp_mean, sp_p99 = err(sp.o_sparse)
+    probes_w = sp_w.export("PROBES").long()
+    mask_w = torch.ones((BH, N), dtype=torch.bool, device=dev)
+    mask_w.scatter_(1, probes_w, False)
+    ew = ((sp_w.out.reshape(BH, N, d).float() - ref).norm(dim=-1) / (ref.norm(dim=-1) + 1e-8))[mask_w].double()
+    warm_err_mean = float(ew.mean())
 
     pairs = np.array([i["executed_pairs"] for i in info], dtype=np.float64)
     cell_pairs = pairs - M * N
@@ -201,6 +225,11 @@ def main():
         "stage_ms": {k: round(v, 4) for k, v in stage.items()},
         "probe_attention_tflops": round(probe_flop / max(stage["probes"], 1e-9) / 1e9, 2),
         "kmeans_iters": [[i["key_iters"], i["query_iters"]] for i in info],
+        "warm": {"call_latency_ms": round(ms_warm, 4), "value": round(dense_flop / (ms_warm * 1e-3) / 1e12, 3),
+                 "speedup_vs_dense": round(ms_dense / ms_warm, 3), "err_mean": round(warm_err_mean, 5),
+                 "stage_ms": {k: round(v, 4) for k, v in stage_w.items()},
+                 "kmeans_iters_max": [max(i["key_iters"] for i in info_w), max(i["query_iters"] for i in info_w)]},
+        "repair_share": round((stage["probes"] + stage["fit"] + stage["apply"]) / ms_step, 4),
         "roofline": roofline,
     }
     if not args.no_cpu_baseline:

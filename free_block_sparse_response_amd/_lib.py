@@ -35,7 +35,7 @@ class sparsepr_config(ctypes.Structure):
                 ("n_query_groups", ctypes.c_int32), ("n_probes", ctypes.c_int32), ("density", ctypes.c_double),
                 ("kmeans_max_iter", ctypes.c_int32), ("kmeans_tol", ctypes.c_float),
                 ("ridge_lambda", ctypes.c_float), ("penalize_bias", ctypes.c_int32), ("seed", ctypes.c_uint64),
-                ("assign_precision", ctypes.c_int32)]
+                ("assign_precision", ctypes.c_int32), ("warm_iters", ctypes.c_int32)]
 
 
 class sparsepr_head_info(ctypes.Structure):
@@ -51,6 +51,7 @@ _SIGS = {
     "sparsepr_plan_destroy": (None, [_P]),
     "sparsepr_workspace_bytes": (_SZ, [_P]),
     "sparsepr_plan": (ctypes.c_int, [_P, _P, _P, _P, _SZ, _P]),
+    "sparsepr_plan_warm": (ctypes.c_int, [_P, _P, _P, _P, _SZ, _P]),
     "sparsepr_plan_from_labels": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _P, _SZ, _P]),
     "sparsepr_attend": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _P, _P]),
     "sparsepr_fit_residual": (ctypes.c_int, [_P, _P, _P, _P, _P, _P]),
@@ -115,7 +116,7 @@ def _stream(stream=None):
 # --------------------------------------------------------------------------- same names
 def make_config(batch, heads, seq_len, head_dim, dtype, n_sampled, n_key_groups, n_query_groups, n_probes,
                 density, kmeans_max_iter=25, kmeans_tol=1e-4, ridge_lambda=1e-3, penalize_bias=0, seed=0,
-                softmax_scale=0.0, assign_precision=0):
+                softmax_scale=0.0, assign_precision=0, warm_iters=2):
     c = sparsepr_config()
     c.batch, c.heads, c.seq_len, c.head_dim = batch, heads, seq_len, head_dim
     c.dtype = {"f32": SPARSEPR_F32, "bf16": SPARSEPR_BF16}.get(dtype, dtype)
@@ -125,6 +126,7 @@ def make_config(batch, heads, seq_len, head_dim, dtype, n_sampled, n_key_groups,
     c.kmeans_max_iter, c.kmeans_tol = kmeans_max_iter, kmeans_tol
     c.ridge_lambda, c.penalize_bias, c.seed = ridge_lambda, penalize_bias, seed
     c.assign_precision = assign_precision
+    c.warm_iters = warm_iters
     return c
 
 
@@ -145,6 +147,12 @@ def sparsepr_workspace_bytes(plan):
 def sparsepr_plan(plan, q, k, workspace, stream=None):
     _check("sparsepr_plan", lib().sparsepr_plan(plan, _ptr(q), _ptr(k), _ptr(workspace),
                                                 workspace.numel() * workspace.element_size(), _stream(stream)))
+
+
+def sparsepr_plan_warm(plan, q, k, workspace, stream=None):
+    _check("sparsepr_plan_warm", lib().sparsepr_plan_warm(plan, _ptr(q), _ptr(k), _ptr(workspace),
+                                                          workspace.numel() * workspace.element_size(),
+                                                          _stream(stream)))
 
 
 def sparsepr_plan_from_labels(plan, q, k, key_labels, query_labels, group_mass, workspace, stream=None):

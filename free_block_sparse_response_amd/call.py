@@ -19,7 +19,7 @@ class SparsePR:
 
     ``cfg`` keys: batch, heads, seq_len, head_dim, dtype ("f32" / "bf16"), n_sampled,
     n_key_groups, n_query_groups, n_probes, density, ridge_lambda, seed and optionally
-    kmeans_max_iter, kmeans_tol, penalize_bias, softmax_scale, assign_precision.
+    kmeans_max_iter, kmeans_tol, penalize_bias, softmax_scale, assign_precision, warm_iters.
     """
 
     def __init__(self, cfg, device="cuda"):
@@ -32,7 +32,7 @@ class SparsePR:
                                  c["n_key_groups"], c["n_query_groups"], c["n_probes"], c["density"],
                                  c.get("kmeans_max_iter", 25), c.get("kmeans_tol", 1e-4), c.get("ridge_lambda", 1e-3),
                                  c.get("penalize_bias", 0), c.get("seed", 0), c.get("softmax_scale", 0.0),
-                                 c.get("assign_precision", 0))
+                                 c.get("assign_precision", 0), c.get("warm_iters", 2))
         self.plan_h = L.sparsepr_plan_create(self._cc)
         self.ws = torch.empty(L.sparsepr_workspace_bytes(self.plan_h), dtype=torch.uint8, device=device)
         shape = (c["batch"], c["heads"], self.N, self.d)
@@ -50,8 +50,10 @@ class SparsePR:
             self.plan_h = None
 
     # the four stages
-    def plan(self, q, k, key_labels=None, query_labels=None, group_mass=None):
-        if key_labels is None:
+    def plan(self, q, k, key_labels=None, query_labels=None, group_mass=None, warm=False):
+        if warm:
+            L.sparsepr_plan_warm(self.plan_h, q, k, self.ws)
+        elif key_labels is None:
             L.sparsepr_plan(self.plan_h, q, k, self.ws)
         else:
             L.sparsepr_plan_from_labels(self.plan_h, q, k, key_labels, query_labels, group_mass, self.ws)
@@ -70,8 +72,9 @@ class SparsePR:
         L.sparsepr_apply(self.plan_h, self.o_sparse, self.o_probe if self.M else None, self.coeffs,
                          self.out if out is None else out)
 
-    def __call__(self, q, k, v):
-        self.plan(q, k)
+    def __call__(self, q, k, v, warm=False):
+        """One call; warm=True starts the planner from the previous call's groups."""
+        self.plan(q, k, warm=warm)
         self.attend(q, k, v)
         self.fit_residual()
         self.apply()

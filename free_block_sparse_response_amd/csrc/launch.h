@@ -6,6 +6,7 @@
 namespace spr {
 
 void launch_plan(const void* q, const void* k, const Dims& D, const Bufs& B, hipStream_t s);
+void launch_plan_warm(const void* q, const void* k, const Dims& D, const Bufs& B, hipStream_t s);
 void launch_plan_from_labels(const void* q, const void* k, const int* klab, const int* qlab,
                              const long long* mass, const Dims& D, const Bufs& B, hipStream_t s);
 void launch_route_probes(const Dims& D, const Bufs& B, hipStream_t s);

@@ -656,6 +656,44 @@ __global__ __launch_bounds__(256) void k_km_update(const T* x, Dims D, Bufs B, K
   km_update_item<T, DD>(x, D, B, st, t, perm, blockIdx.x, blockIdx.y);
 }
 
+// Warm start (paper Table C.1: a first k-means of up to 25 iterations, 2 for subsequent
+// calls). Centroid b starts from the d-dimensional representative reps[b] of the previous
+// plan (key groups: mean key; query groups: mean of alpha q), which is what the metric form
+// needs: G m_b and m_b G m_b under the current metric. Only the prev[bh].c_final groups the
+// previous plan realised are live; the other slots score +inf, never win an assignment and
+// are dropped again at compaction.
+template <int DD>
+__global__ __launch_bounds__(256) void k_km_warm_init(Dims D, Bufs B, const float* reps, int rep_groups,
+                                                       const KmState* prev) {
+  __shared__ float m[DD];
+  __shared__ float red[4];
+  const int b = blockIdx.x, bh = blockIdx.y, i = threadIdx.x;
+  const bool live = b < prev[bh].c_final;
+  if (i < DD) m[i] = live ? reps[((size_t)bh * rep_groups + b) * DD + i] : 0.f;
+  __syncthreads();
+  float p = 0.f;
+  if (i < DD) {
+    const float* G = B.metric + (size_t)bh * DD * DD;
+    float t = 0.f;
+    for (int k = 0; k < DD; ++k) t = fmaf(G[(size_t)k * DD + i], m[k], t);
+    const size_t o = ((size_t)bh * D.C + b) * DD + i;
+    B.cent[o] = m[i];
+    B.cent_t[o] = t;
+    const bf16 th = (bf16)t;
+    B.cent_h[o] = th;
+    B.cent_l[o] = (bf16)(t - (float)th);
+    p = m[i] * t;
+  }
+  p = wave_sum(p);
+  if (lane_id() == 0) red[i / kWave] = p;
+  __syncthreads();
+  if (i == 0) {
+    float sum = 0.f;
+    for (int w = 0; w < DD / kWave; ++w) sum += red[w];
+    B.cnorm[(size_t)bh * D.C + b] = live ? sum : INFINITY;
+  }
+}
+
 // Drop empty groups: compacted labels, offsets and the realised group count.
 __global__ __launch_bounds__(1024) void k_km_compact(Dims D, Bufs B, int C, KmState* st, int* lab_out,
                                                      int* off_out, int off_stride) {
@@ -697,6 +735,21 @@ __global__ __launch_bounds__(256) void k_key_centroids(const T* k, Dims D, Bufs 
     B.kcent_h[o] = vh;
     B.kcent_l[o] = (bf16)(v - (float)vh);
   }
+}
+
+// Query-group representative: mean of alpha_i q_i over the compacted group (the query
+// features are F_i = alpha_i q_i C_k^T, so a group's feature mean is this times C_k^T).
+template <typename T, int DD>
+__global__ __launch_bounds__(256) void k_query_reps(const T* q, Dims D, Bufs B) {
+  __shared__ float sh[2048];
+  __shared__ float m[DD];
+  const int a = blockIdx.x, bh = blockIdx.y;
+  if (a >= B.qst[bh].c_final) return;
+  const int* off = B.qoff + (size_t)bh * (D.Cq + 1);
+  const int s0 = off[a], n = off[a + 1] - off[a];
+  group_mean<T, DD>(q + (size_t)bh * D.N * DD, B.alpha + (size_t)bh * D.N, B.qperm + (size_t)bh * D.N + s0, n, m,
+                    sh);
+  if (threadIdx.x < DD) B.qcent[((size_t)bh * D.Cq + a) * DD + threadIdx.x] = m[threadIdx.x];
 }
 
 // =====================================================================================
@@ -827,7 +880,7 @@ __global__ __launch_bounds__(256, 2) void k_km_assign_bf16(const bf16* x, Dims D
     load_row_operand<DD>(x + ((size_t)bh * D.N + (valid ? row : D.N - 1)) * DD, xr[rs]);
     a2[rs] = 2.f * (B.alpha ? B.alpha[(size_t)bh * D.N + (valid ? row : 0)] : 1.f);
     best[rs] = INFINITY;
-    bidx[rs] = 0x7fffffff;
+    bidx[rs] = 0;
   }
   const bf16* Cop[2] = {B.cent_h + (size_t)bh * D.C * DD, B.cent_l + (size_t)bh * D.C * DD};
   const float* cn = B.cnorm + (size_t)bh * D.C;
@@ -885,13 +938,15 @@ __global__ __launch_bounds__(256, 2) void k_km_assign_bf16(const bf16* x, Dims D
       }
       // A lane visits its centroids in increasing index order, so a strict comparison keeps
       // the lowest index among equal scores; the two lane halves merge with the full rule.
+      // The index kept is c0 + yb + 8 (v / 4) + v % 4 (wave-uniform); the lane-half offset
+      // 4 h is added once at the end.
 #pragma unroll
       for (int rs = 0; rs < RS; ++rs)
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
           const int cl = yb + acc_row(v);
           const float sc = fmaf(-a2[rs], acc[rs][v], cns[cur][cl]);
-          if (sc < best[rs]) { best[rs] = sc; bidx[rs] = c0 + cl; }
+          if (sc < best[rs]) { best[rs] = sc; bidx[rs] = c0 + yb + 8 * (v >> 2) + (v & 3); }
         }
     }
     if (more) store_chunk(cur ^ 1);
@@ -900,6 +955,7 @@ __global__ __launch_bounds__(256, 2) void k_km_assign_bf16(const bf16* x, Dims D
   }
 #pragma unroll
   for (int rs = 0; rs < RS; ++rs) {
+    bidx[rs] += 4 * h;
     const float ob = __shfl_xor(best[rs], 32, kWave);
     const int oi = __shfl_xor(bidx[rs], 32, kWave);
     if (ob < best[rs] || (ob == best[rs] && oi < bidx[rs])) { best[rs] = ob; bidx[rs] = oi; }
@@ -1468,11 +1524,10 @@ __global__ void k_identity_plan(Dims D, Bufs B) {
     else FN<float, 64>(__VA_ARGS__);                                      \
   } while (0)
 
+// Lloyd iterations from the centroids already in B.cent / cent_t / cnorm (state in st).
 template <typename T, int DD>
-static void run_lloyd(const void* xv, const Dims& D, const Bufs& B, int C, const int* init, KmState* st, int* perm,
-                      hipStream_t s) {
-  const T* x = (const T*)xv;
-  hipLaunchKernelGGL((k_km_init<T, DD>), dim3(C, D.BH), dim3(256), 0, s, x, D, B, C, init, st);
+static void lloyd_iterations(const T* x, const Dims& D, const Bufs& B, int C, KmState* st, int* perm,
+                             hipStream_t s) {
   for (int t = 1; t <= D.max_iter; ++t) {
     if constexpr (std::is_same<T, bf16>::value)
       if (D.assign_lo)
@@ -1489,6 +1544,14 @@ static void run_lloyd(const void* xv, const Dims& D, const Bufs& B, int C, const
     if (t < D.max_iter)
       hipLaunchKernelGGL((k_km_update<T, DD>), dim3(C, D.BH), dim3(256), 0, s, x, D, B, st, t, perm);
   }
+}
+
+template <typename T, int DD>
+static void run_lloyd(const void* xv, const Dims& D, const Bufs& B, int C, const int* init, KmState* st, int* perm,
+                      hipStream_t s) {
+  const T* x = (const T*)xv;
+  hipLaunchKernelGGL((k_km_init<T, DD>), dim3(C, D.BH), dim3(256), 0, s, x, D, B, C, init, st);
+  lloyd_iterations<T, DD>(x, D, B, C, st, perm, s);
 }
 
 template <typename T, int DD>
@@ -1533,8 +1596,43 @@ static void plan_impl(const void* qv, const void* kv, const Dims& D, const Bufs&
   rowquad<T, DD>(q, D, B, B.metric, B.rowconst, B.alpha, (const KmState*)B.kst, s);
   run_lloyd<T, DD>(q, D, B, D.Cq, B.init_q, B.qst, B.qperm, s);
   hipLaunchKernelGGL(k_km_compact, dim3(D.BH), dim3(1024), 0, s, D, B, D.Cq, B.qst, B.qlab, B.qoff, D.Cq + 1);
+  hipLaunchKernelGGL((k_query_reps<T, DD>), dim3(D.Cq, D.BH), dim3(256), 0, s, q, D, B);
   hipLaunchKernelGGL(k_build_tiles, dim3(D.BH), dim3(1024), 0, s, D, B);
   // 03: group masses
+  group_mass<T, DD>(q, D, B, s);
+}
+
+// Warm-started plan: both k-means start from the previous plan's groups (k_km_warm_init)
+// and run at most D.warm_iter iterations.
+template <typename T, int DD>
+static void plan_warm_impl(const void* qv, const void* kv, const Dims& D0, const Bufs& B, hipStream_t s) {
+  const T* q = (const T*)qv;
+  const T* k = (const T*)kv;
+  Dims D = D0;
+  D.max_iter = D0.warm_iter;
+  hipLaunchKernelGGL(k_select_all, dim3(D.BH, 3), dim3(1024), 0, s, D, B);
+  hipLaunchKernelGGL((k_gather_rows<T>), dim3(D.S, D.BH), dim3(DD), 0, s, q, B.sampled, D.N, D.S, DD, B.qs);
+  hipLaunchKernelGGL((k_gram<DD>), dim3(DD * DD / 256, D.BH), dim3(256), 0, s, B.qs, D.S, (const KmState*)nullptr,
+                     D.scale * D.scale, B.metric, B.metric_h, B.metric_l);
+  // key groups from the previous key centroids
+  Bufs Bk = B;
+  Bk.alpha = nullptr;
+  rowquad<T, DD>(k, D, B, B.metric, B.rowconst, (float*)nullptr, (const KmState*)nullptr, s);
+  hipLaunchKernelGGL((k_km_warm_init<DD>), dim3(D.Ck, D.BH), dim3(256), 0, s, D, Bk, B.kcent, D.Ck, B.kst);
+  hipLaunchKernelGGL(k_state_reset, dim3((D.BH + 63) / 64), dim3(64), 0, s, B.kst, D.BH, D.Ck, 0x7fffffff);
+  lloyd_iterations<T, DD>(k, D, Bk, D.Ck, B.kst, B.kperm, s);
+  hipLaunchKernelGGL(k_km_compact, dim3(D.BH), dim3(1024), 0, s, D, B, D.Ck, B.kst, B.klab, B.koff, D.Ck + 1);
+  hipLaunchKernelGGL((k_key_centroids<T, DD>), dim3(D.Ck, D.BH), dim3(256), 0, s, k, D, B);
+  // query groups from the previous query representatives
+  hipLaunchKernelGGL((k_gram<DD>), dim3(DD * DD / 256, D.BH), dim3(256), 0, s, B.kcent, D.Ck, (const KmState*)B.kst, 1.f,
+                     B.metric, B.metric_h, B.metric_l);
+  rowquad<T, DD>(q, D, B, B.metric, B.rowconst, B.alpha, (const KmState*)B.kst, s);
+  hipLaunchKernelGGL((k_km_warm_init<DD>), dim3(D.Cq, D.BH), dim3(256), 0, s, D, B, B.qcent, D.Cq, B.qst);
+  hipLaunchKernelGGL(k_state_reset, dim3((D.BH + 63) / 64), dim3(64), 0, s, B.qst, D.BH, D.Cq, 0x7fffffff);
+  lloyd_iterations<T, DD>(q, D, B, D.Cq, B.qst, B.qperm, s);
+  hipLaunchKernelGGL(k_km_compact, dim3(D.BH), dim3(1024), 0, s, D, B, D.Cq, B.qst, B.qlab, B.qoff, D.Cq + 1);
+  hipLaunchKernelGGL((k_query_reps<T, DD>), dim3(D.Cq, D.BH), dim3(256), 0, s, q, D, B);
+  hipLaunchKernelGGL(k_build_tiles, dim3(D.BH), dim3(1024), 0, s, D, B);
   group_mass<T, DD>(q, D, B, s);
 }
 
@@ -1558,6 +1656,11 @@ static void plan_labels_impl(const void* qv, const void* kv, const int* klab, co
   hipLaunchKernelGGL(k_km_scan_head, dim3(D.BH), dim3(256), 0, s, D, B, D.Cq, B.qst, 1);
   hipLaunchKernelGGL(k_km_scatter, dim3(D.nblk, D.BH), dim3(kKmRows), 0, s, D, B, B.qst, 1, B.qperm);
   hipLaunchKernelGGL(k_km_compact, dim3(D.BH), dim3(1024), 0, s, D, B, D.Cq, B.qst, B.qlab, B.qoff, D.Cq + 1);
+  // query scales alpha (as the planner computes them) for the warm-start representatives
+  hipLaunchKernelGGL((k_gram<DD>), dim3(DD * DD / 256, D.BH), dim3(256), 0, s, B.kcent, D.Ck, (const KmState*)B.kst, 1.f,
+                     B.metric, B.metric_h, B.metric_l);
+  rowquad<T, DD>(q, D, B, B.metric, B.rowconst, B.alpha, (const KmState*)B.kst, s);
+  hipLaunchKernelGGL((k_query_reps<T, DD>), dim3(D.Cq, D.BH), dim3(256), 0, s, q, D, B);
   hipLaunchKernelGGL(k_build_tiles, dim3(D.BH), dim3(1024), 0, s, D, B);
   if (mass) {
     (void)hipMemcpyAsync(B.u, mass, sizeof(long long) * (size_t)D.BH * D.Cq * D.Ck, hipMemcpyDeviceToDevice, s);
@@ -1568,6 +1671,10 @@ static void plan_labels_impl(const void* qv, const void* kv, const int* klab, co
 
 void launch_plan(const void* q, const void* k, const Dims& D, const Bufs& B, hipStream_t s) {
   SPR_DISPATCH(D.dtype, D.d, plan_impl, q, k, D, B, s);
+}
+
+void launch_plan_warm(const void* q, const void* k, const Dims& D, const Bufs& B, hipStream_t s) {
+  SPR_DISPATCH(D.dtype, D.d, plan_warm_impl, q, k, D, B, s);
 }
 
 void launch_plan_from_labels(const void* q, const void* k, const int* klab, const int* qlab,

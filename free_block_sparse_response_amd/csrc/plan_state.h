@@ -41,6 +41,7 @@ struct Dims {
   double density;
   long long budget;
   int max_iter;
+  int warm_iter;  // iteration limit of a warm-started plan
   float tol;
   float lambda;
   int pen_bias;
@@ -77,6 +78,7 @@ struct Bufs {
   float* kcent;      // [BH][Ck][d] key-space centroids of the compacted groups
   bf16* kcent_h;     // [BH][Ck][d] key centroids rounded to bf16
   bf16* kcent_l;     // [BH][Ck][d] key centroids minus their bf16 rounding
+  float* qcent;      // [BH][Cq][d] query-group means of alpha q (warm-start representatives)
   int* qlab;         // [BH][N]
   int* qperm;        // [BH][N]
   int* qoff;         // [BH][Cq+1]

@@ -100,6 +100,7 @@ Bufs carve(const Dims& D, void* base, size_t* total) {
   B.kcent = c.take<float>(BH * D.Ck * d);
   B.kcent_h = c.take<spr::bf16>(BH * D.Ck * d);
   B.kcent_l = c.take<spr::bf16>(BH * D.Ck * d);
+  B.qcent = c.take<float>(BH * D.Cq * d);
   B.qlab = c.take<int>(BH * N);
   B.qperm = c.take<int>(BH * N);
   B.qoff = c.take<int>(BH * (D.Cq + 1));
@@ -186,6 +187,7 @@ sparsepr_status sparsepr_plan_create(const sparsepr_config* cfg, sparsepr_plan_t
   if (!finite_d(c.ridge_lambda) || c.ridge_lambda < 0.f) return SPARSEPR_ERR_INVALID_ARG;
   if (!finite_d(c.softmax_scale) || c.softmax_scale < 0.f) return SPARSEPR_ERR_INVALID_ARG;
   if (c.assign_precision != 0 && c.assign_precision != 1) return SPARSEPR_ERR_INVALID_ARG;
+  if (c.warm_iters < 0 || c.warm_iters > 10000) return SPARSEPR_ERR_INVALID_ARG;
 
   sparsepr_plan_s* p = new (std::nothrow) sparsepr_plan_s();
   if (!p) return SPARSEPR_ERR_INVALID_ARG;
@@ -219,6 +221,7 @@ sparsepr_status sparsepr_plan_create(const sparsepr_config* cfg, sparsepr_plan_t
   D.density = c.density;
   D.budget = (long long)floor(c.density * (double)((long long)N * N)) - (long long)D.M * N;
   D.max_iter = c.kmeans_max_iter;
+  D.warm_iter = c.warm_iters > 0 ? c.warm_iters : 2;
   D.tol = c.kmeans_tol;
   D.lambda = c.ridge_lambda;
   D.pen_bias = c.penalize_bias ? 1 : 0;
@@ -304,6 +307,24 @@ sparsepr_status sparsepr_plan(sparsepr_plan_t p, const void* q, const void* k, v
   {
     StageTimer t(p, SPARSEPR_STAGE_PLAN, s);
     spr::launch_plan(q, k, p->D, B, s);
+    spr::launch_route_probes(p->D, B, s);
+  }
+  st = hip_status();
+  if (st == SPARSEPR_OK) p->planned = 1;
+  return st;
+}
+
+sparsepr_status sparsepr_plan_warm(sparsepr_plan_t p, const void* q, const void* k, void* ws, size_t bytes,
+                                   void* stream) {
+  if (!p || !q || !k) return SPARSEPR_ERR_INVALID_ARG;
+  if (!p->planned || p->ws != ws) return SPARSEPR_ERR_STATE;
+  hipStream_t s = (hipStream_t)stream;
+  Bufs B;
+  sparsepr_status st = begin_plan(p, ws, bytes, &B, s);
+  if (st != SPARSEPR_OK) return st;
+  {
+    StageTimer t(p, SPARSEPR_STAGE_PLAN, s);
+    spr::launch_plan_warm(q, k, p->D, B, s);
     spr::launch_route_probes(p->D, B, s);
   }
   st = hip_status();

@@ -79,6 +79,8 @@ typedef struct {
   int32_t assign_precision;                /* bf16 inputs, Lloyd assignment products:     */
                                            /*   0 centroid operand rounded to bf16,       */
                                            /*   1 bf16 + bf16 remainder (~16-bit operand) */
+  int32_t warm_iters;                      /* Lloyd limit of sparsepr_plan_warm; 0 -> 2   */
+                                           /* (paper Table C.1: 2 for subsequent calls)   */
 } sparsepr_config;
 
 typedef struct sparsepr_plan_s* sparsepr_plan_t;
@@ -124,6 +126,19 @@ size_t sparsepr_workspace_bytes(sparsepr_plan_t plan);
  * q, k: [B,H,N,d] of cfg.dtype. Binds `workspace` to the plan. */
 sparsepr_status sparsepr_plan(sparsepr_plan_t plan, const void* q, const void* k,
                               void* workspace, size_t workspace_bytes, void* stream);
+
+/* Warm-started planning for a subsequent call (paper Table C.1: the first k-means runs up
+ * to 25 iterations, subsequent ones up to 2). Both k-means start from the groups the
+ * previous successful sparsepr_plan / sparsepr_plan_warm / sparsepr_plan_from_labels on this
+ * handle left in `workspace`: key groups from their mean keys (mapped to responses under
+ * the current sampled queries), query groups from their means of (s / RMS_i) q_i (mapped
+ * through the current key centroids); the groups realised then are the ones requested now,
+ * and any left empty are dropped. At most cfg.warm_iters iterations per k-means, same
+ * tolerance rule. q, k: [B,H,N,d] of cfg.dtype (the new call's inputs). Returns
+ * SPARSEPR_ERR_STATE when there is no previous plan in this workspace (none yet, another
+ * workspace, or sparsepr_dense_attention used it since). */
+sparsepr_status sparsepr_plan_warm(sparsepr_plan_t plan, const void* q, const void* k,
+                                   void* workspace, size_t workspace_bytes, void* stream);
 
 /* The same plan from caller-given partitions (used to check the downstream steps against
  * a reference partition): key_labels / query_labels [B*H, N] int32 in [0, C_k) /

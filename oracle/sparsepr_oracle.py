@@ -147,7 +147,12 @@ def lloyd(x, init_rows, max_iter, tol):
     inertia decrease from iteration t-1 is at most tol times the previous inertia.
     The labels returned are those of the last assignment.
     """
-    cent = x[np.asarray(init_rows)].astype(np.float64).copy()
+    return lloyd_from(x, x[np.asarray(init_rows)], max_iter, tol)
+
+
+def lloyd_from(x, init_centroids, max_iter, tol):
+    """The iterations of ``lloyd`` started from explicit centroids (rows of init_centroids)."""
+    cent = np.array(init_centroids, dtype=np.float64, copy=True)
     C = cent.shape[0]
     prev = None
     hist = []
@@ -457,6 +462,7 @@ class HeadPlan:
     k_off: np.ndarray = None
     n_k: np.ndarray = None
     key_centroids: np.ndarray = None
+    query_reps: np.ndarray = None
     query_labels: np.ndarray = None
     query_iters: int = 0
     Cq: int = 0
@@ -490,6 +496,45 @@ def plan_head(q, k, p, head, max_iter, tol):
     return finish_plan(q, k, p, head, hp)
 
 
+def query_representatives(q, L, scale, q_labels, Cq):
+    """Query-group centroids as d-dimensional means of x_i = (s / RMS_i) q_i.
+
+    F_i = x_i C_k^T (query_features), so the mean of F over a group is its
+    representative times C_k^T; a warm start maps it through the new key centroids.
+    """
+    rms = np.sqrt((L * L).mean(axis=1))
+    a = np.where(rms > 0, scale / np.where(rms > 0, rms, 1.0), 0.0)
+    return group_means(a[:, None] * q, q_labels, Cq)
+
+
+def plan_head_warm(q, k, p, head, prev, max_iter=2, tol=1e-4):
+    """Planning started from the centroids of a previous plan (prev, a HeadPlan).
+
+    [C.1] gives 25 iterations for the first k-means and 2 for subsequent ones.
+    Reading: "subsequent" calls start from the previous call's final centroids, kept
+    as d-dimensional means (key groups: mean of the member keys; query groups: the
+    query_representatives), mapped into this call's response spaces: key centroids
+    s m_b Q_S^T for the current sampled queries, query centroids z_a C_k^T for the
+    current key centroids. The groups the previous call realised are the requested
+    ones; groups left empty are dropped again.
+    """
+    N = q.shape[0]
+    s = p["scale"]
+    hp = HeadPlan()
+    hp.sampled = select_smallest(p["seed"], STREAM_SAMPLED, head, np.arange(N), p["n_sampled"])
+    qs = q[hp.sampled]
+    RK = key_responses(k, qs, s)
+    res = lloyd_from(RK, key_responses(prev.key_centroids, qs, s), max_iter, tol)
+    hp.key_iters = res.iterations
+    hp.key_labels, hp.Ck = compact_labels(res.labels, prev.Ck)
+    kc = group_means(k, hp.key_labels, hp.Ck)
+    _, F = query_features(q, kc, s)
+    res = lloyd_from(F, prev.query_reps @ kc.T, max_iter, tol)
+    hp.query_iters = res.iterations
+    hp.query_labels, hp.Cq = compact_labels(res.labels, prev.Cq)
+    return finish_plan(q, k, p, head, hp)
+
+
 def finish_plan(q, k, p, head, hp, u=None, probes=None):
     """Everything downstream of the two label vectors (also the labels-given entry).
 
@@ -503,8 +548,9 @@ def finish_plan(q, k, p, head, hp, u=None, probes=None):
     hp.k_perm, hp.k_off, hp.n_k = group_permutation(hp.key_labels, hp.Ck)
     hp.q_perm, hp.q_off, hp.n_q = group_permutation(hp.query_labels, hp.Cq)
     hp.key_centroids = group_means(k, hp.key_labels, hp.Ck)
+    L, _ = query_features(q, hp.key_centroids, p["scale"])
+    hp.query_reps = query_representatives(q, L, p["scale"], hp.query_labels, hp.Cq)
     if u is None:
-        L, _ = query_features(q, hp.key_centroids, p["scale"])
         hp.P, hp.u = group_masses(L, hp.n_k, hp.query_labels, hp.Cq)
     else:
         hp.u = np.asarray(u, dtype=np.int64)

@@ -62,6 +62,7 @@ def _create(lib, cfg):
     (dict(seq_len=0), L.SPARSEPR_ERR_INVALID_ARG),
     (dict(batch=0), L.SPARSEPR_ERR_INVALID_ARG),
     (dict(assign_precision=2), L.SPARSEPR_ERR_INVALID_ARG),
+    (dict(warm_iters=-1), L.SPARSEPR_ERR_INVALID_ARG),
 ])
 def test_plan_create_rejects(lib, over, want):
     st, h = _create(lib, _cfg(**over))
@@ -87,7 +88,9 @@ def test_workspace_size_and_host_side_errors(lib):
         assert lib.sparsepr_plan(h, fake, fake, fake, ws - 1, None) == L.SPARSEPR_ERR_WORKSPACE
         assert lib.sparsepr_plan(h, fake, fake, ctypes.c_void_p(0x100010), ws, None) == L.SPARSEPR_ERR_WORKSPACE
         assert lib.sparsepr_plan(h, None, fake, fake, ws, None) == L.SPARSEPR_ERR_INVALID_ARG
-        # later stages before a plan
+        # later stages before a plan; a warm start needs a previous plan in the same workspace
+        assert lib.sparsepr_plan_warm(h, fake, fake, fake, ws, None) == L.SPARSEPR_ERR_STATE
+        assert lib.sparsepr_plan_warm(h, None, fake, fake, ws, None) == L.SPARSEPR_ERR_INVALID_ARG
         assert lib.sparsepr_attend(h, fake, fake, fake, fake, fake, fake, None) == L.SPARSEPR_ERR_STATE
         assert lib.sparsepr_attend(h, fake, fake, fake, fake, fake, None, None) == L.SPARSEPR_ERR_INVALID_ARG
         assert lib.sparsepr_attend(h, fake, fake, fake, fake, None, fake, None) == L.SPARSEPR_ERR_INVALID_ARG

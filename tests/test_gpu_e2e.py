@@ -236,3 +236,80 @@ def test_max_groups_1024_bf16():
     e = max_rel(np_(sp.out[0, 0]), refs[0].out)
     say(f"  1024 groups: Ck' {refs[0].plan.Ck} Cq' {refs[0].plan.Cq} out {e:.2e}")
     assert e <= 2e-2
+
+
+# ------------------------------------------------------------------- warm-started planning
+@pytest.mark.parametrize("name,heads", [("c1", [0]), ("c2", [0, 1])])
+def test_warm_plan_after_convergence_keeps_the_plan(name, heads):
+    # k-means run until the inertia stops falling (tolerance 0): a warm start on the same
+    # inputs starts from the centroids the cold plan ended with; it must keep (nearly) every
+    # label, and when it keeps all of them every integer of the plan and the output must be
+    # bitwise those of the cold plan (rounding can stop a cold run one step short of an
+    # exact fixed point, hence the agreement bound)
+    w = configs.CONFIGS[name]
+    say(f"case: warm start after convergence, {name}, heads {heads}")
+    (tq, _), (tk, _), (tv, _) = inputs(w, heads)
+    sp = SparsePR(config_from_workload(w, heads=len(heads), kmeans_max_iter=200, kmeans_tol=0.0, warm_iters=3),
+                  device=DEV)
+    sp(tq, tk, tv)
+    torch.cuda.synchronize()
+    kinds = ("KEY_LABELS", "QUERY_LABELS", "ROUTE_ROWPTR", "ROUTE_COLS", "PROBES")
+    cold = {k: sp.export(k).clone() for k in kinds}
+    cold_out = sp.out.clone()
+    cold_info = sp.info()
+    sp(tq, tk, tv, warm=True)
+    torch.cuda.synchronize()
+    info = sp.info()
+    agree = [float((cold[k] == sp.export(k)).float().mean()) for k in ("KEY_LABELS", "QUERY_LABELS")]
+    say(f"  cold iters {[(i['key_iters'], i['query_iters']) for i in cold_info]} "
+        f"warm {[(i['key_iters'], i['query_iters']) for i in info]}; label agreement {agree}")
+    assert min(agree) >= 0.99
+    for b in info:
+        assert b["status"] == 0 and b["key_iters"] <= 3 and b["query_iters"] <= 3
+    if agree == [1.0, 1.0]:
+        for k in kinds:
+            assert torch.equal(cold[k], sp.export(k)), k
+        assert torch.equal(cold_out, sp.out)
+
+
+def test_warm_plan_on_new_inputs_matches_oracle_warm():
+    # the previous call's groups are the oracle's (labels given); the next call's inputs are
+    # perturbed; the GPU warm plan against the oracle's warm plan from the same groups
+    w = configs.CONFIGS["c1"]
+    say("case: warm start on perturbed inputs, c1")
+    (tq, q64), (tk, k64), (tv, v64) = inputs(w)
+    p = O.call_params(w)
+    cold = [O.plan_head(q64[0], k64[0], p, 0, 25, 1e-4)]
+    sp = gpu_from_labels(w, tq, tk, tv, cold)
+    rng = np.random.default_rng(5)
+    pert = [0.3 * rng.standard_normal(q64.shape) for _ in range(3)]
+    q2, k2, v2 = q64 + pert[0], k64 + pert[1], v64 + pert[2]
+    tq2, tk2, tv2 = (torch.from_numpy(x).to(torch.float32).unsqueeze(0).contiguous().to(DEV) for x in (q2, k2, v2))
+    q2, k2, v2 = (t[0].double().cpu().numpy() for t in (tq2, tk2, tv2))
+    sp(tq2, tk2, tv2, warm=True)
+    torch.cuda.synchronize()
+    hp = O.plan_head_warm(q2[0], k2[0], p, 0, cold[0], max_iter=2, tol=1e-4)
+    ref = O.attend_fit_apply(q2[0], k2[0], v2[0], p, hp)
+    info = sp.info()[0]
+    kl, ql = np_(sp.export("KEY_LABELS"))[0], np_(sp.export("QUERY_LABELS"))[0]
+    agree = np.mean(kl == hp.key_labels), np.mean(ql == hp.query_labels)
+    say(f"  iters gpu {info['key_iters']}/{info['query_iters']} oracle {hp.key_iters}/{hp.query_iters}; "
+        f"label agreement key {agree[0]:.4f} query {agree[1]:.4f}")
+    assert info["key_iters"] <= 2 and info["query_iters"] <= 2
+    assert agree[0] >= 0.99 and agree[1] >= 0.99
+    N = configs.seq_len(w)
+    mask = np.ones(N, bool)
+    mask[hp.probes] = False
+    mask[np_(sp.export("PROBES"))[0]] = False
+    dn = O.dense_attention(q2[0], k2[0], v2[0], p["scale"])
+    g = O.rel_l2(np_(sp.out[0])[0][mask], dn[mask])
+    o = O.rel_l2(ref.out[mask], dn[mask])
+    say(f"  mean unprobed error gpu {g.mean():.4f} oracle {o.mean():.4f}")
+    assert abs(g.mean() - o.mean()) <= 0.05 * o.mean()
+    if agree == (1.0, 1.0):
+        # same partitions: permutations, offsets and probes are integer functions of them
+        # (the route also depends on the float group masses, so it is not compared here)
+        for kind, want in (("KEY_PERM", hp.k_perm), ("QUERY_PERM", hp.q_perm), ("PROBES", hp.probes)):
+            assert np.array_equal(np_(sp.export(kind))[0], want), kind
+        assert np.array_equal(np_(sp.export("KEY_OFFSETS"))[0][:hp.Ck + 1], hp.k_off)
+        assert np.array_equal(np_(sp.export("QUERY_OFFSETS"))[0][:hp.Cq + 1], hp.q_off)

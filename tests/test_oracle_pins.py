@@ -537,3 +537,72 @@ def test_row_subset_entry_matches_whole_call():
     np.testing.assert_allclose(sub["o_sparse"], r.o_sparse[rows], rtol=1e-12, atol=1e-12)
     np.testing.assert_allclose(sub["theta"], r.theta, rtol=1e-9, atol=1e-12)
     np.testing.assert_allclose(sub["out"], r.out[rows], rtol=1e-9, atol=1e-12)
+
+
+# ---------------------------------------------------------------- warm-started planning
+def _clustered(rng, N, d, C, sep=4.0):
+    means = sep * rng.standard_normal((C, d)) / math.sqrt(d)
+    lab = rng.integers(0, C, N)
+    return means[lab] + 0.3 * rng.standard_normal((N, d))
+
+
+def test_warm_key_init_is_the_group_mean_of_responses():
+    # a key group's response centroid is the response of its mean key (responses are linear)
+    rng = np.random.default_rng(30)
+    N, d, S = 200, 8, 12
+    q, k = _clustered(rng, N, d, 5), _clustered(rng, N, d, 5)
+    p = dict(_tiny_cfg(N, d), n_sampled=S)
+    hp = O.plan_head(q, k, p, head=0, max_iter=25, tol=1e-4)
+    qs = q[hp.sampled]
+    RK = O.key_responses(k, qs, p["scale"])
+    np.testing.assert_allclose(O.key_responses(hp.key_centroids, qs, p["scale"]),
+                               O.group_means(RK, hp.key_labels, hp.Ck), rtol=1e-10, atol=1e-12)
+
+
+def test_warm_query_init_is_the_group_mean_of_features():
+    # F_i = (s / RMS_i) q_i C_k^T, so a query group's feature mean is its representative times C_k^T
+    rng = np.random.default_rng(31)
+    N, d = 200, 8
+    q, k = _clustered(rng, N, d, 5), _clustered(rng, N, d, 5)
+    p = _tiny_cfg(N, d)
+    hp = O.plan_head(q, k, p, head=2, max_iter=25, tol=1e-4)
+    _, F = O.query_features(q, hp.key_centroids, p["scale"])
+    np.testing.assert_allclose(hp.query_reps @ hp.key_centroids.T, O.group_means(F, hp.query_labels, hp.Cq),
+                               rtol=1e-10, atol=1e-12)
+
+
+def test_warm_start_from_a_fixed_point_keeps_the_partition():
+    # cold k-means run to a fixed point (tol 0); warm-starting on the same inputs must
+    # reproduce both partitions exactly, stopping after the second assignment (the warm
+    # centroids equal the final ones up to rounding, hence a round-off tolerance)
+    rng = np.random.default_rng(32)
+    N, d = 240, 8
+    q, k = _clustered(rng, N, d, 6), _clustered(rng, N, d, 6)
+    p = _tiny_cfg(N, d)
+    cold = O.plan_head(q, k, p, head=1, max_iter=500, tol=0.0)
+    warm = O.plan_head_warm(q, k, p, head=1, prev=cold, max_iter=25, tol=1e-12)
+    assert np.array_equal(warm.key_labels, cold.key_labels)
+    assert np.array_equal(warm.query_labels, cold.query_labels)
+    assert (warm.Ck, warm.Cq) == (cold.Ck, cold.Cq)
+    assert warm.key_iters == 2 and warm.query_iters == 2
+    assert np.array_equal(warm.probes, cold.probes)
+
+
+def test_warm_start_obeys_its_iteration_limit_and_drops_empty_groups():
+    rng = np.random.default_rng(33)
+    N, d = 240, 8
+    q, k = _clustered(rng, N, d, 6), _clustered(rng, N, d, 6)
+    p = _tiny_cfg(N, d)
+    cold = O.plan_head(q, k, p, head=0, max_iter=25, tol=1e-4)
+    q2 = q + 0.8 * rng.standard_normal(q.shape)
+    k2 = k + 0.8 * rng.standard_normal(k.shape)
+    warm = O.plan_head_warm(q2, k2, p, head=0, prev=cold, max_iter=2, tol=1e-4)
+    assert warm.key_iters <= 2 and warm.query_iters <= 2
+    assert warm.Ck <= cold.Ck and warm.Cq <= cold.Cq
+    for lab, C in ((warm.key_labels, warm.Ck), (warm.query_labels, warm.Cq)):
+        assert set(np.unique(lab)) == set(range(C))
+    # the two iterations are those of lloyd_from on the mapped centroids
+    qs = q2[warm.sampled]
+    RK = O.key_responses(k2, qs, p["scale"])
+    ref = O.lloyd_from(RK, O.key_responses(cold.key_centroids, qs, p["scale"]), 2, 1e-4)
+    assert np.array_equal(O.compact_labels(ref.labels, cold.Ck)[0], warm.key_labels)
