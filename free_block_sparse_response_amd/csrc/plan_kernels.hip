@@ -202,6 +202,38 @@ __global__ __launch_bounds__(256) void k_select_probes(Dims D, Bufs B) {
   }
 }
 
+// Probe rows of the comparison selectors (paper Table 4): random = the M tokens with the
+// smallest probe hash; uniform = tokens floor((2p + 1) N / 2M), evenly spaced in token
+// (raster) order. Ascending token id, unit weights.
+__global__ __launch_bounds__(1024) void k_select_probes_plain(Dims D, Bufs B) {
+  const int bh = blockIdx.x;
+  int* out = B.probes + (size_t)bh * D.M;
+  if (D.probe_sel == 1) {
+    const uint64_t base = head_hash_base(D.seed, kStreamProbes, (uint64_t)bh);
+    select_smallest<1024>(D.N, D.M, [](int i) { return i; }, base, out);
+  } else {
+    for (int r = threadIdx.x; r < D.M; r += 1024) out[r] = (int)(((2ll * r + 1) * D.N) / (2ll * D.M));
+  }
+  __syncthreads();
+  for (int r = threadIdx.x; r < D.M; r += 1024) {
+    B.pweights[(size_t)bh * D.M + r] = 1.f;
+    B.pslot[(size_t)bh * D.N + out[r]] = r;
+  }
+}
+
+// Identity Lloyd metric: semantic partitions cluster the raw vectors (paper Table 2).
+template <int DD>
+__global__ void k_identity_metric(Dims D, Bufs B) {
+  const int bh = blockIdx.y;
+  for (int e = blockIdx.x * blockDim.x + threadIdx.x; e < DD * DD; e += gridDim.x * blockDim.x) {
+    const float v = (e / DD == e % DD) ? 1.f : 0.f;
+    const size_t o = (size_t)bh * DD * DD + e;
+    B.metric[o] = v;
+    B.metric_h[o] = (bf16)v;
+    B.metric_l[o] = (bf16)0.f;
+  }
+}
+
 // =====================================================================================
 // Small dense helpers
 // =====================================================================================
@@ -747,8 +779,8 @@ __global__ __launch_bounds__(256) void k_query_reps(const T* q, Dims D, Bufs B) 
   if (a >= B.qst[bh].c_final) return;
   const int* off = B.qoff + (size_t)bh * (D.Cq + 1);
   const int s0 = off[a], n = off[a + 1] - off[a];
-  group_mean<T, DD>(q + (size_t)bh * D.N * DD, B.alpha + (size_t)bh * D.N, B.qperm + (size_t)bh * D.N + s0, n, m,
-                    sh);
+  group_mean<T, DD>(q + (size_t)bh * D.N * DD, B.alpha ? B.alpha + (size_t)bh * D.N : nullptr,
+                    B.qperm + (size_t)bh * D.N + s0, n, m, sh);
   if (threadIdx.x < DD) B.qcent[((size_t)bh * D.Cq + a) * DD + threadIdx.x] = m[threadIdx.x];
 }
 
@@ -1574,6 +1606,35 @@ static void group_mass(const T* q, const Dims& D, const Bufs& B, hipStream_t s) 
   }
 }
 
+// Lloyd metric of the key side: s^2 Q_S^T Q_S (responses to the sampled queries), or the
+// identity for the semantic partition.
+template <int DD>
+static void key_metric(const Dims& D, const Bufs& B, hipStream_t s) {
+  if (D.partition == 1)
+    hipLaunchKernelGGL((k_identity_metric<DD>), dim3(DD * DD / 256, D.BH), dim3(256), 0, s, D, B);
+  else
+    hipLaunchKernelGGL((k_gram<DD>), dim3(DD * DD / 256, D.BH), dim3(256), 0, s, B.qs, D.S, (const KmState*)nullptr,
+                       D.scale * D.scale, B.metric, B.metric_h, B.metric_l);
+}
+
+// Metric, row constants and row scales of the query side: responses to the key centroids,
+// RMS-normalised (G_k = C_k^T C_k, alpha = s / RMS), or raw queries (identity, alpha = 1).
+// Returns the buffers the query Lloyd runs with.
+template <typename T, int DD>
+static Bufs query_side(const T* q, const Dims& D, const Bufs& B, hipStream_t s) {
+  Bufs Bq = B;
+  if (D.partition == 0) {
+    hipLaunchKernelGGL((k_gram<DD>), dim3(DD * DD / 256, D.BH), dim3(256), 0, s, B.kcent, D.Ck, (const KmState*)B.kst,
+                       1.f, B.metric, B.metric_h, B.metric_l);
+    rowquad<T, DD>(q, D, B, B.metric, B.rowconst, B.alpha, (const KmState*)B.kst, s);
+  } else {
+    hipLaunchKernelGGL((k_identity_metric<DD>), dim3(DD * DD / 256, D.BH), dim3(256), 0, s, D, B);
+    rowquad<T, DD>(q, D, B, B.metric, B.rowconst, (float*)nullptr, (const KmState*)nullptr, s);
+    Bq.alpha = nullptr;
+  }
+  return Bq;
+}
+
 template <typename T, int DD>
 static void plan_impl(const void* qv, const void* kv, const Dims& D, const Bufs& B, hipStream_t s) {
   const T* q = (const T*)qv;
@@ -1581,8 +1642,7 @@ static void plan_impl(const void* qv, const void* kv, const Dims& D, const Bufs&
   // 01: sampled queries and their key-response metric
   hipLaunchKernelGGL(k_select_all, dim3(D.BH, 3), dim3(1024), 0, s, D, B);
   hipLaunchKernelGGL((k_gather_rows<T>), dim3(D.S, D.BH), dim3(DD), 0, s, q, B.sampled, D.N, D.S, DD, B.qs);
-  hipLaunchKernelGGL((k_gram<DD>), dim3(DD * DD / 256, D.BH), dim3(256), 0, s, B.qs, D.S, (const KmState*)nullptr,
-                     D.scale * D.scale, B.metric, B.metric_h, B.metric_l);
+  key_metric<DD>(D, B, s);
   // 02a: paired K/V groups by Lloyd on the key responses
   Bufs Bk = B;
   Bk.alpha = nullptr;
@@ -1591,12 +1651,10 @@ static void plan_impl(const void* qv, const void* kv, const Dims& D, const Bufs&
   hipLaunchKernelGGL(k_km_compact, dim3(D.BH), dim3(1024), 0, s, D, B, D.Ck, B.kst, B.klab, B.koff, D.Ck + 1);
   hipLaunchKernelGGL((k_key_centroids<T, DD>), dim3(D.Ck, D.BH), dim3(256), 0, s, k, D, B);
   // 02b: query-response coordinates (RMS-normalised) and query groups
-  hipLaunchKernelGGL((k_gram<DD>), dim3(DD * DD / 256, D.BH), dim3(256), 0, s, B.kcent, D.Ck, (const KmState*)B.kst, 1.f,
-                     B.metric, B.metric_h, B.metric_l);
-  rowquad<T, DD>(q, D, B, B.metric, B.rowconst, B.alpha, (const KmState*)B.kst, s);
-  run_lloyd<T, DD>(q, D, B, D.Cq, B.init_q, B.qst, B.qperm, s);
+  const Bufs Bq = query_side<T, DD>(q, D, B, s);
+  run_lloyd<T, DD>(q, D, Bq, D.Cq, B.init_q, B.qst, B.qperm, s);
   hipLaunchKernelGGL(k_km_compact, dim3(D.BH), dim3(1024), 0, s, D, B, D.Cq, B.qst, B.qlab, B.qoff, D.Cq + 1);
-  hipLaunchKernelGGL((k_query_reps<T, DD>), dim3(D.Cq, D.BH), dim3(256), 0, s, q, D, B);
+  hipLaunchKernelGGL((k_query_reps<T, DD>), dim3(D.Cq, D.BH), dim3(256), 0, s, q, D, Bq);
   hipLaunchKernelGGL(k_build_tiles, dim3(D.BH), dim3(1024), 0, s, D, B);
   // 03: group masses
   group_mass<T, DD>(q, D, B, s);
@@ -1612,8 +1670,7 @@ static void plan_warm_impl(const void* qv, const void* kv, const Dims& D0, const
   D.max_iter = D0.warm_iter;
   hipLaunchKernelGGL(k_select_all, dim3(D.BH, 3), dim3(1024), 0, s, D, B);
   hipLaunchKernelGGL((k_gather_rows<T>), dim3(D.S, D.BH), dim3(DD), 0, s, q, B.sampled, D.N, D.S, DD, B.qs);
-  hipLaunchKernelGGL((k_gram<DD>), dim3(DD * DD / 256, D.BH), dim3(256), 0, s, B.qs, D.S, (const KmState*)nullptr,
-                     D.scale * D.scale, B.metric, B.metric_h, B.metric_l);
+  key_metric<DD>(D, B, s);
   // key groups from the previous key centroids
   Bufs Bk = B;
   Bk.alpha = nullptr;
@@ -1624,14 +1681,12 @@ static void plan_warm_impl(const void* qv, const void* kv, const Dims& D0, const
   hipLaunchKernelGGL(k_km_compact, dim3(D.BH), dim3(1024), 0, s, D, B, D.Ck, B.kst, B.klab, B.koff, D.Ck + 1);
   hipLaunchKernelGGL((k_key_centroids<T, DD>), dim3(D.Ck, D.BH), dim3(256), 0, s, k, D, B);
   // query groups from the previous query representatives
-  hipLaunchKernelGGL((k_gram<DD>), dim3(DD * DD / 256, D.BH), dim3(256), 0, s, B.kcent, D.Ck, (const KmState*)B.kst, 1.f,
-                     B.metric, B.metric_h, B.metric_l);
-  rowquad<T, DD>(q, D, B, B.metric, B.rowconst, B.alpha, (const KmState*)B.kst, s);
-  hipLaunchKernelGGL((k_km_warm_init<DD>), dim3(D.Cq, D.BH), dim3(256), 0, s, D, B, B.qcent, D.Cq, B.qst);
+  const Bufs Bq = query_side<T, DD>(q, D, B, s);
+  hipLaunchKernelGGL((k_km_warm_init<DD>), dim3(D.Cq, D.BH), dim3(256), 0, s, D, Bq, B.qcent, D.Cq, B.qst);
   hipLaunchKernelGGL(k_state_reset, dim3((D.BH + 63) / 64), dim3(64), 0, s, B.qst, D.BH, D.Cq, 0x7fffffff);
-  lloyd_iterations<T, DD>(q, D, B, D.Cq, B.qst, B.qperm, s);
+  lloyd_iterations<T, DD>(q, D, Bq, D.Cq, B.qst, B.qperm, s);
   hipLaunchKernelGGL(k_km_compact, dim3(D.BH), dim3(1024), 0, s, D, B, D.Cq, B.qst, B.qlab, B.qoff, D.Cq + 1);
-  hipLaunchKernelGGL((k_query_reps<T, DD>), dim3(D.Cq, D.BH), dim3(256), 0, s, q, D, B);
+  hipLaunchKernelGGL((k_query_reps<T, DD>), dim3(D.Cq, D.BH), dim3(256), 0, s, q, D, Bq);
   hipLaunchKernelGGL(k_build_tiles, dim3(D.BH), dim3(1024), 0, s, D, B);
   group_mass<T, DD>(q, D, B, s);
 }
@@ -1656,11 +1711,9 @@ static void plan_labels_impl(const void* qv, const void* kv, const int* klab, co
   hipLaunchKernelGGL(k_km_scan_head, dim3(D.BH), dim3(256), 0, s, D, B, D.Cq, B.qst, 1);
   hipLaunchKernelGGL(k_km_scatter, dim3(D.nblk, D.BH), dim3(kKmRows), 0, s, D, B, B.qst, 1, B.qperm);
   hipLaunchKernelGGL(k_km_compact, dim3(D.BH), dim3(1024), 0, s, D, B, D.Cq, B.qst, B.qlab, B.qoff, D.Cq + 1);
-  // query scales alpha (as the planner computes them) for the warm-start representatives
-  hipLaunchKernelGGL((k_gram<DD>), dim3(DD * DD / 256, D.BH), dim3(256), 0, s, B.kcent, D.Ck, (const KmState*)B.kst, 1.f,
-                     B.metric, B.metric_h, B.metric_l);
-  rowquad<T, DD>(q, D, B, B.metric, B.rowconst, B.alpha, (const KmState*)B.kst, s);
-  hipLaunchKernelGGL((k_query_reps<T, DD>), dim3(D.Cq, D.BH), dim3(256), 0, s, q, D, B);
+  // query scales (as the planner computes them) for the warm-start representatives
+  const Bufs Bq = query_side<T, DD>(q, D, B, s);
+  hipLaunchKernelGGL((k_query_reps<T, DD>), dim3(D.Cq, D.BH), dim3(256), 0, s, q, D, Bq);
   hipLaunchKernelGGL(k_build_tiles, dim3(D.BH), dim3(1024), 0, s, D, B);
   if (mass) {
     (void)hipMemcpyAsync(B.u, mass, sizeof(long long) * (size_t)D.BH * D.Cq * D.Ck, hipMemcpyDeviceToDevice, s);
@@ -1688,9 +1741,11 @@ void launch_route_probes(const Dims& D, const Bufs& B, hipStream_t s) {
   hipLaunchKernelGGL(k_route_tau, dim3(D.BH), dim3(1024), 0, s, D, B);
   hipLaunchKernelGGL(k_route_emit, dim3(D.Cq, D.BH), dim3(1024), 0, s, D, B);
   hipLaunchKernelGGL(k_fill_i32, dim3(256), dim3(256), 0, s, B.pslot, (long long)D.BH * D.N, -1);
-  if (D.M > 0) {
+  if (D.M > 0 && D.probe_sel == 0) {
     hipLaunchKernelGGL(k_probe_alloc, dim3(D.BH), dim3(1024), 0, s, D, B);
     hipLaunchKernelGGL(k_select_probes, dim3(D.Cq, D.BH), dim3(256), 0, s, D, B);
+  } else if (D.M > 0) {
+    hipLaunchKernelGGL(k_select_probes_plain, dim3(D.BH), dim3(1024), 0, s, D, B);
   }
 }
 

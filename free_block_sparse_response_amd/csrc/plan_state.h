@@ -46,6 +46,9 @@ struct Dims {
   float lambda;
   int pen_bias;
   int assign_lo;  // Lloyd assignment with the bf16 remainder of the centroid operand
+  int partition;  // 0 response-coupled, 1 semantic (raw K and Q), 2 key responses + raw Q
+  int correction; // 0 weighted ridge, 1 mean-only, 2 none
+  int probe_sel;  // 0 query-group stratified, 1 random, 2 uniform in token order
   uint64_t seed;
 };
 

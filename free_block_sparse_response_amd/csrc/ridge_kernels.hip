@@ -361,10 +361,35 @@ __global__ __launch_bounds__(256) void k_apply_bf16(Dims D, Bufs B, const bf16* 
   }
 }
 
+// Correction families other than the ridge (paper Table 4 "Mean-only"; repair disabled in
+// the Table 2 partition rows): Theta = 0 except the bias row, which is the weighted mean
+// probe residual (mean-only) or zero (none). Probes summed in order; fp64 accumulation.
+template <int DD>
+__global__ __launch_bounds__(DD) void k_fit_mean(Dims D, Bufs B, const float* o_psp, const float* o_dn,
+                                                 const float* weights, float* coeffs) {
+  const int bh = blockIdx.x, i = threadIdx.x;
+  float* th = coeffs + (size_t)bh * (DD + 1) * DD;
+  for (int r = 0; r < DD; ++r) th[(size_t)r * DD + i] = 0.f;
+  double num = 0.0, den = 0.0;
+  if (D.correction == 1) {
+    const float* wp = weights ? weights + (size_t)bh * D.M : B.pweights + (size_t)bh * D.M;
+    for (int p = 0; p < D.M; ++p) {
+      const size_t o = ((size_t)bh * D.M + p) * DD + i;
+      num += (double)wp[p] * ((double)o_dn[o] - (double)o_psp[o]);
+      den += (double)wp[p];
+    }
+  }
+  th[(size_t)DD * DD + i] = den > 0.0 ? (float)(num / den) : 0.f;
+}
+
 template <int DD>
 static void fit_impl(const Dims& D, const Bufs& B, const float* o_psp, const float* o_dn, const float* w, float* coeffs,
                      hipStream_t s) {
   constexpr int n = DD + 1;
+  if (D.correction != 0) {
+    hipLaunchKernelGGL((k_fit_mean<DD>), dim3(D.BH), dim3(DD), 0, s, D, B, o_psp, o_dn, w, coeffs);
+    return;
+  }
   if (D.M > 0) {
     dim3 g((n + 31) / 32, (n + DD + 31) / 32, D.BH);
     hipLaunchKernelGGL((k_ridge_gram<DD>), g, dim3(256), 0, s, D, B, o_psp, o_dn, w);

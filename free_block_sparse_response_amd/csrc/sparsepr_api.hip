@@ -188,6 +188,9 @@ sparsepr_status sparsepr_plan_create(const sparsepr_config* cfg, sparsepr_plan_t
   if (!finite_d(c.softmax_scale) || c.softmax_scale < 0.f) return SPARSEPR_ERR_INVALID_ARG;
   if (c.assign_precision != 0 && c.assign_precision != 1) return SPARSEPR_ERR_INVALID_ARG;
   if (c.warm_iters < 0 || c.warm_iters > 10000) return SPARSEPR_ERR_INVALID_ARG;
+  if (c.partition < 0 || c.partition > 2) return SPARSEPR_ERR_INVALID_ARG;
+  if (c.correction < 0 || c.correction > 2) return SPARSEPR_ERR_INVALID_ARG;
+  if (c.probe_selector < 0 || c.probe_selector > 2) return SPARSEPR_ERR_INVALID_ARG;
 
   sparsepr_plan_s* p = new (std::nothrow) sparsepr_plan_s();
   if (!p) return SPARSEPR_ERR_INVALID_ARG;
@@ -226,6 +229,9 @@ sparsepr_status sparsepr_plan_create(const sparsepr_config* cfg, sparsepr_plan_t
   D.lambda = c.ridge_lambda;
   D.pen_bias = c.penalize_bias ? 1 : 0;
   D.assign_lo = c.assign_precision ? 1 : 0;
+  D.partition = c.partition;
+  D.correction = c.correction;
+  D.probe_sel = c.probe_selector;
   D.seed = c.seed;
   carve(D, nullptr, &p->ws_bytes);
   p->ws = nullptr;

@@ -81,6 +81,16 @@ typedef struct {
                                            /*   1 bf16 + bf16 remainder (~16-bit operand) */
   int32_t warm_iters;                      /* Lloyd limit of sparsepr_plan_warm; 0 -> 2   */
                                            /* (paper Table C.1: 2 for subsequent calls)   */
+  /* Comparison settings of paper Tables 2 and 4 (0 = the method everywhere):             */
+  int32_t partition;                       /* 0 response-coupled; 1 semantic (k-means on  */
+                                           /*   raw K and raw Q); 2 key-response K/V      */
+                                           /*   groups with semantic query groups         */
+  int32_t correction;                      /* 0 weighted ridge; 1 mean-only (Theta bias = */
+                                           /*   weighted mean probe residual); 2 none     */
+                                           /*   (unprobed rows keep the sparse output)    */
+  int32_t probe_selector;                  /* 0 query-group stratified; 1 random (smallest*/
+                                           /*   probe hash over all tokens); 2 uniform    */
+                                           /*   (tokens floor((2p+1)N/2M)); 1, 2 weigh 1  */
 } sparsepr_config;
 
 typedef struct sparsepr_plan_s* sparsepr_plan_t;

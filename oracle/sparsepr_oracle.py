@@ -355,6 +355,25 @@ def select_probes(seed, head, q_perm, q_off, n_q, M, N):
     return np.concatenate(idx).astype(np.int64), np.concatenate(wt)
 
 
+PROBES_STRATIFIED = 0  # query-group stratified (the method, [T4])
+PROBES_RANDOM = 1      # [T4] "Random probes"
+PROBES_UNIFORM = 2     # [T4] "Uniform spatiotemporal probes"
+
+
+def select_probes_plain(seed, head, N, M, selector):
+    """The comparison probe sets of [T4], ascending token id, all weights 1 (reading).
+
+    Random: the M tokens with the smallest probe hash (uniform without replacement).
+    Uniform spatiotemporal: tokens floor((p + 1/2) N / M), p = 0..M-1, evenly spaced in
+    the raster order of the latent grid (reading: the pages name the set only).
+    """
+    if M == 0:
+        return np.zeros(0, dtype=np.int64)
+    if selector == PROBES_RANDOM:
+        return select_smallest(seed, STREAM_PROBES, head, np.arange(N), M).astype(np.int64)
+    return ((2 * np.arange(M, dtype=np.int64) + 1) * N // (2 * M)).astype(np.int64)
+
+
 # ----------------------------------------------------------------------------------
 # Probe-Fitted Residual Reconstruction ([abstract]; [method] PFRR panel)
 # ----------------------------------------------------------------------------------
@@ -419,6 +438,29 @@ def ridge_fit(o_sp_probe, o_dn_probe, weights, lam, penalize_bias=False):
     return solve_upper(L.T, solve_lower(L, B))
 
 
+CORRECTION_RIDGE = 0      # full weighted ridge (the method)
+CORRECTION_MEAN_ONLY = 1  # [T4] "Mean-only": add the weighted mean probe residual
+CORRECTION_NONE = 2       # repair disabled ([T2] partition rows): sparse output kept
+
+
+def fit_correction(o_sp_probe, o_dn_probe, weights, p):
+    """Theta of the correction family p["correction"] (ridge by default).
+
+    Mean-only is the lam -> infinity limit of the ridge with the bias unpenalised:
+    Theta = [0; sum_p w_p r_p / sum_p w_p]. With repair disabled Theta = 0, so unprobed
+    rows keep their sparse output (probe rows still return the exact output).
+    """
+    mode = p.get("correction", CORRECTION_RIDGE)
+    M, d = o_sp_probe.shape
+    if mode == CORRECTION_RIDGE:
+        return ridge_fit(o_sp_probe, o_dn_probe, weights, p["ridge_lambda"], p.get("penalize_bias", False))
+    theta = np.zeros((d + 1, d))
+    if mode == CORRECTION_MEAN_ONLY and M > 0:
+        w = np.asarray(weights, dtype=np.float64)
+        theta[d] = (w[:, None] * (o_dn_probe - o_sp_probe)).sum(axis=0) / w.sum()
+    return theta
+
+
 def apply_residual(o_sp, probes, o_dn_probe, theta):
     """out_i = o_i + [o_i, 1] Theta for unprobed rows; probe rows keep their exact output."""
     out = o_sp + o_sp @ theta[:-1] + theta[-1][None, :]
@@ -477,18 +519,32 @@ class HeadPlan:
     pairs: int = 0
 
 
+PARTITION_RESPONSE = 0   # response-coupled: key responses, then query responses (the method)
+PARTITION_SEMANTIC = 1   # k-means on the raw keys and on the raw queries ([T2] "Semantic partition")
+PARTITION_KEY_RESPONSE = 2  # key-response K/V groups, semantic query groups ([T2] second row)
+
+
 def plan_head(q, k, p, head, max_iter, tol):
-    """Response-Coupled Partitioning, masses, routing and probes for one head."""
+    """Response-Coupled Partitioning, masses, routing and probes for one head.
+
+    p["partition"] selects the partition of [T2]: the method's response-coupled one
+    (default), the semantic baseline (Lloyd on raw K and raw Q), or key-response K/V
+    groups with semantic query groups. Everything after the two partitions is the same.
+    """
     N = q.shape[0]
     s = p["scale"]
+    mode = p.get("partition", PARTITION_RESPONSE)
     hp = HeadPlan()
     hp.sampled = select_smallest(p["seed"], STREAM_SAMPLED, head, np.arange(N), p["n_sampled"])
-    RK = key_responses(k, q[hp.sampled], s)
+    RK = k if mode == PARTITION_SEMANTIC else key_responses(k, q[hp.sampled], s)
     kinit = select_smallest(p["seed"], STREAM_KEY_INIT, head, np.arange(N), p["n_key_groups"])
     res = lloyd(RK, kinit, max_iter, tol)
     hp.key_iters = res.iterations
     hp.key_labels, hp.Ck = compact_labels(res.labels, p["n_key_groups"])
-    _, F = query_features(q, group_means(k, hp.key_labels, hp.Ck), s)
+    if mode == PARTITION_RESPONSE:
+        _, F = query_features(q, group_means(k, hp.key_labels, hp.Ck), s)
+    else:
+        F = q
     qinit = select_smallest(p["seed"], STREAM_QUERY_INIT, head, np.arange(N), p["n_query_groups"])
     res = lloyd(F, qinit, max_iter, tol)
     hp.query_iters = res.iterations
@@ -522,14 +578,20 @@ def plan_head_warm(q, k, p, head, prev, max_iter=2, tol=1e-4):
     s = p["scale"]
     hp = HeadPlan()
     hp.sampled = select_smallest(p["seed"], STREAM_SAMPLED, head, np.arange(N), p["n_sampled"])
+    mode = p.get("partition", PARTITION_RESPONSE)
     qs = q[hp.sampled]
-    RK = key_responses(k, qs, s)
-    res = lloyd_from(RK, key_responses(prev.key_centroids, qs, s), max_iter, tol)
+    if mode == PARTITION_SEMANTIC:
+        res = lloyd_from(k, prev.key_centroids, max_iter, tol)
+    else:
+        res = lloyd_from(key_responses(k, qs, s), key_responses(prev.key_centroids, qs, s), max_iter, tol)
     hp.key_iters = res.iterations
     hp.key_labels, hp.Ck = compact_labels(res.labels, prev.Ck)
     kc = group_means(k, hp.key_labels, hp.Ck)
-    _, F = query_features(q, kc, s)
-    res = lloyd_from(F, prev.query_reps @ kc.T, max_iter, tol)
+    if mode == PARTITION_RESPONSE:
+        _, F = query_features(q, kc, s)
+        res = lloyd_from(F, prev.query_reps @ kc.T, max_iter, tol)
+    else:
+        res = lloyd_from(q, prev.query_reps, max_iter, tol)
     hp.query_iters = res.iterations
     hp.query_labels, hp.Cq = compact_labels(res.labels, prev.Cq)
     return finish_plan(q, k, p, head, hp)
@@ -549,14 +611,21 @@ def finish_plan(q, k, p, head, hp, u=None, probes=None):
     hp.q_perm, hp.q_off, hp.n_q = group_permutation(hp.query_labels, hp.Cq)
     hp.key_centroids = group_means(k, hp.key_labels, hp.Ck)
     L, _ = query_features(q, hp.key_centroids, p["scale"])
-    hp.query_reps = query_representatives(q, L, p["scale"], hp.query_labels, hp.Cq)
+    if p.get("partition", PARTITION_RESPONSE) == PARTITION_RESPONSE:
+        hp.query_reps = query_representatives(q, L, p["scale"], hp.query_labels, hp.Cq)
+    else:
+        hp.query_reps = group_means(q, hp.query_labels, hp.Cq)
     if u is None:
         hp.P, hp.u = group_masses(L, hp.n_k, hp.query_labels, hp.Cq)
     else:
         hp.u = np.asarray(u, dtype=np.int64)
     hp.route = route(hp.u, hp.n_q, hp.n_k, N, M, p["density"])
-    if probes is None:
+    sel = p.get("probe_selector", PROBES_STRATIFIED)
+    if probes is None and sel == PROBES_STRATIFIED:
         hp.probes, hp.weights = select_probes(p["seed"], head, hp.q_perm, hp.q_off, hp.n_q, M, N)
+    elif probes is None:
+        hp.probes = select_probes_plain(p["seed"], head, N, M, sel)
+        hp.weights = np.ones(len(hp.probes))
     else:
         hp.probes = np.asarray(probes, dtype=np.int64)
         hp.weights = np.ones(len(hp.probes))
@@ -578,7 +647,7 @@ def attend_fit_apply(q, k, v, p, hp):
     o_sp = block_sparse_attention(q, k, v, s, hp.q_perm, hp.q_off, hp.k_perm, hp.k_off,
                                   hp.route.row_ptr, hp.route.cols)
     o_dn = dense_attention(q[hp.probes], k, v, s)
-    theta = ridge_fit(o_sp[hp.probes], o_dn, hp.weights, p["ridge_lambda"], p.get("penalize_bias", False))
+    theta = fit_correction(o_sp[hp.probes], o_dn, hp.weights, p)
     out = apply_residual(o_sp, hp.probes, o_dn, theta)
     return HeadResult(plan=hp, o_sparse=o_sp, o_probe_dense=o_dn, theta=theta, out=out)
 
@@ -589,7 +658,7 @@ def attend_fit_apply_rows(q, k, v, p, hp, rows):
     rt = hp.route
     o_sp_pr = block_sparse_rows(q, k, v, s, hp.probes, hp.query_labels, hp.k_perm, hp.k_off, rt.row_ptr, rt.cols)
     o_dn = dense_attention(q[hp.probes], k, v, s)
-    theta = ridge_fit(o_sp_pr, o_dn, hp.weights, p["ridge_lambda"], p.get("penalize_bias", False))
+    theta = fit_correction(o_sp_pr, o_dn, hp.weights, p)
     o_sp = block_sparse_rows(q, k, v, s, rows, hp.query_labels, hp.k_perm, hp.k_off, rt.row_ptr, rt.cols)
     out = o_sp + o_sp @ theta[:-1] + theta[-1][None, :]
     slot = {int(t): j for j, t in enumerate(hp.probes)}
@@ -606,7 +675,10 @@ def call_params(cfg):
                 n_sampled=cfg["n_sampled"], n_key_groups=cfg["n_key_groups"],
                 n_query_groups=cfg["n_query_groups"], n_probes=cfg["n_probes"],
                 density=cfg["density"], ridge_lambda=cfg["ridge_lambda"],
-                penalize_bias=cfg.get("penalize_bias", False))
+                penalize_bias=cfg.get("penalize_bias", False),
+                partition=cfg.get("partition", PARTITION_RESPONSE),
+                correction=cfg.get("correction", CORRECTION_RIDGE),
+                probe_selector=cfg.get("probe_selector", PROBES_STRATIFIED))
 
 
 def sparsepr_head(q, k, v, p, head, max_iter=25, tol=1e-4):

@@ -63,6 +63,9 @@ def _create(lib, cfg):
     (dict(batch=0), L.SPARSEPR_ERR_INVALID_ARG),
     (dict(assign_precision=2), L.SPARSEPR_ERR_INVALID_ARG),
     (dict(warm_iters=-1), L.SPARSEPR_ERR_INVALID_ARG),
+    (dict(partition=3), L.SPARSEPR_ERR_INVALID_ARG),
+    (dict(correction=-1), L.SPARSEPR_ERR_INVALID_ARG),
+    (dict(probe_selector=3), L.SPARSEPR_ERR_INVALID_ARG),
 ])
 def test_plan_create_rejects(lib, over, want):
     st, h = _create(lib, _cfg(**over))

@@ -239,15 +239,15 @@ def test_max_groups_1024_bf16():
 
 
 # ------------------------------------------------------------------- warm-started planning
-@pytest.mark.parametrize("name,heads", [("c1", [0]), ("c2", [0, 1])])
-def test_warm_plan_after_convergence_keeps_the_plan(name, heads):
+@pytest.mark.parametrize("name,heads,partition", [("c1", [0], 0), ("c2", [0, 1], 0), ("c2", [0], 1)])
+def test_warm_plan_after_convergence_keeps_the_plan(name, heads, partition):
     # k-means run until the inertia stops falling (tolerance 0): a warm start on the same
     # inputs starts from the centroids the cold plan ended with; it must keep (nearly) every
     # label, and when it keeps all of them every integer of the plan and the output must be
     # bitwise those of the cold plan (rounding can stop a cold run one step short of an
     # exact fixed point, hence the agreement bound)
-    w = configs.CONFIGS[name]
-    say(f"case: warm start after convergence, {name}, heads {heads}")
+    w = dict(configs.CONFIGS[name], partition=partition)
+    say(f"case: warm start after convergence, {name}, heads {heads}, partition {partition}")
     (tq, _), (tk, _), (tv, _) = inputs(w, heads)
     sp = SparsePR(config_from_workload(w, heads=len(heads), kmeans_max_iter=200, kmeans_tol=0.0, warm_iters=3),
                   device=DEV)
@@ -313,3 +313,14 @@ def test_warm_plan_on_new_inputs_matches_oracle_warm():
             assert np.array_equal(np_(sp.export(kind))[0], want), kind
         assert np.array_equal(np_(sp.export("KEY_OFFSETS"))[0][:hp.Ck + 1], hp.k_off)
         assert np.array_equal(np_(sp.export("QUERY_OFFSETS"))[0][:hp.Cq + 1], hp.q_off)
+
+
+# ------------------------------------------------------------------- comparison partitions
+@pytest.mark.parametrize("partition", [1, 2])
+@pytest.mark.parametrize("name", ["c1", "c2"])
+def test_comparison_partitions_match_oracle(name, partition):
+    # semantic K and Q groups (1), key-response K/V groups with semantic Q groups (2): the
+    # library's own k-means against the oracle's, by the unprobed error statistics
+    w = dict(configs.CONFIGS[name], partition=partition)
+    heads = [0] if name == "c1" else [0, 3]
+    _error_stats_vs_oracle(w, heads, rows_per_head=None if name == "c1" else 2048)

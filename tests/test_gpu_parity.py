@@ -106,3 +106,33 @@ def test_dense_entry_point_matches_oracle():
             e = max_rel(o[i], ref)
             say(f"  head {i}: dense rel-L2 {e:.2e}")
             assert e <= TOL[w["dtype"]] / 2
+
+
+# ------------------------------------------------------------- probe selectors and corrections
+@pytest.mark.parametrize("selector", [1, 2])
+@pytest.mark.parametrize("name", ["c1", "c2"])
+def test_plain_probe_selectors_from_labels(name, selector):
+    # random (smallest probe hash over all tokens) and uniform raster-order probes, unit
+    # weights: probes bit-exact, outputs within tolerance
+    w = configs.CONFIGS[name]
+    _parity_from_labels(w, [0] if name == "c1" else [0, 2], probe_selector=selector)
+
+
+@pytest.mark.parametrize("correction", [1, 2])
+@pytest.mark.parametrize("name", ["c1", "c2"])
+def test_corrections_from_labels(name, correction):
+    w = configs.CONFIGS[name]
+    sp, refs = _parity_from_labels(w, [0] if name == "c1" else [1, 4], correction=correction)
+    th = np_(sp.coeffs)
+    d = w["head_dim"]
+    for i, r in enumerate(refs):
+        assert np.all(th[0, i, :d] == 0.0)
+        # the bias is a mean of probe residuals: its error is bounded by that of the probe rows
+        scale = np.abs(r.o_probe_dense).max()
+        np.testing.assert_allclose(th[0, i, d], r.theta[d], rtol=0, atol=TOL[w["dtype"]] * scale)
+    if correction == 2:
+        out, osp = sp.out[0], sp.o_sparse[0]
+        for i, r in enumerate(refs):
+            un = torch.ones(out.shape[1], dtype=torch.bool, device=out.device)
+            un[torch.from_numpy(r.plan.probes).to(out.device)] = False
+            assert torch.equal(out[i][un], osp[i][un].to(out.dtype))

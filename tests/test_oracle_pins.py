@@ -606,3 +606,128 @@ def test_warm_start_obeys_its_iteration_limit_and_drops_empty_groups():
     RK = O.key_responses(k2, qs, p["scale"])
     ref = O.lloyd_from(RK, O.key_responses(cold.key_centroids, qs, p["scale"]), 2, 1e-4)
     assert np.array_equal(O.compact_labels(ref.labels, cold.Ck)[0], warm.key_labels)
+
+
+# ---------------------------------------------------------------- comparison settings (Tables 2, 4)
+def _planted_same_as(labels, planted):
+    """True iff two labelings induce the same partition."""
+    pairs = set(zip(labels.tolist(), planted.tolist()))
+    return len(pairs) == len(set(labels.tolist())) == len(set(planted.tolist()))
+
+
+def _hidden_key_clusters(rng, N, d, C):
+    # queries live in the first half of the coordinates; the planted key clusters differ only
+    # in the second half, so every key response s q k^T is blind to them
+    h = d // 2
+    q = np.zeros((N, d))
+    q[:, :h] = rng.standard_normal((N, h))
+    lab = np.arange(N) % C
+    means = np.zeros((C, d))
+    means[:, h:] = 6.0 * rng.standard_normal((C, d - h))
+    k = means[lab] + 0.05 * rng.standard_normal((N, d))
+    k[:, :h] = rng.standard_normal((N, h))
+    return q, k, lab
+
+
+def test_semantic_partition_clusters_raw_keys_and_queries():
+    # [T2] semantic baseline: k-means on raw K and raw Q. Planted raw clusters invisible to
+    # the key responses are recovered by the semantic partition and not by the response one.
+    rng = np.random.default_rng(40)
+    N, d, C = 240, 8, 3
+    q, k, lab = _hidden_key_clusters(rng, N, d, C)
+    qlab = rng.integers(0, C, N)
+    qmeans = np.zeros((C, d))
+    qmeans[:, : d // 2] = 6.0 * rng.standard_normal((C, d // 2))
+    q = qmeans[qlab] + 0.05 * rng.standard_normal((N, d))
+    q[:, d // 2:] = 0.0
+    p = dict(_tiny_cfg(N, d), n_key_groups=C, n_query_groups=C, n_sampled=24)
+    # Forgy rows vary with the head; Lloyd finds the planted clusters from a good start
+    sem_k = sem_q = rsp_k = 0
+    for head in range(20):
+        sem = O.plan_head(q, k, dict(p, partition=O.PARTITION_SEMANTIC), head, 50, 0.0)
+        rsp = O.plan_head(q, k, dict(p, partition=O.PARTITION_RESPONSE), head, 50, 0.0)
+        sem_k += _planted_same_as(sem.key_labels, lab)
+        sem_q += _planted_same_as(sem.query_labels, qlab)
+        rsp_k += _planted_same_as(rsp.key_labels, lab)
+    assert sem_k >= 2 and sem_q >= 2 and rsp_k == 0
+
+
+def test_key_response_partition_mixes_the_two_sides():
+    # [T2] second row: K/V groups of the response-coupled partition, query groups of the
+    # semantic one (both Lloyd runs start from the same Forgy rows in every mode)
+    rng = np.random.default_rng(41)
+    N, d = 200, 8
+    q, k = rng.standard_normal((N, d)), _clustered(rng, N, d, 5)
+    p = _tiny_cfg(N, d)
+    plans = {m: O.plan_head(q, k, dict(p, partition=m), 1, 25, 1e-4)
+             for m in (O.PARTITION_RESPONSE, O.PARTITION_SEMANTIC, O.PARTITION_KEY_RESPONSE)}
+    mix = plans[O.PARTITION_KEY_RESPONSE]
+    assert np.array_equal(mix.key_labels, plans[O.PARTITION_RESPONSE].key_labels)
+    assert np.array_equal(mix.query_labels, plans[O.PARTITION_SEMANTIC].query_labels)
+    assert not np.array_equal(plans[O.PARTITION_RESPONSE].query_labels, mix.query_labels)
+    # semantic query representatives are plain member means of q
+    np.testing.assert_allclose(mix.query_reps[0], q[mix.query_labels == 0].mean(axis=0), rtol=1e-12)
+
+
+def test_random_probes_are_the_smallest_hashes_over_all_tokens():
+    # [T4] random probes: M tokens uniformly without replacement, by brute force over the hashes
+    N, M, seed, head = 150, 9, 5, 3
+    got = O.select_probes_plain(seed, head, N, M, O.PROBES_RANDOM)
+    h = [int(x) for x in O.token_hash(seed, O.STREAM_PROBES, head, np.arange(N))]
+    assert got.tolist() == sorted(i for _, i in sorted(zip(h, range(N)))[:M])
+
+
+def test_uniform_probes_take_one_token_per_equal_bin():
+    # [T4] uniform spatiotemporal probes: evenly spaced in the raster order. Bins at least two
+    # tokens wide each hold exactly one probe; gaps differ by at most one token; the set is
+    # mirror-symmetric about the middle of the sequence (centres c and N - c).
+    for N, M in [(100, 7), (96, 12), (5, 5), (1000, 1), (37, 36), (75600, 2268)]:
+        got = O.select_probes_plain(0, 0, N, M, O.PROBES_UNIFORM)
+        assert len(got) == M and np.all(np.diff(got) > 0) and got[0] >= 0 and got[-1] < N
+        if N >= 2 * M:
+            for b, t in enumerate(got.tolist()):
+                assert b * N <= t * M < (b + 1) * N
+        gaps = np.diff(got)
+        if M > 1:
+            assert gaps.max() - gaps.min() <= 1 and gaps.min() >= N // M - 1
+        assert set((got + got[::-1]).tolist()) <= {N - 1, N}
+    assert O.select_probes_plain(0, 0, 96, 12, O.PROBES_UNIFORM).tolist() == list(range(4, 96, 8))
+
+
+def test_plain_selectors_weigh_every_probe_one():
+    rng = np.random.default_rng(42)
+    N, d = 96, 8
+    q, k, v = (rng.standard_normal((N, d)) for _ in range(3))
+    for sel in (O.PROBES_RANDOM, O.PROBES_UNIFORM):
+        p = dict(_tiny_cfg(N, d), probe_selector=sel)
+        r = O.sparsepr_head(q, k, v, p, head=0)
+        assert np.array_equal(r.plan.probes, O.select_probes_plain(p["seed"], 0, N, p["n_probes"], sel))
+        assert np.all(r.plan.weights == 1.0)
+        assert np.array_equal(r.out[r.plan.probes], O.dense_attention(q, k, v, p["scale"])[r.plan.probes])
+
+
+def test_mean_only_correction_is_the_infinite_lambda_ridge():
+    # [T4] mean-only: unprobed rows shift by the weighted mean probe residual, which is the
+    # lam -> inf limit of the ridge with an unpenalised bias
+    rng = np.random.default_rng(43)
+    N, d = 96, 8
+    q, k, v = (rng.standard_normal((N, d)) for _ in range(3))
+    p = _tiny_cfg(N, d)
+    mo = O.sparsepr_head(q, k, v, dict(p, correction=O.CORRECTION_MEAN_ONLY), head=2)
+    big = O.sparsepr_head(q, k, v, dict(p, ridge_lambda=1e12), head=2)
+    np.testing.assert_allclose(mo.out, big.out, rtol=0, atol=1e-9)
+    pr, w = mo.plan.probes, mo.plan.weights
+    resid = O.dense_attention(q, k, v, p["scale"])[pr] - mo.o_sparse[pr]
+    assert np.abs((w[:, None] * (resid - mo.theta[-1])).sum(axis=0)).max() < 1e-12
+    assert np.all(mo.theta[:-1] == 0.0)
+
+
+def test_disabled_correction_keeps_the_sparse_output():
+    rng = np.random.default_rng(44)
+    N, d = 96, 8
+    q, k, v = (rng.standard_normal((N, d)) for _ in range(3))
+    p = dict(_tiny_cfg(N, d), correction=O.CORRECTION_NONE)
+    r = O.sparsepr_head(q, k, v, p, head=1)
+    un = np.setdiff1d(np.arange(N), r.plan.probes)
+    assert np.array_equal(r.out[un], r.o_sparse[un])
+    assert np.array_equal(r.out[r.plan.probes], O.dense_attention(q, k, v, p["scale"])[r.plan.probes])
