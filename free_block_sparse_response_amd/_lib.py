@@ -53,6 +53,7 @@ _SIGS = {
     "sparsepr_workspace_bytes": (_SZ, [_P]),
     "sparsepr_plan": (ctypes.c_int, [_P, _P, _P, _P, _SZ, _P]),
     "sparsepr_plan_warm": (ctypes.c_int, [_P, _P, _P, _P, _SZ, _P]),
+    "sparsepr_plan_set_probes": (ctypes.c_int, [_P, _P, _P, _P, _SZ, _P]),
     "sparsepr_plan_from_labels": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _P, _SZ, _P]),
     "sparsepr_attend": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _P, _P]),
     "sparsepr_fit_residual": (ctypes.c_int, [_P, _P, _P, _P, _P, _P]),
@@ -156,6 +157,12 @@ def sparsepr_plan_warm(plan, q, k, workspace, stream=None):
     _check("sparsepr_plan_warm", lib().sparsepr_plan_warm(plan, _ptr(q), _ptr(k), _ptr(workspace),
                                                           workspace.numel() * workspace.element_size(),
                                                           _stream(stream)))
+
+
+def sparsepr_plan_set_probes(plan, probes, weights, workspace, stream=None):
+    _check("sparsepr_plan_set_probes", lib().sparsepr_plan_set_probes(plan, _ptr(probes), _ptr(weights), _ptr(workspace),
+                                                                      workspace.numel() * workspace.element_size(),
+                                                                      _stream(stream)))
 
 
 def sparsepr_plan_from_labels(plan, q, k, key_labels, query_labels, group_mass, workspace, stream=None):

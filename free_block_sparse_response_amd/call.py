@@ -60,6 +60,10 @@ class SparsePR:
         else:
             L.sparsepr_plan_from_labels(self.plan_h, q, k, key_labels, query_labels, group_mass, self.ws)
 
+    def set_probes(self, probes, weights=None):
+        """Replace the current plan's probe rows ([B*H, M] int32 device; unit weights if None)."""
+        L.sparsepr_plan_set_probes(self.plan_h, probes, weights, self.ws)
+
     def attend(self, q, k, v):
         m = self.M > 0
         L.sparsepr_attend(self.plan_h, q, k, v, self.o_sparse, self.o_probe_sparse if m else None,

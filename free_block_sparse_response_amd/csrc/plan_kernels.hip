@@ -221,6 +221,26 @@ __global__ __launch_bounds__(1024) void k_select_probes_plain(Dims D, Bufs B) {
   }
 }
 
+// Probe rows given by the caller (validated on the host: in range and distinct per head):
+// weights given or 1, slots rebuilt.
+__global__ __launch_bounds__(256) void k_set_probes(Dims D, Bufs B, const int* probes, const float* weights) {
+  const int bh = blockIdx.x;
+  int* slot = B.pslot + (size_t)bh * D.N;
+  for (int i = threadIdx.x; i < D.N; i += 256) slot[i] = -1;
+  __syncthreads();
+  for (int r = threadIdx.x; r < D.M; r += 256) {
+    const size_t o = (size_t)bh * D.M + r;
+    const int t = probes[o];
+    B.probes[o] = t;
+    B.pweights[o] = weights ? weights[o] : 1.f;
+    slot[t] = r;
+  }
+}
+
+void launch_set_probes(const Dims& D, const Bufs& B, const int* probes, const float* weights, hipStream_t s) {
+  hipLaunchKernelGGL(k_set_probes, dim3(D.BH), dim3(256), 0, s, D, B, probes, weights);
+}
+
 // Identity Lloyd metric: semantic partitions cluster the raw vectors (paper Table 2).
 template <int DD>
 __global__ void k_identity_metric(Dims D, Bufs B) {

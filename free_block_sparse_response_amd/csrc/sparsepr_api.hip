@@ -356,6 +356,50 @@ sparsepr_status sparsepr_plan_from_labels(sparsepr_plan_t p, const void* q, cons
   return st;
 }
 
+sparsepr_status sparsepr_plan_set_probes(sparsepr_plan_t p, const int32_t* probes, const float* weights, void* ws,
+                                        size_t bytes, void* stream) {
+  if (!p || !probes) return SPARSEPR_ERR_INVALID_ARG;
+  if (!p->planned || p->ws != ws) return SPARSEPR_ERR_STATE;
+  sparsepr_status st = check_ws(p, ws, bytes);
+  if (st != SPARSEPR_OK) return st;
+  const Dims& D = p->D;
+  if (D.M == 0) return SPARSEPR_OK;
+  hipStream_t s = (hipStream_t)stream;
+  // host-side validation: every head's M rows in [0, N) and distinct
+  const size_t n = (size_t)D.BH * D.M;
+  int32_t* h = (int32_t*)malloc(n * sizeof(int32_t));
+  unsigned char* seen = (unsigned char*)malloc((size_t)D.N);
+  if (!h || !seen) {
+    free(h);
+    free(seen);
+    return SPARSEPR_ERR_INVALID_ARG;
+  }
+  bool ok = hipMemcpyAsync(h, probes, n * sizeof(int32_t), hipMemcpyDeviceToHost, s) == hipSuccess &&
+            hipStreamSynchronize(s) == hipSuccess;
+  if (!ok) {
+    free(h);
+    free(seen);
+    return SPARSEPR_ERR_HIP;
+  }
+  for (int bh = 0; bh < D.BH && ok; ++bh) {
+    memset(seen, 0, (size_t)D.N);
+    for (int r = 0; r < D.M && ok; ++r) {
+      const int32_t t = h[(size_t)bh * D.M + r];
+      ok = t >= 0 && t < D.N && !seen[t];
+      if (ok) seen[t] = 1;
+    }
+  }
+  free(h);
+  free(seen);
+  if (!ok) return SPARSEPR_ERR_INVALID_ARG;
+  Bufs B = carve(D, ws, nullptr);
+  {
+    StageTimer t(p, SPARSEPR_STAGE_PLAN, s);
+    spr::launch_set_probes(D, B, probes, weights, s);
+  }
+  return hip_status();
+}
+
 sparsepr_status sparsepr_attend(sparsepr_plan_t p, const void* q, const void* k, const void* v, void* o_sparse,
                                 float* o_probe_sparse, float* o_probe_dense, void* stream) {
   if (!p || !q || !k || !v || !o_sparse) return SPARSEPR_ERR_INVALID_ARG;

@@ -170,6 +170,15 @@ sparsepr_status sparsepr_plan_from_labels(sparsepr_plan_t plan, const void* q, c
 sparsepr_status sparsepr_attend(sparsepr_plan_t plan, const void* q, const void* k, const void* v,
                                 void* o_sparse, float* o_probe_sparse, float* o_probe_dense, void* stream);
 
+/* Probe rows chosen by the caller, replacing those of the current plan (paper Table 2: the
+ * repair comparisons hold the probe indices fixed across partitions). probes [B*H, M] int32
+ * device, any order, each head's rows in [0, N) and distinct; weights [B*H, M] float device
+ * or NULL for unit weights. The rows are copied to the host and checked (the call
+ * synchronises the stream): ERR_INVALID_ARG if out of range or repeated, ERR_STATE if no
+ * plan is current in this workspace. A later plan call selects probes again. */
+sparsepr_status sparsepr_plan_set_probes(sparsepr_plan_t plan, const int32_t* probes, const float* weights,
+                                         void* workspace, size_t workspace_bytes, void* stream);
+
 /* Stage 04 fit (paper abstract; website PFRR panel): coeffs [B,H,d+1,d] float receives
  * Theta = (Z^T W Z + Lambda)^-1 Z^T W R with Z = [o_probe_sparse, 1],
  * R = o_probe_dense - o_probe_sparse, W = diag(weights), Lambda = diag(lambda 1_d, 0)

@@ -94,6 +94,8 @@ def test_workspace_size_and_host_side_errors(lib):
         # later stages before a plan; a warm start needs a previous plan in the same workspace
         assert lib.sparsepr_plan_warm(h, fake, fake, fake, ws, None) == L.SPARSEPR_ERR_STATE
         assert lib.sparsepr_plan_warm(h, None, fake, fake, ws, None) == L.SPARSEPR_ERR_INVALID_ARG
+        assert lib.sparsepr_plan_set_probes(h, fake, None, fake, ws, None) == L.SPARSEPR_ERR_STATE
+        assert lib.sparsepr_plan_set_probes(h, None, None, fake, ws, None) == L.SPARSEPR_ERR_INVALID_ARG
         assert lib.sparsepr_attend(h, fake, fake, fake, fake, fake, fake, None) == L.SPARSEPR_ERR_STATE
         assert lib.sparsepr_attend(h, fake, fake, fake, fake, fake, None, None) == L.SPARSEPR_ERR_INVALID_ARG
         assert lib.sparsepr_attend(h, fake, fake, fake, fake, None, fake, None) == L.SPARSEPR_ERR_INVALID_ARG

@@ -8,6 +8,7 @@ import numpy as np
 import pytest
 import torch
 
+from free_block_sparse_response_amd import _lib as L
 from free_block_sparse_response_amd import configs
 from oracle import sparsepr_oracle as O
 
@@ -136,3 +137,40 @@ def test_corrections_from_labels(name, correction):
             un = torch.ones(out.shape[1], dtype=torch.bool, device=out.device)
             un[torch.from_numpy(r.plan.probes).to(out.device)] = False
             assert torch.equal(out[i][un], osp[i][un].to(out.dtype))
+
+
+def test_caller_probes_from_labels():
+    # probe rows given by the caller (any order, unit weights): the oracle's plan with the
+    # same injected rows; out-of-range and repeated rows are refused before any launch
+    w = configs.CONFIGS["c2"]
+    heads = [0, 6]
+    say(f"case: caller probes, c2 heads {heads}")
+    (tq, q64), (tk, k64), (tv, v64) = inputs(w, heads)
+    plans = oracle_heads(w, q64, k64, v64, heads, labels_only=True)
+    N, M = configs.seq_len(w), w["n_probes"]
+    rng = np.random.default_rng(9)
+    inj = [rng.choice(N, M, replace=False) for _ in heads]
+    p = O.call_params(w)
+    refs = []
+    for i, hp in enumerate(plans):
+        hp2 = O.finish_plan(q64[i], k64[i], p, i, hp, u=hp.u, probes=inj[i])
+        refs.append(O.attend_fit_apply(q64[i], k64[i], v64[i], p, hp2))
+    sp = gpu_from_labels(w, tq, tk, tv, plans)
+    bad = torch.from_numpy(np.stack(inj).astype(np.int32)).to(DEV)
+    bad[1, 3] = bad[1, 7]
+    with pytest.raises(L.SparsePRError):
+        sp.set_probes(bad)
+    bad[1, 3] = N
+    with pytest.raises(L.SparsePRError):
+        sp.set_probes(bad)
+    sp.set_probes(torch.from_numpy(np.stack(inj).astype(np.int32)).to(DEV))
+    sp.attend(tq, tk, tv)
+    sp.fit_residual()
+    sp.apply()
+    torch.cuda.synchronize()
+    assert np.array_equal(np_(sp.export("PROBES")), np.stack(inj))
+    out, o_pr = np_(sp.out[0]), np_(sp.o_probe[0])
+    for i, r in enumerate(refs):
+        e_out, e_pr = max_rel(out[i], r.out), max_rel(o_pr[i], r.o_probe_dense)
+        say(f"  head {heads[i]}: out {e_out:.2e} probe dense {e_pr:.2e}")
+        assert e_out <= TOL["bf16"] and e_pr <= TOL["bf16"]
