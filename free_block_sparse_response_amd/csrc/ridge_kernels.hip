@@ -70,160 +70,250 @@ __global__ __launch_bounds__(256) void k_ridge_gram(Dims D, Bufs B, const float*
   }
 }
 
-// Orders the LDS accesses of one wave (its lanes run in lockstep): waits for this wave's
-// outstanding LDS operations and keeps the compiler from moving memory operations across.
-__device__ inline void wave_lds_sync() {
-  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-  __builtin_amdgcn_wave_barrier();
-}
-
-// One block per (head, 32 right-hand-side columns); each block redoes the elimination of A
-// in LDS (lower triangle, packed). A = L1 Dg L1^T (unit lower L1, pivots Dg) is formed by
-// Gaussian elimination without pivoting -- the Cholesky factorisation up to the scaling
-// sqrt(Dg), stable for symmetric positive definite A -- with the same row operations on
-// the right-hand side, Z = L1^-1 B, then L1^T X = Dg^-1 Z. Blocked by 8-column panels: one
-// wave factors a panel (its columns in order, lockstep, no block barrier), then all threads
-// apply the panel's rank-8 update to the trailing matrix and right-hand side; the back
-// substitution is blocked the same way. A pivot at or below 1e-12 x max diag(A) (the
-// squared Cholesky diagonal) fails the head.
+// One block of 512 threads per (head, 32 right-hand-side columns); each block redoes the
+// elimination of A. A = L1 Dg L1^T (unit lower L1, pivots Dg) by Gaussian elimination
+// without pivoting -- the Cholesky factorisation up to the scaling sqrt(Dg), stable for
+// symmetric positive definite A -- with the same row operations on the right-hand side,
+// Z = L1^-1 B, then L1^T X = Dg^-1 Z.
+//
+// The system lives in registers: thread (ty, tx) of a 16 x 32 grid holds A(i, k) for
+// i = ty + 16 r, k = tx + 32 q and B(i, c0 + tx). Elimination goes by panels of 3 columns:
+// the panel's owners publish its columns and right-hand-side rows in LDS (double-buffered,
+// so one barrier per panel), every thread factors the 3 x 3 diagonal block itself
+// (identical arithmetic everywhere, so a failed pivot stops all threads together), forms
+// the multipliers of its own rows and applies the rank-3 update to its elements. The back
+// substitution runs panel by panel from the last, publishing panel rows of L1 and of the
+// right-hand side the same way. A pivot at or below 1e-12 x max diag(A) (the squared
+// Cholesky diagonal) fails the head.
 template <int DD>
-__global__ __launch_bounds__(256) void k_ridge_solve(Dims D, Bufs B, float* coeffs) {
+__global__ __launch_bounds__(512) void k_ridge_solve(Dims D, Bufs B, float* coeffs) {
   constexpr int n = DD + 1;
   constexpr int W = n + DD;
-  constexpr int NP = n * (n + 1) / 2;
-  constexpr int CB = 32;
-  constexpr int PB = 8;
-  __shared__ double Lp[NP];
-  __shared__ double Bs[n][CB];
-  __shared__ double pan[n][PB];   // multipliers L1(i, j0 + jj) of the current panel
-  __shared__ double panU[n][PB];  // the same column entries before scaling (A(i, j0 + jj))
-  __shared__ double piv_s[n];
+  constexpr int CB = 32;  // right-hand-side columns per block
+  constexpr int TY = 16, TX = 32;
+  constexpr int RT = (n + TY - 1) / TY;  // rows per thread
+  constexpr int QT = (n + TX - 1) / TX;  // matrix columns per thread
+  constexpr int NP = RT * TY > QT * TX ? RT * TY : QT * TX;  // padded index range
+  constexpr int P = 3;                   // panel width (n = 129 = 43 panels)
+  __shared__ double cb[2][P][NP];        // panel columns / panel rows of L1
+  __shared__ double rb[2][P][CB];        // panel rows of the right-hand side
+  __shared__ double piv[NP];
   __shared__ double s_floor;
-  __shared__ int s_fail;
-  const int cb = blockIdx.x, bh = blockIdx.y, tid = threadIdx.x;
-  const int ty = tid / 16, tx = tid % 16, lane = tid & 63;
-  const bool wave0 = tid < 64;
-  const int c0 = cb * CB;
+  const int bh = blockIdx.y, c0 = blockIdx.x * CB;
+  const int tid = threadIdx.x, ty = tid / TX, tx = tid % TX;
   float* Th = coeffs + (size_t)bh * n * DD;
-  auto write_zero = [&]() {
-    for (int e = tid; e < n * CB; e += 256) {
-      const int i = e / CB, c = e % CB;
-      if (c0 + c < DD) Th[(size_t)i * DD + c0 + c] = 0.f;
-    }
-  };
+  const bool col_ok = c0 + tx < DD;
   if (D.M == 0) {
-    write_zero();
+#pragma unroll
+    for (int r = 0; r < RT; ++r) {
+      const int i = ty + TY * r;
+      if (i < n && col_ok) Th[(size_t)i * DD + c0 + tx] = 0.f;
+    }
     return;
   }
   const double* G = B.gram + (size_t)bh * n * W;
-  auto pk = [](int i, int k) { return i * (i + 1) / 2 + k; };
-  for (int i = ty; i < n; i += 16)
-    for (int k = tx; k <= i; k += 16) Lp[pk(i, k)] = G[(size_t)i * W + k];
-  for (int e = tid; e < n * CB; e += 256) {
-    const int i = e / CB, c = e % CB;
-    Bs[i][c] = (c0 + c < DD) ? G[(size_t)i * W + n + c0 + c] : 0.0;
+  double a[RT][QT], b[RT];
+#pragma unroll
+  for (int r = 0; r < RT; ++r) {
+    const int i = ty + TY * r;
+#pragma unroll
+    for (int q = 0; q < QT; ++q) {
+      const int k = tx + TX * q;
+      a[r][q] = (i < n && k < n) ? G[(size_t)i * W + k] : 0.0;
+    }
+    b[r] = (i < n && col_ok) ? G[(size_t)i * W + n + c0 + tx] : 0.0;
   }
-  if (tid == 0) {
+  // entries never published stay zero (indices beyond n)
+  for (int e = tid; e < 2 * P * NP; e += 512) (&cb[0][0][0])[e] = 0.0;
+  for (int e = tid; e < 2 * P * CB; e += 512) (&rb[0][0][0])[e] = 0.0;
+  if (tid < 64) {
     double mx = 0.0;
-    for (int i = 0; i < n; ++i) mx = fmax(mx, G[(size_t)i * W + i]);
-    s_floor = kPivotRtol * mx;
-    s_fail = 0;
+    for (int i = tid; i < n; i += 64) mx = fmax(mx, G[(size_t)i * W + i]);
+    for (int o = 32; o > 0; o >>= 1) mx = fmax(mx, __shfl_xor(mx, o, 64));
+    if (tid == 0) s_floor = kPivotRtol * mx;
   }
   __syncthreads();
-  for (int j0 = 0; j0 < n; j0 += PB) {
-    const int w = min(PB, n - j0), je = j0 + w;
-    if (wave0) {
-      // ---- panel factorisation by one wave: columns j0 .. je-1 in order
-      for (int jj = j0; jj < je; ++jj) {
-        wave_lds_sync();
-        const double piv = Lp[pk(jj, jj)];
-        if (!(piv > s_floor)) {
-          if (lane == 0) s_fail = 1;
-          break;
-        }
-        if (lane == 0) piv_s[jj] = piv;
-        const double ipiv = 1.0 / piv;
-        for (int i = jj + 1 + lane; i < n; i += 64) {
-          const double u = Lp[pk(i, jj)];
-          const double lv = u * ipiv;
-          panU[i][jj - j0] = u;
-          pan[i][jj - j0] = lv;
-          Lp[pk(i, jj)] = lv;
-        }
-        wave_lds_sync();
-        // panel-local update: rows i > jj, panel columns k in (jj, min(i, je - 1)]
-        for (int i = jj + 1 + lane; i < n; i += 64) {
-          const double lv = pan[i][jj - j0];
-          const int kmax = min(i, je - 1);
-          for (int k = jj + 1; k <= kmax; ++k) Lp[pk(i, k)] -= lv * panU[k][jj - j0];
-        }
-        // right-hand side rows inside the panel
-        for (int e = lane; e < (je - jj - 1) * CB; e += 64) {
-          const int i = jj + 1 + e / CB, c = e % CB;
-          Bs[i][c] -= pan[i][jj - j0] * Bs[jj][c];
+  const double floor_ = s_floor;
+  bool fail = false;
+  int buf = 0;
+  for (int j0 = 0; j0 < n; j0 += P, buf ^= 1) {
+    const int pw = min(P, n - j0);
+    // owners publish the panel columns (rows >= j0) and the panel rows of the right-hand side
+#pragma unroll
+    for (int q = 0; q < QT; ++q) {
+      const int pc = tx + TX * q - j0;
+      if (pc >= 0 && pc < pw) {
+#pragma unroll
+        for (int r = 0; r < RT; ++r) {
+          const int i = ty + TY * r;
+          if (i >= j0 && i < n) cb[buf][pc][i] = a[r][q];
         }
       }
     }
-    __syncthreads();
-    if (s_fail) break;
-    // ---- rank-w update of the trailing rows i >= je (matrix and right-hand side)
-    for (int i = je + ty; i < n; i += 16) {
-      double li[PB];
 #pragma unroll
-      for (int q = 0; q < PB; ++q) li[q] = q < w ? pan[i][q] : 0.0;
-      for (int k = je + tx; k <= i; k += 16) {
-        double acc = Lp[pk(i, k)];
-#pragma unroll
-        for (int q = 0; q < PB; ++q) acc -= li[q] * panU[k][q];
-        Lp[pk(i, k)] = acc;
-      }
-      for (int c = tx; c < CB; c += 16) {
-        double acc = Bs[i][c];
-#pragma unroll
-        for (int q = 0; q < PB; ++q)
-          if (q < w) acc -= li[q] * Bs[j0 + q][c];
-        Bs[i][c] = acc;
-      }
+    for (int r = 0; r < RT; ++r) {
+      const int pr = ty + TY * r - j0;
+      if (pr >= 0 && pr < pw) rb[buf][pr][tx] = b[r];
     }
     __syncthreads();
+    // the diagonal block, factored by every thread alike: Lb unit lower, db pivots; entries
+    // beyond the panel width are zero (their reciprocal pivots too)
+    double Lb[P][P], db[P], rd[P];
+#pragma unroll
+    for (int p1 = 0; p1 < P; ++p1) {
+      const bool in1 = p1 < pw;
+#pragma unroll
+      for (int p2 = 0; p2 < p1; ++p2) {
+        double v = cb[buf][p2][j0 + p1];
+#pragma unroll
+        for (int m = 0; m < p2; ++m) v -= Lb[p1][m] * Lb[p2][m] * db[m];
+        Lb[p1][p2] = in1 ? v * rd[p2] : 0.0;
+      }
+      double d = cb[buf][p1][j0 + p1];
+#pragma unroll
+      for (int m = 0; m < p1; ++m) d -= Lb[p1][m] * Lb[p1][m] * db[m];
+      db[p1] = in1 ? d : 1.0;
+      rd[p1] = in1 ? 1.0 / d : 0.0;
+      fail |= in1 && !(d > floor_);
+    }
+    if (fail) break;
+    if (tid == 0) {
+#pragma unroll
+      for (int p = 0; p < P; ++p)
+        if (p < pw) piv[j0 + p] = db[p];
+    }
+    // the panel entries of my columns, solved (y Lb^T = c); zero unless a trailing column
+    double yq[QT][P];
+#pragma unroll
+    for (int q = 0; q < QT; ++q) {
+      const int k = tx + TX * q;
+      const bool tk = k >= j0 + pw && k < n;
+      double y[P];
+#pragma unroll
+      for (int p = 0; p < P; ++p) {
+        double v = cb[buf][p][k];
+#pragma unroll
+        for (int m = 0; m < p; ++m) v -= y[m] * Lb[p][m];
+        y[p] = v;
+        yq[q][p] = (tk && p < pw) ? v : 0.0;
+      }
+    }
+    // right-hand side of the panel: z = Lb^-1 b_J
+    double z[P];
+#pragma unroll
+    for (int p = 0; p < P; ++p) {
+      double v = rb[buf][p][tx];
+#pragma unroll
+      for (int m = 0; m < p; ++m) v -= Lb[p][m] * z[m];
+      z[p] = p < pw ? v : 0.0;
+    }
+    // row by row: the multipliers of my row (below the diagonal of a panel column they are
+    // L1's entries, for the panel's own rows too), the rank-pw update of a trailing row and
+    // its right-hand side; the panel rows of the right-hand side take z
+#pragma unroll
+    for (int r = 0; r < RT; ++r) {
+      const int i = ty + TY * r;
+      const bool tr = i >= j0 + pw && i < n;
+      double lf[P], li[P];
+#pragma unroll
+      for (int p = 0; p < P; ++p) {
+        double v = cb[buf][p][i];
+#pragma unroll
+        for (int m = 0; m < p; ++m) v -= lf[m] * db[m] * Lb[p][m];
+        lf[p] = v * rd[p];
+        li[p] = tr ? lf[p] : 0.0;
+      }
+#pragma unroll
+      for (int q = 0; q < QT; ++q) {
+        double v = a[r][q];
+#pragma unroll
+        for (int p = 0; p < P; ++p) v -= li[p] * yq[q][p];
+        const int k = tx + TX * q, pc = k - j0;
+        if (pc >= 0 && pc < pw && i > k && i < n) {
+          double m = lf[0];
+#pragma unroll
+          for (int u = 1; u < P; ++u) m = pc == u ? lf[u] : m;
+          v = m;
+        }
+        a[r][q] = v;
+      }
+      double v = b[r];
+#pragma unroll
+      for (int p = 0; p < P; ++p) v -= li[p] * z[p];
+      const int pr = i - j0;
+      if (pr >= 0 && pr < pw) {
+        double m = z[0];
+#pragma unroll
+        for (int u = 1; u < P; ++u) m = pr == u ? z[u] : m;
+        v = m;
+      }
+      b[r] = v;
+    }
   }
-  if (s_fail) {
-    write_zero();
+  if (fail) {
+#pragma unroll
+    for (int r = 0; r < RT; ++r) {
+      const int i = ty + TY * r;
+      if (i < n && col_ok) Th[(size_t)i * DD + c0 + tx] = 0.f;
+    }
     if (tid == 0) B.status[bh] = 5;  // SPARSEPR_ERR_NUMERICAL
     return;
   }
-  for (int e = tid; e < n * CB; e += 256) {
-    const int i = e / CB, c = e % CB;
-    Bs[i][c] /= piv_s[i];
-  }
   __syncthreads();
-  // ---- L1^T X = Dg^-1 Z, panels from the last: one wave solves inside the panel, then all
-  //      threads remove the panel's unknowns from the rows above it
-  const int np = (n + PB - 1) / PB;
-  for (int p = np - 1; p >= 0; --p) {
-    const int j0 = p * PB, je = min(n, j0 + PB);
-    if (wave0) {
-      for (int jj = je - 1; jj > j0; --jj) {
-        wave_lds_sync();
-        for (int e = lane; e < (jj - j0) * CB; e += 64) {
-          const int k = j0 + e / CB, c = e % CB;
-          Bs[k][c] -= Lp[pk(jj, k)] * Bs[jj][c];
+#pragma unroll
+  for (int r = 0; r < RT; ++r) {
+    const int i = ty + TY * r;
+    if (i < n) b[r] /= piv[i];
+  }
+  // ---- L1^T X = Dg^-1 Z, panels from the last
+  for (int j0 = ((n - 1) / P) * P; j0 >= 0; j0 -= P, buf ^= 1) {
+    const int pw = min(P, n - j0);
+    // owners publish the panel rows: right-hand side, and L1 left of the diagonal
+#pragma unroll
+    for (int r = 0; r < RT; ++r) {
+      const int i = ty + TY * r;
+      const int pr = i - j0;
+      if (pr >= 0 && pr < pw) {
+        rb[buf][pr][tx] = b[r];
+#pragma unroll
+        for (int q = 0; q < QT; ++q) {
+          const int k = tx + TX * q;
+          if (k < i) cb[buf][pr][k] = a[r][q];
         }
       }
     }
     __syncthreads();
-    for (int k = ty; k < j0; k += 16) {
-      for (int c = tx; c < CB; c += 16) {
-        double acc = Bs[k][c];
-        for (int jj = j0; jj < je; ++jj) acc -= Lp[pk(jj, k)] * Bs[jj][c];
-        Bs[k][c] = acc;
-      }
+    // Lb^T x = z inside the panel, for my column
+    double x[P];
+#pragma unroll
+    for (int p = P - 1; p >= 0; --p) {
+      double v = rb[buf][p][tx];
+#pragma unroll
+      for (int m = p + 1; m < P; ++m) v -= cb[buf][m][j0 + p] * x[m];
+      x[p] = p < pw ? v : 0.0;
     }
-    __syncthreads();
+#pragma unroll
+    for (int r = 0; r < RT; ++r) {
+      const int i = ty + TY * r;
+      double v = b[r];
+      if (i < j0) {
+#pragma unroll
+        for (int p = 0; p < P; ++p) v -= cb[buf][p][i] * x[p];
+      }
+      const int pr = i - j0;
+      if (pr >= 0 && pr < pw) {
+        double m = x[0];
+#pragma unroll
+        for (int u = 1; u < P; ++u) m = pr == u ? x[u] : m;
+        v = m;
+      }
+      b[r] = v;
+    }
   }
-  for (int e = tid; e < n * CB; e += 256) {
-    const int i = e / CB, c = e % CB;
-    if (c0 + c < DD) Th[(size_t)i * DD + c0 + c] = (float)Bs[i][c];
+#pragma unroll
+  for (int r = 0; r < RT; ++r) {
+    const int i = ty + TY * r;
+    if (i < n && col_ok) Th[(size_t)i * DD + c0 + tx] = (float)b[r];
   }
 }
 
@@ -394,7 +484,7 @@ static void fit_impl(const Dims& D, const Bufs& B, const float* o_psp, const flo
     dim3 g((n + 31) / 32, (n + DD + 31) / 32, D.BH);
     hipLaunchKernelGGL((k_ridge_gram<DD>), g, dim3(256), 0, s, D, B, o_psp, o_dn, w);
   }
-  hipLaunchKernelGGL((k_ridge_solve<DD>), dim3((DD + 31) / 32, D.BH), dim3(256), 0, s, D, B, coeffs);
+  hipLaunchKernelGGL((k_ridge_solve<DD>), dim3((DD + 31) / 32, D.BH), dim3(512), 0, s, D, B, coeffs);
 }
 
 template <typename T, int DD>
