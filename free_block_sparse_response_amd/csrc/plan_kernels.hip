@@ -624,19 +624,19 @@ __device__ void group_mean(const T* xb, const float* alpha, const int* members, 
     for (int e = 0; e < EV; ++e) acc[e] = fmaf(a, to_f32(v[e]), acc[e]);
   };
   int r = slot;
-  for (; r + 3 * RS < n; r += 4 * RS) {
-    int rows[4];
-    uint4 raw[4];
-    float al[4];
+  for (; r + 7 * RS < n; r += 8 * RS) {
+    int rows[8];
+    uint4 raw[8];
+    float al[8];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) rows[u] = members[r + u * RS];
+    for (int u = 0; u < 8; ++u) rows[u] = members[r + u * RS];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
+    for (int u = 0; u < 8; ++u) {
       raw[u] = *reinterpret_cast<const uint4*>(xb + (size_t)rows[u] * DD + c0);
       al[u] = alpha ? alpha[rows[u]] : 1.f;
     }
 #pragma unroll
-    for (int u = 0; u < 4; ++u) add_row(raw[u], al[u]);
+    for (int u = 0; u < 8; ++u) add_row(raw[u], al[u]);
   }
   for (; r < n; r += RS) {
     const int row = members[r];
@@ -665,16 +665,17 @@ __device__ void km_update_item(const T* x, const Dims& D, const Bufs& B, KmState
   const int s0 = B.gstart[(size_t)bh * (D.C + 1) + b];
   const T* xb = x + (size_t)bh * D.N * DD;
   const float* alpha = B.alpha ? B.alpha + (size_t)bh * D.N : nullptr;
-  group_mean<T, DD>(xb, alpha, perm + (size_t)bh * D.N + s0, n, m, sh);
+  // G m: threads i and i + DD (, ...) take interleaved parts of k; combined in order. The
+  // metric's loads are issued before the gather so that the two latencies overlap.
   const float* G = B.metric + (size_t)bh * DD * DD;
+  constexpr int KH = 256 / DD;
+  const int i = threadIdx.x % DD, part = threadIdx.x / DD;
+  float gv[DD / KH];
+#pragma unroll
+  for (int kk = 0; kk < DD / KH; ++kk) gv[kk] = G[(size_t)(part + kk * KH) * DD + i];
+  group_mean<T, DD>(xb, alpha, perm + (size_t)bh * D.N + s0, n, m, sh);
   float p = 0.f;
   {
-    // G m: threads i and i + DD (, ...) take interleaved parts of k; combined in order
-    constexpr int KH = 256 / DD;
-    const int i = threadIdx.x % DD, part = threadIdx.x / DD;
-    float gv[DD / KH];
-#pragma unroll
-    for (int kk = 0; kk < DD / KH; ++kk) gv[kk] = G[(size_t)(part + kk * KH) * DD + i];
     float tt = 0.f;
 #pragma unroll
     for (int kk = 0; kk < DD / KH; ++kk) tt = fmaf(gv[kk], m[part + kk * KH], tt);
@@ -877,33 +878,6 @@ __device__ inline f32x16 mfma_rows(const bf16* Yh, const bf16* Yl, int y0, const
 
 __device__ inline int acc_row(int v) { return 8 * (v >> 2) + 4 * (lane_id() >> 5) + (v & 3); }
 
-// Stable in-block rank and histogram of the labels of one 128-row counting-sort block
-// (labels in lab_s[0..127]); run by threads 0..127, rows 0..63 in wave 0 and 64..127 in 1.
-__device__ inline void km_rank_block(const Dims& D, const Bufs& B, int C, int bh, int blk, const int* lab_s,
-                                     int* hist) {
-  const int tid = threadIdx.x, w = tid / kWave;
-  const int r0 = blk * kKmRows;
-  for (int i = tid; i < C; i += blockDim.x) hist[i] = 0;
-  __syncthreads();
-  const bool rvalid = tid < kKmRows && r0 + tid < D.N;
-  const int lab = tid < kKmRows ? lab_s[tid] : 0;
-  uint64_t mask = 0;
-  if (w < 2) mask = wave_match(lab, rvalid, 10);
-  const int rin = __popcll(mask & lanemask_lt());
-  const bool leader = rvalid && rin == 0;
-  if (w == 0 && leader) hist[lab] = __popcll(mask);
-  __syncthreads();
-  int rank = rin;
-  if (w == 1 && rvalid) rank += hist[lab];
-  __syncthreads();
-  if (w == 1 && leader) hist[lab] += __popcll(mask);
-  if (rvalid) B.rank[(size_t)bh * D.N + r0 + tid] = rank;
-  __syncthreads();
-  int* tab = B.tab + (size_t)bh * D.C * D.nblk;
-  for (int i = tid; i < C; i += blockDim.x) tab[(size_t)i * D.nblk + blk] = hist[i];
-  __syncthreads();
-}
-
 // Assignment of iteration t for 128*RS rows: each of the 4 waves owns RS sets of 32 rows, so
 // every centroid operand read from LDS feeds RS products. Centroid operands (G m_b in
 // bf16, plus its bf16 remainder when LO) are double-buffered in LDS 64 centroids at a time:
@@ -913,11 +887,13 @@ __global__ __launch_bounds__(256, 2) void k_km_assign_bf16(const bf16* x, Dims D
   constexpr int CB = 64, KS = DD + 8, NB = kKmRows * RS;
   constexpr int NL = CB * DD / 8 / 256;  // 16-byte loads per thread per chunk and operand
   constexpr int NO = LO ? 2 : 1;
-  __shared__ __attribute__((aligned(16))) bf16 Y[2][NO][CB * KS];
+  // the centroid operands; after the last chunk the same bytes hold the per-wave label counts
+  constexpr size_t YB = sizeof(bf16) * 2 * NO * CB * KS, CNB = sizeof(int) * RS * 4 * kMaxGroups;
+  __shared__ __attribute__((aligned(16))) char smem[YB > CNB ? YB : CNB];
+  auto Y = reinterpret_cast<bf16(*)[NO][CB * KS]>(smem);
+  auto cnt = reinterpret_cast<int(*)[4][kMaxGroups]>(smem);
   __shared__ float cns[2][CB];
-  __shared__ int lab_s[NB];
-  __shared__ double dred[NB];
-  __shared__ int hist[kMaxGroups];
+  __shared__ double wpart[RS][4];
   const int sb0 = blockIdx.x * RS, bh = blockIdx.y;  // first 128-row sort block
   if (st[bh].done_iter < t) return;
   const int tid = threadIdx.x, w = tid / kWave, l32 = lane_id() & 31, h = lane_id() >> 5;
@@ -1005,29 +981,45 @@ __global__ __launch_bounds__(256, 2) void k_km_assign_bf16(const bf16* x, Dims D
     __syncthreads();
     cur ^= 1;
   }
+  // Tail, one barrier: labels; the inertia partial of each sort block (wave sums, then the
+  // four waves in order); the stable in-block rank = rank among the wave's rows with the same
+  // label + the counts of that label in the earlier waves; the block's label histogram.
+  uint64_t mk[RS];
+  int lab[RS];
 #pragma unroll
   for (int rs = 0; rs < RS; ++rs) {
     bidx[rs] += 4 * h;
     const float ob = __shfl_xor(best[rs], 32, kWave);
     const int oi = __shfl_xor(bidx[rs], 32, kWave);
     if (ob < best[rs] || (ob == best[rs] && oi < bidx[rs])) { best[rs] = ob; bidx[rs] = oi; }
-    const int lrow = 128 * rs + 32 * w + l32, row = r0 + lrow;
-    const bool valid = row < D.N;
-    if (h == 0) {
-      lab_s[lrow] = valid ? bidx[rs] : 0;
-      dred[lrow] = valid ? (double)B.rowconst[(size_t)bh * D.N + row] + (double)best[rs] : 0.0;
-      if (valid) B.lab[(size_t)bh * D.N + row] = bidx[rs];
-    }
+    const int row = r0 + 128 * rs + 32 * w + l32;
+    const bool valid = h == 0 && row < D.N;
+    lab[rs] = valid ? bidx[rs] : 0;
+    if (valid) B.lab[(size_t)bh * D.N + row] = bidx[rs];
+    double v = valid ? (double)B.rowconst[(size_t)bh * D.N + row] + (double)best[rs] : 0.0;
+    v = wave_sum(v);
+    if (lane_id() == 0) wpart[rs][w] = v;
+    mk[rs] = wave_match(lab[rs], valid, 10);
+    // this wave's counts (zeroed, then one leader per label writes; one wave, in order)
+    int* cw = cnt[rs][w];
+    for (int i = lane_id(); i < C; i += kWave) cw[i] = 0;
+    if (valid && __popcll(mk[rs] & lanemask_lt()) == 0) cw[lab[rs]] = __popcll(mk[rs]);
   }
   __syncthreads();
-  for (int sb = 0; sb < RS && sb0 + sb < D.nblk; ++sb) {
-    double* dr = dred + 128 * sb;
-    for (int sz = kKmRows / 2; sz > 0; sz >>= 1) {
-      if (tid < sz) dr[tid] += dr[tid + sz];
-      __syncthreads();
+  int* tab = B.tab + (size_t)bh * D.C * D.nblk;
+#pragma unroll
+  for (int rs = 0; rs < RS; ++rs) {
+    const int sb = sb0 + rs;
+    if (sb >= D.nblk) break;
+    const int row = r0 + 128 * rs + 32 * w + l32;
+    if (h == 0 && row < D.N) {
+      int rank = __popcll(mk[rs] & lanemask_lt());
+      for (int w2 = 0; w2 < w; ++w2) rank += cnt[rs][w2][lab[rs]];
+      B.rank[(size_t)bh * D.N + row] = rank;
     }
-    if (tid == 0) B.ipart[(size_t)bh * D.nblk + sb0 + sb] = dr[0];
-    km_rank_block(D, B, C, bh, sb0 + sb, lab_s + 128 * sb, hist);
+    for (int i = tid; i < C; i += 256)
+      tab[(size_t)i * D.nblk + sb] = cnt[rs][0][i] + cnt[rs][1][i] + cnt[rs][2][i] + cnt[rs][3][i];
+    if (tid == 0) B.ipart[(size_t)bh * D.nblk + sb] = ((wpart[rs][0] + wpart[rs][1]) + wpart[rs][2]) + wpart[rs][3];
   }
 }
 

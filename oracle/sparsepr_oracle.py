@@ -212,6 +212,29 @@ def key_responses(k, q_sampled, scale):
     return scale * (k @ q_sampled.T)
 
 
+def response_basis(q_sampled, rank):
+    """Top-`rank` principal directions of the sampled queries' response space.
+
+    [C.1] gives a key response rank r_K = 48 and nothing more. Reading: a key's response
+    vector s q_S k^T (one entry per sampled query) is represented by its coordinates on
+    the `rank` leading left singular vectors of Q_S (the directions in which the sampled
+    queries respond most), so the key k-means runs on a rank-`rank` image of R_K. Returns
+    the S x rank orthonormal basis, or None when rank is 0 or not below the rank of Q_S
+    (no reduction).
+    """
+    if rank <= 0 or rank >= min(q_sampled.shape):
+        return None
+    U, _, _ = np.linalg.svd(q_sampled, full_matrices=False)
+    return U[:, :rank]
+
+
+def key_features(k, q_sampled, scale, rank=0):
+    """The rows the key k-means clusters: R_K, or R_K on the response basis when reduced."""
+    RK = key_responses(k, q_sampled, scale)
+    A = response_basis(q_sampled, rank)
+    return RK if A is None else RK @ A
+
+
 def query_features(q, key_centroids, scale):
     """Logits L = s Q C_k^T and their per-query RMS-normalised rows F.
 
@@ -536,7 +559,7 @@ def plan_head(q, k, p, head, max_iter, tol):
     mode = p.get("partition", PARTITION_RESPONSE)
     hp = HeadPlan()
     hp.sampled = select_smallest(p["seed"], STREAM_SAMPLED, head, np.arange(N), p["n_sampled"])
-    RK = k if mode == PARTITION_SEMANTIC else key_responses(k, q[hp.sampled], s)
+    RK = k if mode == PARTITION_SEMANTIC else key_features(k, q[hp.sampled], s, p.get("key_rank", 0))
     kinit = select_smallest(p["seed"], STREAM_KEY_INIT, head, np.arange(N), p["n_key_groups"])
     res = lloyd(RK, kinit, max_iter, tol)
     hp.key_iters = res.iterations
@@ -583,7 +606,8 @@ def plan_head_warm(q, k, p, head, prev, max_iter=2, tol=1e-4):
     if mode == PARTITION_SEMANTIC:
         res = lloyd_from(k, prev.key_centroids, max_iter, tol)
     else:
-        res = lloyd_from(key_responses(k, qs, s), key_responses(prev.key_centroids, qs, s), max_iter, tol)
+        r = p.get("key_rank", 0)
+        res = lloyd_from(key_features(k, qs, s, r), key_features(prev.key_centroids, qs, s, r), max_iter, tol)
     hp.key_iters = res.iterations
     hp.key_labels, hp.Ck = compact_labels(res.labels, prev.Ck)
     kc = group_means(k, hp.key_labels, hp.Ck)
@@ -678,7 +702,8 @@ def call_params(cfg):
                 penalize_bias=cfg.get("penalize_bias", False),
                 partition=cfg.get("partition", PARTITION_RESPONSE),
                 correction=cfg.get("correction", CORRECTION_RIDGE),
-                probe_selector=cfg.get("probe_selector", PROBES_STRATIFIED))
+                probe_selector=cfg.get("probe_selector", PROBES_STRATIFIED),
+                key_rank=cfg.get("key_rank", 0))
 
 
 def sparsepr_head(q, k, v, p, head, max_iter=25, tol=1e-4):

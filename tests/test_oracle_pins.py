@@ -731,3 +731,51 @@ def test_disabled_correction_keeps_the_sparse_output():
     un = np.setdiff1d(np.arange(N), r.plan.probes)
     assert np.array_equal(r.out[un], r.o_sparse[un])
     assert np.array_equal(r.out[r.plan.probes], O.dense_attention(q, k, v, p["scale"])[r.plan.probes])
+
+
+# ---------------------------------------------------------------- key response rank ([C.1] r_K)
+def test_reduced_key_features_are_the_rank_r_metric():
+    # distances between reduced key features equal (k_i - k_j) G_r (k_i - k_j)^T, with G_r the
+    # rank-r truncation of G = s^2 Q_S^T Q_S from its own eigendecomposition (eigh, not svd)
+    rng = np.random.default_rng(50)
+    N, d, S, r = 40, 8, 24, 3
+    k, qs = rng.standard_normal((N, d)), rng.standard_normal((S, d)) * np.linspace(3, 0.5, d)
+    s = 0.7
+    Y = O.key_features(k, qs, s, r)
+    assert Y.shape == (N, r)
+    lam, U = np.linalg.eigh(s * s * qs.T @ qs)
+    Gr = (U[:, -r:] * lam[-r:]) @ U[:, -r:].T
+    D = k[:, None, :] - k[None, :, :]
+    want = np.einsum("ija,ab,ijb->ij", D, Gr, D)
+    got = ((Y[:, None, :] - Y[None, :, :]) ** 2).sum(-1)
+    np.testing.assert_allclose(got, want, rtol=1e-9, atol=1e-9)
+
+
+def test_key_rank_at_or_above_d_is_the_full_response():
+    rng = np.random.default_rng(51)
+    N, d = 120, 8
+    q, k = _clustered(rng, N, d, 4), _clustered(rng, N, d, 4)
+    p = _tiny_cfg(N, d)
+    full = O.plan_head(q, k, p, 0, 25, 1e-4)
+    for r in (d, d + 5):
+        same = O.plan_head(q, k, dict(p, key_rank=r), 0, 25, 1e-4)
+        assert np.array_equal(same.key_labels, full.key_labels)
+        assert np.array_equal(same.query_labels, full.query_labels)
+
+
+def test_low_key_rank_drops_weak_response_directions():
+    # key clusters separated only along the direction the sampled queries barely probe: the
+    # full response separates them, a rank that keeps only the strong directions cannot
+    rng = np.random.default_rng(52)
+    N, d, C = 240, 8, 3
+    q = rng.standard_normal((N, d))
+    q[:, -1] *= 0.05                      # the last coordinate is barely probed
+    lab = np.arange(N) % C
+    k = rng.standard_normal((N, d))
+    k[:, -1] = 80.0 * np.array([-1.0, 0.0, 1.0])[lab]
+    p = dict(_tiny_cfg(N, d), n_key_groups=C, n_sampled=64)
+    full_ok = low_ok = 0
+    for head in range(12):
+        full_ok += _planted_same_as(O.plan_head(q, k, p, head, 50, 0.0).key_labels, lab)
+        low_ok += _planted_same_as(O.plan_head(q, k, dict(p, key_rank=d - 1), head, 50, 0.0).key_labels, lab)
+    assert full_ok >= 2 and low_ok == 0
