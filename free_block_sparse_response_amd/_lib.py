@@ -36,7 +36,8 @@ class sparsepr_config(ctypes.Structure):
                 ("kmeans_max_iter", ctypes.c_int32), ("kmeans_tol", ctypes.c_float),
                 ("ridge_lambda", ctypes.c_float), ("penalize_bias", ctypes.c_int32), ("seed", ctypes.c_uint64),
                 ("assign_precision", ctypes.c_int32), ("warm_iters", ctypes.c_int32),
-                ("partition", ctypes.c_int32), ("correction", ctypes.c_int32), ("probe_selector", ctypes.c_int32)]
+                ("partition", ctypes.c_int32), ("correction", ctypes.c_int32), ("probe_selector", ctypes.c_int32),
+                ("key_rank", ctypes.c_int32)]
 
 
 class sparsepr_head_info(ctypes.Structure):
@@ -119,7 +120,7 @@ def _stream(stream=None):
 def make_config(batch, heads, seq_len, head_dim, dtype, n_sampled, n_key_groups, n_query_groups, n_probes,
                 density, kmeans_max_iter=25, kmeans_tol=1e-4, ridge_lambda=1e-3, penalize_bias=0, seed=0,
                 softmax_scale=0.0, assign_precision=0, warm_iters=2, partition=0, correction=0,
-                probe_selector=0):
+                probe_selector=0, key_rank=0):
     c = sparsepr_config()
     c.batch, c.heads, c.seq_len, c.head_dim = batch, heads, seq_len, head_dim
     c.dtype = {"f32": SPARSEPR_F32, "bf16": SPARSEPR_BF16}.get(dtype, dtype)
@@ -131,6 +132,7 @@ def make_config(batch, heads, seq_len, head_dim, dtype, n_sampled, n_key_groups,
     c.assign_precision = assign_precision
     c.warm_iters = warm_iters
     c.partition, c.correction, c.probe_selector = partition, correction, probe_selector
+    c.key_rank = key_rank
     return c
 
 

@@ -1618,15 +1618,133 @@ static void group_mass(const T* q, const Dims& D, const Bufs& B, hipStream_t s) 
   }
 }
 
+// Key response rank (paper Table C.1, r_K): the key metric G = s^2 Q_S^T Q_S is replaced
+// by its truncation to the r_K largest eigenvalues, G_r = sum_i lambda_i u_i u_i^T, which
+// is the metric of the key responses projected on the sampled queries' r_K leading
+// response directions. One block per head: cyclic two-sided Jacobi in LDS (float),
+// round-robin pairings so that the n/2 rotations of a round act on disjoint index pairs
+// and are applied together, 2 x 2 block by 2 x 2 block; sweeps until the off-diagonal
+// mass is below 1e-14 of the total (at most 15). The r_K largest diagonal entries (ties
+// to the lower index) select the eigenvectors.
+template <int DD>
+__global__ __launch_bounds__(1024) void k_metric_rank(Dims D, Bufs B) {
+  constexpr int n = DD, H2 = DD / 2, LD = DD + 1;
+  __shared__ float A[DD * LD], V[DD * LD];
+  __shared__ float cs_c[H2], cs_s[H2];
+  __shared__ int pp[H2], qq[H2];
+  __shared__ float red[2][16];
+  __shared__ int sel[DD];
+  const int bh = blockIdx.x, tid = threadIdx.x;
+  float* G = B.metric + (size_t)bh * DD * DD;
+  for (int e = tid; e < n * n; e += 1024) {
+    const int i = e / n, j = e % n;
+    A[i * LD + j] = G[e];
+    V[i * LD + j] = i == j ? 1.f : 0.f;
+  }
+  __syncthreads();
+  for (int sweep = 0; sweep < 15; ++sweep) {
+    // off-diagonal and total mass, summed in a fixed order
+    float off = 0.f, tot = 0.f;
+    for (int e = tid; e < n * n; e += 1024) {
+      const float v = A[(e / n) * LD + e % n];
+      tot += v * v;
+      if (e / n != e % n) off += v * v;
+    }
+    off = wave_sum(off);
+    tot = wave_sum(tot);
+    if (lane_id() == 0) {
+      red[0][tid / kWave] = off;
+      red[1][tid / kWave] = tot;
+    }
+    __syncthreads();
+    float o = 0.f, t = 0.f;
+    for (int w = 0; w < 16; ++w) {
+      o += red[0][w];
+      t += red[1][w];
+    }
+    __syncthreads();
+    if (!(o > 1e-14f * t)) break;
+    for (int rnd = 0; rnd < n - 1; ++rnd) {
+      if (tid < H2) {
+        auto player = [&](int pos) { return pos == 0 ? 0 : ((pos - 1 + rnd) % (n - 1)) + 1; };
+        const int a = player(tid), b = player(n - 1 - tid);
+        const int p = min(a, b), q = max(a, b);
+        const float apq = A[p * LD + q];
+        float c = 1.f, sn = 0.f;
+        if (apq != 0.f) {
+          const float tau = (A[q * LD + q] - A[p * LD + p]) / (2.f * apq);
+          const float tt = (tau >= 0.f ? 1.f : -1.f) / (fabsf(tau) + sqrtf(1.f + tau * tau));
+          c = 1.f / sqrtf(1.f + tt * tt);
+          sn = tt * c;
+        }
+        cs_c[tid] = c;
+        cs_s[tid] = sn;
+        pp[tid] = p;
+        qq[tid] = q;
+      }
+      __syncthreads();
+      // A <- J^T A J, block (i, j) = rows (p_i, q_i) x columns (p_j, q_j)
+      for (int e = tid; e < H2 * H2; e += 1024) {
+        const int i = e / H2, j = e % H2;
+        const int pi = pp[i], qi = qq[i], pj = pp[j], qj = qq[j];
+        const float ci = cs_c[i], si = cs_s[i], cj = cs_c[j], sj = cs_s[j];
+        const float m00 = A[pi * LD + pj], m01 = A[pi * LD + qj], m10 = A[qi * LD + pj], m11 = A[qi * LD + qj];
+        const float t00 = m00 * cj - m01 * sj, t01 = m00 * sj + m01 * cj;
+        const float t10 = m10 * cj - m11 * sj, t11 = m10 * sj + m11 * cj;
+        A[pi * LD + pj] = ci * t00 - si * t10;
+        A[pi * LD + qj] = ci * t01 - si * t11;
+        A[qi * LD + pj] = si * t00 + ci * t10;
+        A[qi * LD + qj] = si * t01 + ci * t11;
+      }
+      // V <- V J
+      for (int e = tid; e < n * H2; e += 1024) {
+        const int r = e / H2, j = e % H2;
+        const int pj = pp[j], qj = qq[j];
+        const float cj = cs_c[j], sj = cs_s[j];
+        const float vp = V[r * LD + pj], vq = V[r * LD + qj];
+        V[r * LD + pj] = vp * cj - vq * sj;
+        V[r * LD + qj] = vp * sj + vq * cj;
+      }
+      __syncthreads();
+    }
+  }
+  // the r_K largest eigenvalues (ties to the lower index)
+  if (tid < n) {
+    const float li = A[tid * LD + tid];
+    int rank = 0;
+    for (int j = 0; j < n; ++j) {
+      const float lj = A[j * LD + j];
+      rank += (lj > li) || (lj == li && j < tid);
+    }
+    sel[tid] = rank < D.key_rank;
+  }
+  __syncthreads();
+  for (int e = tid; e < n * n; e += 1024) {
+    const int a = e / n, b = e % n;
+    float g = 0.f;
+    for (int i = 0; i < n; ++i)
+      if (sel[i]) g = fmaf(A[i * LD + i] * V[a * LD + i], V[b * LD + i], g);
+    const size_t o = (size_t)bh * DD * DD + e;
+    B.metric[o] = g;
+    const bf16 gh = (bf16)g;
+    B.metric_h[o] = gh;
+    B.metric_l[o] = (bf16)(g - (float)gh);
+  }
+}
+
 // Lloyd metric of the key side: s^2 Q_S^T Q_S (responses to the sampled queries), or the
 // identity for the semantic partition.
 template <int DD>
 static void key_metric(const Dims& D, const Bufs& B, hipStream_t s) {
-  if (D.partition == 1)
+  if (D.partition == 1) {
     hipLaunchKernelGGL((k_identity_metric<DD>), dim3(DD * DD / 256, D.BH), dim3(256), 0, s, D, B);
-  else
-    hipLaunchKernelGGL((k_gram<DD>), dim3(DD * DD / 256, D.BH), dim3(256), 0, s, B.qs, D.S, (const KmState*)nullptr,
-                       D.scale * D.scale, B.metric, B.metric_h, B.metric_l);
+    return;
+  }
+  hipLaunchKernelGGL((k_gram<DD>), dim3(DD * DD / 256, D.BH), dim3(256), 0, s, B.qs, D.S, (const KmState*)nullptr,
+                     D.scale * D.scale, B.metric, B.metric_h, B.metric_l);
+  // rank reduction only below the rank of Q_S (at most min(d, S))
+  if (D.key_rank > 0 && D.key_rank < DD && D.key_rank < D.S)
+    hipLaunchKernelGGL((k_metric_rank<DD>), dim3(D.BH), dim3(1024), 0, s, D, B);
 }
 
 // Metric, row constants and row scales of the query side: responses to the key centroids,

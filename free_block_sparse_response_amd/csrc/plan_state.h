@@ -49,6 +49,7 @@ struct Dims {
   int partition;  // 0 response-coupled, 1 semantic (raw K and Q), 2 key responses + raw Q
   int correction; // 0 weighted ridge, 1 mean-only, 2 none
   int probe_sel;  // 0 query-group stratified, 1 random, 2 uniform in token order
+  int key_rank;   // key response rank r_K (0: full)
   uint64_t seed;
 };
 

@@ -191,6 +191,7 @@ sparsepr_status sparsepr_plan_create(const sparsepr_config* cfg, sparsepr_plan_t
   if (c.partition < 0 || c.partition > 2) return SPARSEPR_ERR_INVALID_ARG;
   if (c.correction < 0 || c.correction > 2) return SPARSEPR_ERR_INVALID_ARG;
   if (c.probe_selector < 0 || c.probe_selector > 2) return SPARSEPR_ERR_INVALID_ARG;
+  if (c.key_rank < 0) return SPARSEPR_ERR_INVALID_ARG;
 
   sparsepr_plan_s* p = new (std::nothrow) sparsepr_plan_s();
   if (!p) return SPARSEPR_ERR_INVALID_ARG;
@@ -232,6 +233,7 @@ sparsepr_status sparsepr_plan_create(const sparsepr_config* cfg, sparsepr_plan_t
   D.partition = c.partition;
   D.correction = c.correction;
   D.probe_sel = c.probe_selector;
+  D.key_rank = c.key_rank;
   D.seed = c.seed;
   carve(D, nullptr, &p->ws_bytes);
   p->ws = nullptr;

@@ -91,6 +91,12 @@ typedef struct {
   int32_t probe_selector;                  /* 0 query-group stratified; 1 random (smallest*/
                                            /*   probe hash over all tokens); 2 uniform    */
                                            /*   (tokens floor((2p+1)N/2M)); 1, 2 weigh 1  */
+  int32_t key_rank;                        /* key response rank r_K (paper Table C.1: 48); */
+                                           /*   0 = full; k-means of the keys on their     */
+                                           /*   responses projected on the r_K leading     */
+                                           /*   directions of the sampled queries (metric  */
+                                           /*   G truncated to its r_K largest eigenvalues)*/
+                                           /*   applied when 0 < r_K < min(d, S)           */
 } sparsepr_config;
 
 typedef struct sparsepr_plan_s* sparsepr_plan_t;

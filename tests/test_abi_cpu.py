@@ -66,6 +66,7 @@ def _create(lib, cfg):
     (dict(partition=3), L.SPARSEPR_ERR_INVALID_ARG),
     (dict(correction=-1), L.SPARSEPR_ERR_INVALID_ARG),
     (dict(probe_selector=3), L.SPARSEPR_ERR_INVALID_ARG),
+    (dict(key_rank=-1), L.SPARSEPR_ERR_INVALID_ARG),
 ])
 def test_plan_create_rejects(lib, over, want):
     st, h = _create(lib, _cfg(**over))

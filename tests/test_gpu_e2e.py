@@ -324,3 +324,13 @@ def test_comparison_partitions_match_oracle(name, partition):
     w = dict(configs.CONFIGS[name], partition=partition)
     heads = [0] if name == "c1" else [0, 3]
     _error_stats_vs_oracle(w, heads, rows_per_head=None if name == "c1" else 2048)
+
+
+# ------------------------------------------------------------------- key response rank
+@pytest.mark.parametrize("name,rank", [("c1", 48), ("c2", 48)])
+def test_key_rank_matches_oracle(name, rank):
+    # keys clustered on their responses reduced to the sampled queries' leading directions
+    # (Jacobi on the GPU, SVD in the oracle): the library's own plan against the oracle's
+    w = dict(configs.CONFIGS[name], key_rank=rank)
+    heads = [0] if name == "c1" else [0, 5]
+    _error_stats_vs_oracle(w, heads, rows_per_head=None if name == "c1" else 2048)
