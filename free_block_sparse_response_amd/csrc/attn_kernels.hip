@@ -78,40 +78,30 @@ struct TileSeq {
 };
 
 // Walks the KT-key tiles of one work item over its key runs (the plan lists each query
-// group's runs). The runs are held one per lane, 64 at a time, and read out with v_readlane,
-// so stepping from tile to tile touches no memory. A run [lo, hi) starts its first tile at lo
-// rounded down to 8 keys (16-byte aligned rows of the transposed V); keys outside [lo, hi)
-// are masked.
+// group's runs). The runs are copied to LDS when the work item starts, so stepping from run
+// to run reads LDS only and never waits on the global loads in flight. A run [lo, hi)
+// starts its first tile at lo rounded down to 8 keys (16-byte aligned rows of the
+// transposed V); keys outside [lo, hi) are masked.
 template <int KT>
 struct TileWalk {
-  const int2* runs;
-  int nr, r;      // runs of the item, current run
-  int rlo, rhi;   // this lane's run of the current batch of 64
+  const int2* runs;  // the item's runs, in LDS
+  int nr, r;         // runs of the item, current run
   int lo, hi, k0;
-  __device__ void load_batch(int base) {
-    const int i = base + lane_id();
-    const int2 v = i < nr ? runs[i] : make_int2(0, 0);
-    rlo = v.x;
-    rhi = v.y;
-  }
   __device__ void set_run() {
-    if (r > 0 && (r & 63) == 0) load_batch(r);
-    lo = __builtin_amdgcn_readlane(rlo, r & 63);
-    hi = __builtin_amdgcn_readlane(rhi, r & 63);
+    const int2 v = runs[r];  // one address for the whole wave
+    lo = __builtin_amdgcn_readfirstlane(v.x);
+    hi = __builtin_amdgcn_readfirstlane(v.y);
     k0 = lo & ~7;
   }
   __device__ bool first() {
     r = 0;
     if (nr <= 0) return false;
-    load_batch(0);
     set_run();
     return true;
   }
   __device__ bool first_single(int a, int b) {  // one run [a, b), no run list
     r = 0;
     nr = a < b ? 1 : 0;
-    rlo = a;
-    rhi = b;
     lo = a;
     hi = b;
     k0 = a & ~7;
@@ -143,9 +133,9 @@ struct TileWalk {
 // registers). The K rows of a 32-key block are read in the order pi (bits 2 and 3 of the row
 // swapped), which makes the eight scores a lane holds for one 16-key chunk eight consecutive
 // keys, so the V^T operand is a single 16-byte read per MFMA.
-// The accumulator is rescaled only when a query's running max grows by more than 2^16 (the
-// stale max keeps every exponential <= 2^16: far from overflow in fp32, and bf16 keeps its
-// relative precision at any magnitude).
+// The reference max is lazy: a tile is exponentiated against the running max, and only a
+// tile whose numerators could exceed 2^16 is redone against its exact max (then the
+// accumulator is rescaled before the next PV product).
 // -------------------------------------------------------------------------------------
 __device__ inline int swap_bits23(int x) { return (x & ~12) | ((x & 4) << 1) | ((x & 8) >> 1); }
 
@@ -162,6 +152,7 @@ __global__ __launch_bounds__(256, 2) void k_bsfa_bf16(const bf16* __restrict__ q
   constexpr int ND = DD / 32;           // 32-wide d blocks of the output
   static_assert((DD == 64 || DD == 128) && KI >= 1 && VI >= 1, "tile shape");
   __shared__ __attribute__((aligned(1024))) bf16 Kb0[KT * DD], Kb1[KT * DD], Vb0[DD * KT], Vb1[DD * KT];
+  __shared__ int2 runs_s[kMaxGroups];
 
   const int nb = gridDim.x;
   const int bid = xcd_remap(blockIdx.x, nb);
@@ -225,7 +216,10 @@ __global__ __launch_bounds__(256, 2) void k_bsfa_bf16(const bf16* __restrict__ q
     vlane = (unsigned)(rv * 2 * D.Npad + 16 * ((l % 4) ^ vswz(rv)));
   }
   // Tile staging through registers, two steps deep: the global loads issued in one step are
-  // stored to LDS at the end of the next, so a load has about two steps to arrive.
+  // stored to LDS at the end of the next, so a load has about two steps to arrive. Every step
+  // issues the same loads (past the last tile they re-read the current one, unused), so the
+  // count of loads in flight is the same on every path and the wait before a store covers
+  // only the loads of the step before.
   struct Stage {
     bf16x8 k[KI], v[VI];
   };
@@ -296,9 +290,11 @@ __global__ __launch_bounds__(256, 2) void k_bsfa_bf16(const bf16* __restrict__ q
         if (16 * (v >> 3) + (v & 7) >= vhi) s[v] = -INFINITY;
     }
   };
-  auto max8 = [&](const f32x16& s, int b) {  // max of scores b .. b+7
-    return fmaxf(fmaxf(fmaxf(s[b], s[b + 1]), fmaxf(s[b + 2], s[b + 3])),
-                 fmaxf(fmaxf(s[b + 4], s[b + 5]), fmaxf(s[b + 6], s[b + 7])));
+  auto max16 = [&](const f32x16& s) {  // max of the 16 scores (v_max3 tree)
+    const float a = fmaxf(fmaxf(s[0], s[1]), s[2]), b = fmaxf(fmaxf(s[3], s[4]), s[5]);
+    const float c = fmaxf(fmaxf(s[6], s[7]), s[8]), e = fmaxf(fmaxf(s[9], s[10]), s[11]);
+    const float f = fmaxf(fmaxf(s[12], s[13]), s[14]);
+    return fmaxf(fmaxf(fmaxf(a, b), s[15]), fmaxf(fmaxf(c, e), f));
   };
   // moves the accumulator and row sum to max mu when any lane of the wave raised its max
   auto rescale = [&](float mu) {
@@ -312,38 +308,46 @@ __global__ __launch_bounds__(256, 2) void k_bsfa_bf16(const bf16* __restrict__ q
         for (int v = 0; v < 16; ++v) o[i][v] *= alpha;
     }
   };
-  // Softmax numerators of one tile, spread over 8 slices (each after one MFMA of the previous
-  // tile's PV product). Slices 0-1 take the tile max and the lazily raised reference max mu
-  // (the tile max when it exceeds the running max by more than 2^16, else the running max).
-  // The 16 scores then go in groups of four through a three-slice pipeline: scale and shift
-  // in slice 2+g, exponentiate in 3+g, sum and pack into the P^T operands in 4+g.
-  auto soft_slice = [&](const f32x16& s, int i, float (&mx)[2], float& mu, float& ps, float (&xe)[16],
-                        bf16x8 (&pn)[2]) {
-    if (i == 0) {
-      mx[0] = max8(s, 0);
-      mx[1] = max8(s, 8);
+  // Softmax numerators of one tile against the reference max mu, in pairs of scores: scale
+  // and shift, exponentiate, pack to bf16 and add the packed pair to the row sum (one
+  // v_dot2 with (1, 1), so the sum is of the same rounded values that enter PV). Pair g
+  // goes through a three-slice pipeline (shift in slice g, exp in g+1, pack in g+2); slices
+  // 0-7 each follow one MFMA of the previous tile's PV product, 8 and 9 close the pipeline.
+  const bf16x2 ones = {(bf16)1.f, (bf16)1.f};
+  auto soft_slice = [&](const f32x16& s, int i, float mu, float& ps, float (&xe)[16], bf16x8 (&pn)[2]) {
+    const int gp = i - 2, ge = i - 1, gf = i;
+    if (gp >= 0 && gp < 8) {
+      bf16x2 pr;
+      pr[0] = (bf16)xe[2 * gp];
+      pr[1] = (bf16)xe[2 * gp + 1];
+      pn[gp >> 2][2 * (gp & 3)] = pr[0];
+      pn[gp >> 2][2 * (gp & 3) + 1] = pr[1];
+      ps = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, ps, false);
     }
-    if (i == 1) {
-      const float mt = fmaxf(mx[0], mx[1]);
-      const float m2 = fmaxf(mt, xor32(mt)) * c2;
-      mu = m2 > m_run + 16.f ? m2 : m_run;
-      ps = 0.f;
+    if (ge >= 0 && ge < 8) {
+      xe[2 * ge] = __builtin_amdgcn_exp2f(xe[2 * ge]);
+      xe[2 * ge + 1] = __builtin_amdgcn_exp2f(xe[2 * ge + 1]);
     }
-    const int ga = i - 4, ge = i - 3, gf = i - 2;
-    if (ga >= 0 && ga < 4) {
-      const int t = 4 * ga;
-      ps += (xe[t] + xe[t + 1]) + (xe[t + 2] + xe[t + 3]);
+    if (gf < 8) {
+      xe[2 * gf] = fmaf(s[2 * gf], c2, -mu);
+      xe[2 * gf + 1] = fmaf(s[2 * gf + 1], c2, -mu);
+    }
+  };
+  // The reference max is kept lazily: numerators are formed against the running max, and
+  // only when a lane's partial row sum of the tile exceeds 2^16 (so some numerator may be
+  // large, or infinite) is the tile redone against its exact max; the first tile of a work
+  // item, with no max yet, always is. Every numerator kept is therefore <= 2^16: far from
+  // overflow in fp32, and bf16 keeps its relative precision at any magnitude.
+  auto soft_exact = [&](const f32x16& s, float& mu, float& ps, bf16x8 (&pn)[2]) {
+    const float mt = max16(s);
+    mu = fmaxf(mu, fmaxf(mt, xor32(mt)) * c2);
+    ps = 0.f;
+    float xe[16];
 #pragma unroll
-      for (int u = 0; u < 4; ++u) pn[t >> 3][(t & 7) + u] = (bf16)xe[t + u];
-    }
-    if (ge >= 0 && ge < 4) {
-#pragma unroll
-      for (int u = 0; u < 4; ++u) xe[4 * ge + u] = __builtin_amdgcn_exp2f(xe[4 * ge + u]);
-    }
-    if (gf >= 0 && gf < 4) {
-#pragma unroll
-      for (int u = 0; u < 4; ++u) xe[4 * gf + u] = fmaf(s[4 * gf + u], c2, -mu);
-    }
+    for (int i = 0; i < 10; ++i) soft_slice(s, i, mu, ps, xe, pn);
+  };
+  auto check = [&](const f32x16& s, float& mu, float& ps, bf16x8 (&pn)[2]) {
+    if (__builtin_amdgcn_ballot_w64(!(ps <= 65536.f))) soft_exact(s, mu, ps, pn);
   };
   // O^T += V^T P^T of the previous tile (V operands two MFMAs ahead) interleaved with the
   // softmax numerators of the current tile
@@ -355,17 +359,19 @@ __global__ __launch_bounds__(256, 2) void k_bsfa_bf16(const bf16* __restrict__ q
     bf16x8 va[NI];
     va[0] = vread(Vp, vb, 0);
     va[1] = vread(Vp, vb, 1);
-    float mx[2], xe[16];
+    float xe[16];
+    ps = 0.f;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
+    for (int i = 0; i < 10; ++i) {
       if (i < NI) {
         const int cc = i / ND, db = i % ND;
         o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[i], pp[cc], o[db], 0, 0, 0);
         if (i + 2 < NI) va[i + 2] = vread(Vp, vb, i + 2);
       }
-      soft_slice(s, i, mx, mu, ps, xe, pn);
+      soft_slice(s, i, mu, ps, xe, pn);
       __builtin_amdgcn_sched_barrier(0);
     }
+    check(s, mu, ps, pn);
   };
   auto pv = [&](const bf16* Vp, const bf16x8 (&pp)[2]) {
     constexpr int NI = 2 * ND;
@@ -382,17 +388,15 @@ __global__ __launch_bounds__(256, 2) void k_bsfa_bf16(const bf16* __restrict__ q
       __builtin_amdgcn_sched_barrier(0);
     }
   };
-  auto soft = [&](const f32x16& s, float& mu, float& ps, bf16x8 (&pn)[2]) {
-    float mx[2], xe[16];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) soft_slice(s, i, mx, mu, ps, xe, pn);
-  };
-
   TileWalk<KT> ts;
   bool has;  // the next tile exists
   if (MODE != 1) {
-    ts.runs = B.runs + (size_t)bh * D.Cq * D.Ck + B.row_ptr[(size_t)bh * (D.Cq + 1) + a];
-    ts.nr = B.nruns[(size_t)bh * D.Cq + a];
+    const int2* rg = B.runs + (size_t)bh * D.Cq * D.Ck + B.row_ptr[(size_t)bh * (D.Cq + 1) + a];
+    const int nr = __builtin_amdgcn_readfirstlane(B.nruns[(size_t)bh * D.Cq + a]);  // <= C_k <= kMaxGroups
+    for (int i = tid; i < nr; i += 256) runs_s[i] = rg[i];
+    __syncthreads();
+    ts.runs = runs_s;
+    ts.nr = nr;
     has = ts.first();
   } else {
     const int clo = a * D.pkc;
@@ -416,19 +420,19 @@ __global__ __launch_bounds__(256, 2) void k_bsfa_bf16(const bf16* __restrict__ q
     Stage sa, sb;  // sa: K(j+1), V(j) (stored at the end of step j); sb: K(j+2), V(j+1)
     load_k(sa, k0c);
     store_k(sa, Kb0);
-    if (has1) load_k(sa, k01);
+    load_k(sa, has1 ? k01 : k0c);
     load_v(sa, k0c);
     // Step j: K(j) is in K buffer j%2, V(j-1) in V buffer (j-1)%2. Load K(j+2) and V(j+1);
     // S(j) = K(j) Q^T; O += V(j-1) P(j-1) while S(j) turns into P(j); store K(j+1) and V(j).
     // Step 0 has no PV; one loop body serves both parities, so O keeps its registers.
     __syncthreads();
-    if (has2) load_k(sb, k02);
-    if (has1) load_v(sb, k01);
+    load_k(sb, has2 ? k02 : k0c);
+    load_v(sb, has1 ? k01 : k0c);
     if (wave_active) {
       f32x16 s;
       qk(Kb0, s);
       if (loc > k0c || hic < k0c + KT) mask(s, k0c, loc, hic);
-      soft(s, mu, ps, pp);
+      soft_exact(s, mu, ps, pp);
     }
     if (has1) store_k(sa, Kb1);
     store_v(sa, Vb0);
@@ -446,8 +450,8 @@ __global__ __launch_bounds__(256, 2) void k_bsfa_bf16(const bf16* __restrict__ q
       const bf16* Vp = par ? Vb0 : Vb1;
       bf16* Vc = par ? Vb1 : Vb0;
       __syncthreads();
-      if (has2) load_k(nxt, k02);
-      if (has1) load_v(nxt, k01);
+      load_k(nxt, has2 ? k02 : k0c);
+      load_v(nxt, has1 ? k01 : k0c);
       if (wave_active) {
         rescale(mu);
         l_half += ps;
