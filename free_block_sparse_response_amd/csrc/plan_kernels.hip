@@ -437,7 +437,7 @@ __device__ void km_init_item(const T* x, const Dims& D, const Bufs& B, int C, co
       st[bh].done_iter = 0x7fffffff;
       st[bh].iters = 0;
       st[bh].c_final = C;
-      st[bh].prev = 0.0;
+      st[bh].inertia[0] = st[bh].inertia[1] = 0.0;
     }
   }
   __syncthreads();
@@ -458,7 +458,7 @@ __global__ __launch_bounds__(64) void k_km_scan_groups(Dims D, Bufs B, int C, Km
   int run = 0;
   for (int i0 = 0; i0 < D.nblk; i0 += kWave) {
     const int i = i0 + l;
-    const int c = i < D.nblk ? tab[i] : 0;
+    const int c = i < D.nblk ? (tab[i] & 255) : 0;  // the count (an update's lists also pack a start)
     const int inc = wave_incl_scan(c);
     if (i < D.nblk) tab[i] = run + inc - c;
     run += __shfl(inc, kWave - 1, kWave);
@@ -466,8 +466,9 @@ __global__ __launch_bounds__(64) void k_km_scan_groups(Dims D, Bufs B, int C, Km
   if (l == 0) B.gcount[(size_t)bh * D.C + b] = run;
 }
 
-// Per head: the inertia of this assignment, the stopping rule, and the group starts.
-// Thread i owns groups [4i, 4i + 4).
+// Per head: the inertia of assignment t, the stopping rule, and the group starts. With
+// t = 0 (offsets of the final assignment of a Lloyd run, whose updates kept the books) only
+// the group starts. Thread i owns groups [4i, 4i + 4).
 __global__ __launch_bounds__(256) void k_km_scan_head(Dims D, Bufs B, int C, KmState* st, int t) {
   constexpr int LPT = kMaxGroups / 256;
   __shared__ long long wsl[4];
@@ -489,17 +490,18 @@ __global__ __launch_bounds__(256) void k_km_scan_head(Dims D, Bufs B, int C, KmS
     if (b < C) B.gstart[(size_t)bh * (D.C + 1) + b] = (int)(base + loc[j]);
   }
   if (tid == 0) B.gstart[(size_t)bh * (D.C + 1) + C] = (int)tot;
-  if (w == 0) {
+  // t = 0: offsets of the final assignment only (the Lloyd updates kept the books)
+  if (w == 0 && t > 0) {
     double sum = 0.0;
     for (int i = l; i < D.nblk; i += kWave) sum += B.ipart[(size_t)bh * D.nblk + i];
     sum = wave_sum(sum);
     if (l == 0) {
-      const double prev = st[bh].prev;
+      const double prev = st[bh].inertia[(t - 1) & 1];
       int done = st[bh].done_iter;
       if (t > 1 && prev - sum <= (double)D.tol * prev) done = t;
       if (t >= D.max_iter) done = t;
       st[bh].done_iter = done;
-      st[bh].prev = sum;
+      st[bh].inertia[t & 1] = sum;
       st[bh].iters = t;
     }
   }
@@ -513,6 +515,38 @@ __device__ inline void km_scatter_item(const Dims& D, const Bufs& B, KmState* st
   const int pos = B.gstart[(size_t)bh * (D.C + 1) + lab] + B.tab[((size_t)bh * D.C + lab) * D.nblk + blk] +
                   B.rank[(size_t)bh * D.N + row];
   perm[(size_t)bh * D.N + pos] = row;
+}
+
+// The sort block's lists for the Lloyd update, 256 threads: per group its count and the
+// start of the group in the block's group-ordered row list (tab, packed: count | start << 8,
+// both at most kKmRows), and that list (lperm), which keeps rows of one group in index order.
+// count(g) gives the block's count of group g; starts (LDS, kMaxGroups) receives the starts.
+// Thread i owns groups 4i .. 4i + 3.
+template <typename CountFn>
+__device__ inline void km_block_lists(CountFn count, int* starts, int* ws, int C, const Dims& D, const Bufs& B, int bh,
+                                      int sb, bool valid, int lab, int rank, int row) {
+  int hc[4], run = 0;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int g = 4 * threadIdx.x + q;
+    hc[q] = g < C ? count(g) : 0;
+    run += hc[q];
+  }
+  int tot;
+  int s = block_excl_scan<256, int>(run, &tot, ws);
+  static_assert(kKmRows < 256, "count and start take 8 bits each");
+  int* tab = B.tab + (size_t)bh * D.C * D.nblk;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int g = 4 * threadIdx.x + q;
+    if (g < C) {
+      tab[(size_t)g * D.nblk + sb] = hc[q] | (s << 8);
+      starts[g] = s;
+    }
+    s += hc[q];
+  }
+  __syncthreads();
+  if (valid) B.lperm[(size_t)bh * D.N + (size_t)sb * kKmRows + starts[lab] + rank] = row;
 }
 
 // Assignment of iteration t: nearest centroid (ties to the lower id) of 128 rows, the
@@ -595,8 +629,8 @@ __global__ __launch_bounds__(256) void k_km_assign(const T* x, Dims D, Bufs B, i
   if (w == 1 && leader) hist[lab] += __popcll(mask);
   if (valid) B.rank[(size_t)bh * D.N + row] = rank;
   __syncthreads();
-  int* tab = B.tab + (size_t)bh * D.C * D.nblk;
-  for (int i = threadIdx.x; i < C; i += 256) tab[(size_t)i * D.nblk + blk] = hist[i];
+  __shared__ int scan_ws[4];
+  km_block_lists([&](int g) { return hist[g]; }, hist, scan_ws, C, D, B, bh, blk, valid, lab, rank, row);
 }
 
 
@@ -653,35 +687,139 @@ __device__ void group_mean(const T* xb, const float* alpha, const int* members, 
   __syncthreads();
 }
 
+constexpr int kUpdWin = 1024;   // sort blocks per window of the update's member listing
+constexpr int kUpdChunk = 1024; // members listed in LDS at a time
+
+// Update of iteration t for group b (one block per group and head, 256 threads).
+// First the stopping rule of the head: every block of the head evaluates it identically
+// (the inertia of assignment t is the fixed-order sum of the sort blocks' partials, set
+// against the inertia of assignment t - 1); block 0 records it. Unless the head stops at t,
+// the new centroid m_b is the mean of the group's rows alpha_j x_j, then G m_b and
+// m_b G m_b. The members are read in stable group order (sort blocks in order, each
+// block's rows of group b from its lists: count and start in tab, rows in lperm), listed
+// in LDS a chunk at a time; member r of a chunk sits in slot r % RS and the slots are
+// summed in a fixed order, so the result does not depend on scheduling.
 template <typename T, int DD>
-__device__ void km_update_item(const T* x, const Dims& D, const Bufs& B, KmState* st, int t, const int* perm, int b,
-                               int bh) {
-  __shared__ float sh[2048];
+__global__ __launch_bounds__(256) void k_km_update(const T* x, Dims D, Bufs B, KmState* st, int t) {
+  constexpr int EV = 16 / sizeof(T);
+  constexpr int LPR = DD / EV;
+  constexpr int RS = 256 / LPR;
+  __shared__ float sh[RS * DD];
   __shared__ float m[DD];
   __shared__ float red[4];
-  if (st[bh].done_iter <= t) return;
-  const int n = B.gcount[(size_t)bh * D.C + b];
-  if (n == 0) return;  // empty cluster keeps its centroid
-  const int s0 = B.gstart[(size_t)bh * (D.C + 1) + b];
+  __shared__ int wpre[kUpdWin], wbeg[kUpdWin], mlist[kUpdChunk], ws[4];
+  __shared__ int go;
+  const int b = blockIdx.x, bh = blockIdx.y, tid = threadIdx.x;
+  if (st[bh].done_iter < t) return;
+  if (tid < kWave) {
+    double sum = 0.0;
+    for (int i = tid; i < D.nblk; i += kWave) sum += B.ipart[(size_t)bh * D.nblk + i];
+    sum = wave_sum(sum);
+    if (tid == 0) {
+      const double prev = st[bh].inertia[(t - 1) & 1];
+      const bool done = (t > 1 && prev - sum <= (double)D.tol * prev) || t >= D.max_iter;
+      if (b == 0) {
+        st[bh].inertia[t & 1] = sum;
+        st[bh].iters = t;
+        if (done) st[bh].done_iter = t;
+      }
+      go = !done;
+    }
+  }
+  __syncthreads();
+  if (!go) return;
   const T* xb = x + (size_t)bh * D.N * DD;
   const float* alpha = B.alpha ? B.alpha + (size_t)bh * D.N : nullptr;
   // G m: threads i and i + DD (, ...) take interleaved parts of k; combined in order. The
   // metric's loads are issued before the gather so that the two latencies overlap.
   const float* G = B.metric + (size_t)bh * DD * DD;
   constexpr int KH = 256 / DD;
-  const int i = threadIdx.x % DD, part = threadIdx.x / DD;
+  const int i = tid % DD, part = tid / DD;
   float gv[DD / KH];
 #pragma unroll
   for (int kk = 0; kk < DD / KH; ++kk) gv[kk] = G[(size_t)(part + kk * KH) * DD + i];
-  group_mean<T, DD>(xb, alpha, perm + (size_t)bh * D.N + s0, n, m, sh);
+  const int* tab = B.tab + ((size_t)bh * D.C + b) * D.nblk;
+  const int* lp = B.lperm + (size_t)bh * D.N;
+  const int slot = tid / LPR, c0 = (tid % LPR) * EV;
+  float acc[EV];
+#pragma unroll
+  for (int e = 0; e < EV; ++e) acc[e] = 0.f;
+  auto add_row = [&](const uint4& raw, float a) {
+    const T* v = reinterpret_cast<const T*>(&raw);
+#pragma unroll
+    for (int e = 0; e < EV; ++e) acc[e] = fmaf(a, to_f32(v[e]), acc[e]);
+  };
+  int n = 0;
+  // windows of 1024 sort blocks (thread i takes blocks 4i .. 4i + 3)
+  for (int j0 = 0; j0 < D.nblk; j0 += kUpdWin) {
+    int cq[4], run = 0;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int j = j0 + 4 * tid + q;
+      const int v = j < D.nblk ? tab[j] : 0;
+      cq[q] = v & 255;
+      wbeg[4 * tid + q] = j * kKmRows + (v >> 8);
+      run += cq[q];
+    }
+    int mw;
+    int pre = block_excl_scan<256, int>(run, &mw, ws);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      wpre[4 * tid + q] = pre;
+      pre += cq[q];
+    }
+    __syncthreads();
+    // members of the window, kUpdChunk at a time: listed in LDS (the last block whose prefix
+    // is <= p holds member p), then gathered
+    for (int p0 = 0; p0 < mw; p0 += kUpdChunk) {
+      const int nc = min(kUpdChunk, mw - p0);
+      for (int p = tid; p < nc; p += 256) {
+        int k = 0;
+#pragma unroll
+        for (int step = kUpdWin / 2; step > 0; step >>= 1)
+          if (wpre[k + step] <= p0 + p) k += step;
+        mlist[p] = lp[wbeg[k] + (p0 + p - wpre[k])];
+      }
+      __syncthreads();
+      int r = slot;
+      for (; r + 7 * RS < nc; r += 8 * RS) {
+        uint4 raw[8];
+        float al[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          const int row = mlist[r + u * RS];
+          raw[u] = *reinterpret_cast<const uint4*>(xb + (size_t)row * DD + c0);
+          al[u] = alpha ? alpha[row] : 1.f;
+        }
+#pragma unroll
+        for (int u = 0; u < 8; ++u) add_row(raw[u], al[u]);
+      }
+      for (; r < nc; r += RS) {
+        const int row = mlist[r];
+        add_row(*reinterpret_cast<const uint4*>(xb + (size_t)row * DD + c0), alpha ? alpha[row] : 1.f);
+      }
+      __syncthreads();
+    }
+    n += mw;
+  }
+  if (n == 0) return;  // an empty group keeps its centroid
+#pragma unroll
+  for (int e = 0; e < EV; ++e) sh[slot * DD + c0 + e] = acc[e];
+  __syncthreads();
+  if (tid < DD) {
+    float tot = 0.f;
+    for (int q = 0; q < RS; ++q) tot += sh[q * DD + tid];
+    m[tid] = tot / (float)n;
+  }
+  __syncthreads();
   float p = 0.f;
   {
     float tt = 0.f;
 #pragma unroll
     for (int kk = 0; kk < DD / KH; ++kk) tt = fmaf(gv[kk], m[part + kk * KH], tt);
-    sh[threadIdx.x] = tt;
+    sh[tid] = tt;
     __syncthreads();
-    if (threadIdx.x < DD) {
+    if (tid < DD) {
       float tot = 0.f;
       for (int q = 0; q < KH; ++q) tot += sh[q * DD + i];
       const size_t o = ((size_t)bh * D.C + b) * DD + i;
@@ -694,19 +832,13 @@ __device__ void km_update_item(const T* x, const Dims& D, const Bufs& B, KmState
     }
   }
   p = wave_sum(p);
-  if (lane_id() == 0) red[threadIdx.x / kWave] = p;
+  if (lane_id() == 0) red[tid / kWave] = p;
   __syncthreads();
-  if (threadIdx.x == 0) {
+  if (tid == 0) {
     float sum = 0.f;
     for (int w = 0; w < DD / kWave; ++w) sum += red[w];
     B.cnorm[(size_t)bh * D.C + b] = sum;
   }
-  __syncthreads();
-}
-
-template <typename T, int DD>
-__global__ __launch_bounds__(256) void k_km_update(const T* x, Dims D, Bufs B, KmState* st, int t, const int* perm) {
-  km_update_item<T, DD>(x, D, B, st, t, perm, blockIdx.x, blockIdx.y);
 }
 
 // Warm start (paper Table C.1: a first k-means of up to 25 iterations, 2 for subsequent
@@ -899,16 +1031,22 @@ __global__ __launch_bounds__(256, 2) void k_km_assign_bf16(const bf16* x, Dims D
   const int tid = threadIdx.x, w = tid / kWave, l32 = lane_id() & 31, h = lane_id() >> 5;
   const int r0 = sb0 * kKmRows;
   bf16x8 xr[RS][DD / 16];
-  float a2[RS], best[RS];
-  int bidx[RS];
+  // The products start from -rc / a2 (rc = alpha^2 x G x, the row constant), so that
+  // cn_b - a2 acc is the squared distance itself, >= 0 up to rounding. A distance's float
+  // bits then order like integers; its low 10 bits are replaced by the centroid index (the
+  // part shared by both lane halves), and one integer min per pair of candidates keeps the
+  // nearest, the lower index among distances equal in the kept bits.
+  float a2[RS], ini[RS];
+  int bkey[RS];
 #pragma unroll
   for (int rs = 0; rs < RS; ++rs) {
     const int row = r0 + 128 * rs + 32 * w + l32;
     const bool valid = row < D.N;
     load_row_operand<DD>(x + ((size_t)bh * D.N + (valid ? row : D.N - 1)) * DD, xr[rs]);
     a2[rs] = 2.f * (B.alpha ? B.alpha[(size_t)bh * D.N + (valid ? row : 0)] : 1.f);
-    best[rs] = INFINITY;
-    bidx[rs] = 0;
+    const float rc = B.rowconst[(size_t)bh * D.N + (valid ? row : 0)];
+    ini[rs] = a2[rs] > 0.f ? -rc / a2[rs] : 0.f;
+    bkey[rs] = 0x7fffffff;
   }
   const bf16* Cop[2] = {B.cent_h + (size_t)bh * D.C * DD, B.cent_l + (size_t)bh * D.C * DD};
   const float* cn = B.cnorm + (size_t)bh * D.C;
@@ -949,11 +1087,16 @@ __global__ __launch_bounds__(256, 2) void k_km_assign_bf16(const bf16* x, Dims D
     if (more) load_chunk(c0 + CB);
 #pragma unroll
     for (int yb = 0; yb < CB; yb += 32) {
-      f32x16 acc[RS];
+      f32x16 acc[RS], cinit[RS];
 #pragma unroll
-      for (int rs = 0; rs < RS; ++rs)
+      for (int rs = 0; rs < RS; ++rs) {
+        // with the remainder operand the registers are short: the start block is rebuilt
+        // per centroid block instead of being kept
+        float iv = ini[rs];
+        if (LO) asm volatile("" : "+v"(iv));
 #pragma unroll
-        for (int v = 0; v < 16; ++v) acc[rs][v] = 0.f;
+        for (int v = 0; v < 16; ++v) cinit[rs][v] = iv;
+      }
 #pragma unroll
       for (int c = 0; c < DD / 16; ++c) {
 #pragma unroll
@@ -961,20 +1104,25 @@ __global__ __launch_bounds__(256, 2) void k_km_assign_bf16(const bf16* x, Dims D
           const bf16x8 av = *reinterpret_cast<const bf16x8*>(&Y[cur][o][(yb + l32) * KS + 16 * c + 8 * h]);
 #pragma unroll
           for (int rs = 0; rs < RS; ++rs)
-            acc[rs] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, xr[rs][c], acc[rs], 0, 0, 0);
+            acc[rs] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, xr[rs][c], c == 0 && o == 0 ? cinit[rs] : acc[rs],
+                                                              0, 0, 0);
         }
       }
-      // A lane visits its centroids in increasing index order, so a strict comparison keeps
-      // the lowest index among equal scores; the two lane halves merge with the full rule.
-      // The index kept is c0 + yb + 8 (v / 4) + v % 4 (wave-uniform); the lane-half offset
-      // 4 h is added once at the end.
+      // Candidate key = distance bits with the low 10 replaced by c0 + yb + 8 (v / 4) + v % 4
+      // (the index without the lane-half offset 4 h, which the merge of the halves restores).
+      // (a bit-field insert per candidate: the mask is kept in a register)
+      int im = 1023;
+      asm volatile("" : "+v"(im));
 #pragma unroll
       for (int rs = 0; rs < RS; ++rs)
 #pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          const int cl = yb + acc_row(v);
-          const float sc = fmaf(-a2[rs], acc[rs][v], cns[cur][cl]);
-          if (sc < best[rs]) { best[rs] = sc; bidx[rs] = c0 + yb + 8 * (v >> 2) + (v & 3); }
+        for (int v = 0; v < 16; v += 2) {
+          const float d0 = fmaf(-a2[rs], acc[rs][v], cns[cur][yb + acc_row(v)]);
+          const float d1 = fmaf(-a2[rs], acc[rs][v + 1], cns[cur][yb + acc_row(v + 1)]);
+          const int i0 = c0 + yb + 8 * (v >> 2) + (v & 3), i1 = i0 + 1;
+          const int k0 = (__float_as_int(d0) & ~im) | (i0 & im);
+          const int k1 = (__float_as_int(d1) & ~im) | (i1 & im);
+          bkey[rs] = min(min(bkey[rs], k0), k1);
         }
     }
     if (more) store_chunk(cur ^ 1);
@@ -988,15 +1136,17 @@ __global__ __launch_bounds__(256, 2) void k_km_assign_bf16(const bf16* x, Dims D
   int lab[RS];
 #pragma unroll
   for (int rs = 0; rs < RS; ++rs) {
-    bidx[rs] += 4 * h;
-    const float ob = __shfl_xor(best[rs], 32, kWave);
-    const int oi = __shfl_xor(bidx[rs], 32, kWave);
-    if (ob < best[rs] || (ob == best[rs] && oi < bidx[rs])) { best[rs] = ob; bidx[rs] = oi; }
+    // merge the halves: the smaller key wins; on equal keys the lower index, half 0
+    const int ok = __shfl_xor(bkey[rs], 32, kWave), myk = bkey[rs];
+    const int wk = min(ok, myk);
+    const int wh = ok < myk ? (h ^ 1) : (ok == myk ? 0 : h);
+    const int bidx = (wk & 1023) + 4 * wh;
+    const float bestd = __int_as_float(wk & ~1023);
     const int row = r0 + 128 * rs + 32 * w + l32;
     const bool valid = h == 0 && row < D.N;
-    lab[rs] = valid ? bidx[rs] : 0;
-    if (valid) B.lab[(size_t)bh * D.N + row] = bidx[rs];
-    double v = valid ? (double)B.rowconst[(size_t)bh * D.N + row] + (double)best[rs] : 0.0;
+    lab[rs] = valid ? bidx : 0;
+    if (valid) B.lab[(size_t)bh * D.N + row] = bidx;
+    double v = valid ? (double)bestd : 0.0;
     v = wave_sum(v);
     if (lane_id() == 0) wpart[rs][w] = v;
     mk[rs] = wave_match(lab[rs], valid, 10);
@@ -1006,20 +1156,27 @@ __global__ __launch_bounds__(256, 2) void k_km_assign_bf16(const bf16* x, Dims D
     if (valid && __popcll(mk[rs] & lanemask_lt()) == 0) cw[lab[rs]] = __popcll(mk[rs]);
   }
   __syncthreads();
-  int* tab = B.tab + (size_t)bh * D.C * D.nblk;
+  int rk[RS];
+#pragma unroll
+  for (int rs = 0; rs < RS; ++rs) {
+    const int sb = sb0 + rs;
+    const int row = r0 + 128 * rs + 32 * w + l32;
+    rk[rs] = __popcll(mk[rs] & lanemask_lt());
+    for (int w2 = 0; w2 < w; ++w2) rk[rs] += cnt[rs][w2][lab[rs]];
+    if (h == 0 && row < D.N) B.rank[(size_t)bh * D.N + row] = rk[rs];
+    if (tid == 0 && sb < D.nblk)
+      B.ipart[(size_t)bh * D.nblk + sb] = ((wpart[rs][0] + wpart[rs][1]) + wpart[rs][2]) + wpart[rs][3];
+  }
+  // the lists for the update; the block's starts overwrite the first wave's counts once every
+  // count of that row set has been read (the scan's barriers)
+  __shared__ int scan_ws[4];
 #pragma unroll
   for (int rs = 0; rs < RS; ++rs) {
     const int sb = sb0 + rs;
     if (sb >= D.nblk) break;
     const int row = r0 + 128 * rs + 32 * w + l32;
-    if (h == 0 && row < D.N) {
-      int rank = __popcll(mk[rs] & lanemask_lt());
-      for (int w2 = 0; w2 < w; ++w2) rank += cnt[rs][w2][lab[rs]];
-      B.rank[(size_t)bh * D.N + row] = rank;
-    }
-    for (int i = tid; i < C; i += 256)
-      tab[(size_t)i * D.nblk + sb] = cnt[rs][0][i] + cnt[rs][1][i] + cnt[rs][2][i] + cnt[rs][3][i];
-    if (tid == 0) B.ipart[(size_t)bh * D.nblk + sb] = ((wpart[rs][0] + wpart[rs][1]) + wpart[rs][2]) + wpart[rs][3];
+    km_block_lists([&](int g) { return cnt[rs][0][g] + cnt[rs][1][g] + cnt[rs][2][g] + cnt[rs][3][g]; }, cnt[rs][0],
+                   scan_ws, C, D, B, bh, sb, h == 0 && row < D.N, lab[rs], rk[rs], row);
   }
 }
 
@@ -1196,7 +1353,7 @@ __global__ void k_state_reset(KmState* st, int BH, int C, int done) {
     st[bh].done_iter = done;
     st[bh].iters = 0;
     st[bh].c_final = C;
-    st[bh].prev = 0.0;
+    st[bh].inertia[0] = st[bh].inertia[1] = 0.0;
   }
 }
 
@@ -1582,12 +1739,12 @@ static void lloyd_iterations(const T* x, const Dims& D, const Bufs& B, int C, Km
                            st, t);
     else
       hipLaunchKernelGGL((k_km_assign<T, DD>), dim3(D.nblk, D.BH), dim3(256), 0, s, x, D, B, C, st, t);
-    hipLaunchKernelGGL(k_km_scan_groups, dim3(C, D.BH), dim3(64), 0, s, D, B, C, st, t);
-    hipLaunchKernelGGL(k_km_scan_head, dim3(D.BH), dim3(256), 0, s, D, B, C, st, t);
-    hipLaunchKernelGGL(k_km_scatter, dim3(D.nblk, D.BH), dim3(kKmRows), 0, s, D, B, st, t, perm);
-    if (t < D.max_iter)
-      hipLaunchKernelGGL((k_km_update<T, DD>), dim3(C, D.BH), dim3(256), 0, s, x, D, B, st, t, perm);
+    hipLaunchKernelGGL((k_km_update<T, DD>), dim3(C, D.BH), dim3(256), 0, s, x, D, B, st, t);
   }
+  // group starts and the permutation of the final assignment
+  hipLaunchKernelGGL(k_km_scan_groups, dim3(C, D.BH), dim3(64), 0, s, D, B, C, st, 0);
+  hipLaunchKernelGGL(k_km_scan_head, dim3(D.BH), dim3(256), 0, s, D, B, C, st, 0);
+  hipLaunchKernelGGL(k_km_scatter, dim3(D.nblk, D.BH), dim3(kKmRows), 0, s, D, B, st, 0, perm);
 }
 
 template <typename T, int DD>

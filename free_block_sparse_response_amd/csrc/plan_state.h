@@ -14,7 +14,7 @@ struct KmState {
   int iters;       // assignments run
   int c_final;     // groups left after dropping empty ones
   int pad;
-  double prev;     // inertia of the previous assignment
+  double inertia[2];  // inertia of assignment t in slot t & 1 (the previous one in the other)
 };
 
 // Routing facts of one head.
@@ -67,7 +67,9 @@ struct Bufs {
   float* alpha;      // [BH][N]    row scales of the query features
   float* rowconst;   // [BH][N]    alpha^2 x G x
   int* rank;         // [BH][N]    stable rank inside a Lloyd row block
-  int* tab;          // [BH][C][nblk] block counts -> scatter offsets
+  int* tab;          // [BH][C][nblk] count of group b in sort block j (low 8 bits) and its start in
+                     //   the block's group-ordered rows (bits 8+); turned into scatter offsets
+  int* lperm;        // [BH][N]    rows of each sort block, ordered by group (stable)
   double* ipart;     // [BH][nblk] inertia partial sums
   int* init_k;       // [BH][Ck] key-group seed rows
   int* init_q;       // [BH][Cq] query-group seed rows

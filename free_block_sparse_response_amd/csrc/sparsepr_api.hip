@@ -86,6 +86,7 @@ Bufs carve(const Dims& D, void* base, size_t* total) {
   B.rowconst = c.take<float>(BH * N);
   B.rank = c.take<int>(BH * N);
   B.tab = c.take<int>(BH * C * D.nblk);
+  B.lperm = c.take<int>(BH * N);
   B.ipart = c.take<double>(BH * D.nblk);
   B.init_k = c.take<int>(BH * D.Ck);
   B.init_q = c.take<int>(BH * D.Cq);
