@@ -113,6 +113,87 @@ __device__ void select_smallest(int n, int m, Cand cand, uint64_t base, int* out
     if (sel) out[pos] = id;
     return;
   }
+  // Three passes: a 4096-bin histogram of the hash's top 12 bits finds the bin T holding
+  // the m-th smallest; the candidates of bin T (about n / 4096) are gathered in LDS and
+  // ranked exactly; the last pass outputs every candidate below the m-th. A bin T larger
+  // than the gather buffer (not expected for uniform hashes) falls back to the radix passes.
+  if constexpr (BT >= 256) {
+    constexpr int NB2 = 4096, BPT = NB2 / BT;
+    __shared__ int hist2[NB2];
+    __shared__ int s_bin, s_below, s_cnt, s_tid;
+    __shared__ uint64_t s_th;
+    for (int i = tid; i < NB2; i += BT) hist2[i] = 0;
+    if (tid == 0) s_cnt = 0;
+    __syncthreads();
+    for (int i = tid; i < n; i += BT) {
+      const uint64_t h = splitmix64(base ^ (uint64_t)(uint32_t)cand(i));
+      atomicAdd(&hist2[(int)(h >> 52)], 1);
+    }
+    __syncthreads();
+    int loc[BPT], sum = 0;
+#pragma unroll
+    for (int q = 0; q < BPT; ++q) {
+      loc[q] = hist2[tid * BPT + q];
+      sum += loc[q];
+    }
+    int tot2;
+    const int exc = block_excl_scan<BT, int>(sum, &tot2, ws);
+    if (exc < m && exc + sum >= m) {
+      int cacc = exc;
+#pragma unroll
+      for (int q = 0; q < BPT; ++q) {
+        if (cacc < m && cacc + loc[q] >= m) {
+          s_bin = tid * BPT + q;
+          s_below = cacc;
+        }
+        cacc += loc[q];
+      }
+    }
+    __syncthreads();
+    const int T = s_bin, kk = m - s_below;
+    for (int i = tid; i < n; i += BT) {
+      const int id = cand(i);
+      const uint64_t h = splitmix64(base ^ (uint64_t)(uint32_t)id);
+      if ((int)(h >> 52) == T) {
+        const int p = atomicAdd(&s_cnt, 1);
+        if (p < BT) {
+          ch[p] = h;
+          ci[p] = id;
+        }
+      }
+    }
+    __syncthreads();
+    const int cnt = s_cnt;
+    if (cnt <= BT) {
+      if (tid < cnt) {
+        const uint64_t h = ch[tid];
+        const int id = ci[tid];
+        int rank = 0;
+        for (int j = 0; j < cnt; ++j) rank += (ch[j] < h) || (ch[j] == h && ci[j] < id);
+        if (rank == kk - 1) {
+          s_th = h;
+          s_tid = id;
+        }
+      }
+      __syncthreads();
+      const uint64_t hT = s_th;
+      const int idT = s_tid;
+      int run_sel = 0;
+      for (int c0 = 0; c0 < n; c0 += BT) {
+        const int i = c0 + tid;
+        const bool valid = i < n;
+        const int id = valid ? cand(i) : 0;
+        const uint64_t h = valid ? splitmix64(base ^ (uint64_t)(uint32_t)id) : 0ull;
+        const int bin = (int)(h >> 52);
+        const bool sel = valid && (bin < T || (bin == T && (h < hT || (h == hT && id <= idT))));
+        int sel_tot;
+        const int pos = block_excl_scan_bool<BT>(sel, &sel_tot, ws) + run_sel;
+        if (sel) out[pos] = id;
+        run_sel += sel_tot;
+      }
+      return;
+    }
+  }
   uint64_t prefix = 0;
   int k = m;
   for (int pass = 0; pass < 8; ++pass) {
@@ -1010,6 +1091,25 @@ __device__ inline f32x16 mfma_rows(const bf16* Yh, const bf16* Yl, int y0, const
 
 __device__ inline int acc_row(int v) { return 8 * (v >> 2) + 4 * (lane_id() >> 5) + (v & 3); }
 
+// The same products with the operands swapped: lane l holds row y0 + l % 32 of Y against
+// the rows acc_row(v) of the wave's x operand.
+template <int DD>
+__device__ inline f32x16 mfma_cols(const bf16* Yh, const bf16* Yl, int y0, const bf16x8* xr) {
+  constexpr int KS = DD + 8;
+  const int l32 = lane_id() & 31, h = lane_id() >> 5;
+  f32x16 acc;
+#pragma unroll
+  for (int v = 0; v < 16; ++v) acc[v] = 0.f;
+#pragma unroll
+  for (int c = 0; c < DD / 16; ++c) {
+    const bf16x8 bh = *reinterpret_cast<const bf16x8*>(&Yh[(y0 + l32) * KS + 16 * c + 8 * h]);
+    acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(xr[c], bh, acc, 0, 0, 0);
+    const bf16x8 bl = *reinterpret_cast<const bf16x8*>(&Yl[(y0 + l32) * KS + 16 * c + 8 * h]);
+    acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(xr[c], bl, acc, 0, 0, 0);
+  }
+  return acc;
+}
+
 // Assignment of iteration t for 128*RS rows: each of the 4 waves owns RS sets of 32 rows, so
 // every centroid operand read from LDS feeds RS products. Centroid operands (G m_b in
 // bf16, plus its bf16 remainder when LO) are double-buffered in LDS 64 centroids at a time:
@@ -1276,6 +1376,13 @@ __global__ __launch_bounds__(256) void k_group_mass_bf16(const bf16* q, Dims D, 
     m = mm;
   }
   const float inv = valid ? 1.f / ssum : 0.f;
+  // pass 2 with the operands swapped, so that a lane holds one centroid against 16 rows and
+  // the column sums are in-lane: the rows' max and 1 / sum come from LDS
+  __shared__ float rowm[128], rowinv[128];
+  if (lane_id() < 32) {
+    rowm[lrow] = m;
+    rowinv[lrow] = inv;
+  }
   float* part = B.mass_part + ((size_t)bh * D.max_tiles + t) * D.Ck;
   for (int c0 = 0; c0 < Ck; c0 += CB) {  // pass 2
     __syncthreads();
@@ -1283,15 +1390,19 @@ __global__ __launch_bounds__(256) void k_group_mass_bf16(const bf16* q, Dims D, 
     __syncthreads();
 #pragma unroll
     for (int yb = 0; yb < CB; yb += 32) {
-      const f32x16 acc = mfma_rows<DD>(Yh, Yl, yb, xr);
+      const f32x16 acc = mfma_cols<DD>(Yh, Yl, yb, xr);
+      const int col = c0 + yb + l32;
+      float cs = 0.f;
+      if (col < Ck) {
+        const float lgc = lg[col];
 #pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const int col = c0 + yb + acc_row(v);
-        float p = col < Ck ? expf(fmaf(D.scale, acc[v], lg[col]) - m) * inv : 0.f;
-#pragma unroll
-        for (int o = 1; o < 32; o <<= 1) p += __shfl_xor(p, o, kWave);
-        if (l32 == 0) colw[w][yb + acc_row(v)] = p;
+        for (int v = 0; v < 16; ++v) {
+          const int r = 32 * w + acc_row(v);
+          cs += expf(fmaf(D.scale, acc[v], lgc) - rowm[r]) * rowinv[r];
+        }
       }
+      cs += xor32(cs);
+      if (lane_id() < 32) colw[w][yb + l32] = cs;
     }
     __syncthreads();
     if (tid < CB && c0 + tid < Ck) part[c0 + tid] = ((colw[0][tid] + colw[1][tid]) + colw[2][tid]) + colw[3][tid];
@@ -1489,13 +1600,14 @@ __global__ __launch_bounds__(1024) void k_route_sort(Dims D, Bufs B) {
   }
 }
 
-__device__ inline int route_take(const long long* cum, int Ck, long long tau) {
-  int lo = 0, hi = Ck;  // first index with cum >= tau
+// First index in [lo, hi] whose prefix mass reaches tau (hi = Ck: none); the caller knows the
+// answer lies in [lo, hi] (the index is monotone in tau).
+__device__ inline int route_first(const long long* cum, long long tau, int lo, int hi) {
   while (lo < hi) {
     const int mid = (lo + hi) >> 1;
     if (cum[mid] >= tau) hi = mid; else lo = mid + 1;
   }
-  return min(max(lo + 1, 1), Ck);
+  return lo;
 }
 
 __global__ __launch_bounds__(1024) void k_route_tau(Dims D, Bufs B) {
@@ -1506,27 +1618,42 @@ __global__ __launch_bounds__(1024) void k_route_tau(Dims D, Bufs B) {
   const size_t ro = ((size_t)bh * D.Cq + a) * D.Ck;
   const long long* cum = B.cum + ro;
   const long long* cc = B.ccost + ro;
-  auto cost = [&](long long tau) -> long long {
-    const long long c = a < Cq ? cc[route_take(cum, Ck, tau) - 1] : 0;
+  // cost(tau) = sum over rows of the pair cost of the shortest prefix reaching tau (at least
+  // one group). Bisection on tau; each row keeps the index range its answer is known to lie
+  // in (the answers at the current lo and hi), so its search shrinks with the interval.
+  auto take = [&](int f) { return min(max(f + 1, 1), Ck); };
+  auto cost_of = [&](int f) -> long long {
+    const long long c = a < Cq ? cc[take(f) - 1] : 0;
     return block_sum<1024, long long>(c, ws);
   };
   const long long budget = D.budget;
   long long hi = (1ll << 32) + Ck, tau;
-  int exceeded = 0;
-  if (cost(0) > budget) {
+  int flo = 0, fhi = a < Cq ? route_first(cum, hi, 0, Ck) : 0;  // cum >= 0: f(0) = 0
+  int exceeded = 0, fsel;
+  if (cost_of(flo) > budget) {
     tau = 0;
     exceeded = 1;
-  } else if (cost(hi) <= budget) {
+    fsel = flo;
+  } else if (cost_of(fhi) <= budget) {
     tau = hi;
+    fsel = fhi;
   } else {
     long long lo = 0;
     while (hi - lo > 1) {
       const long long mid = (lo + hi) >> 1;
-      if (cost(mid) <= budget) lo = mid; else hi = mid;
+      const int fm = a < Cq ? route_first(cum, mid, flo, fhi) : 0;
+      if (cost_of(fm) <= budget) {
+        lo = mid;
+        flo = fm;
+      } else {
+        hi = mid;
+        fhi = fm;
+      }
     }
     tau = lo;
+    fsel = flo;
   }
-  const int j = a < Cq ? route_take(cum, Ck, tau) : 0;
+  const int j = a < Cq ? take(fsel) : 0;
   const long long pc = a < Cq ? cc[j - 1] : 0;
   const long long pairs = block_sum<1024, long long>(pc, ws);
   int tot;
