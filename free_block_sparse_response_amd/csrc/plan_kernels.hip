@@ -1571,21 +1571,20 @@ __global__ __launch_bounds__(1024) void k_route_sort(Dims D, Bufs B) {
   if (a >= Cq) return;
   const int tid = threadIdx.x;
   const long long* u = B.u + ((size_t)bh * D.Cq + a) * D.Ck;
+  // order by (-u, b): each key group's rank is the number of keys below its own (distinct
+  // keys: the group id is in the low bits); every thread reads the same key at a time
+  __shared__ int order[kMaxGroups];
   key[tid] = tid < Ck ? ((((1ull << 34) - 1ull - (unsigned long long)u[tid]) << 10) | (unsigned)tid) : ~0ull;
   __syncthreads();
-  for (int size = 2; size <= kMaxGroups; size <<= 1) {
-    for (int stride = size >> 1; stride > 0; stride >>= 1) {
-      const int p = tid ^ stride;
-      if (p > tid) {
-        const bool up = (tid & size) == 0;
-        const unsigned long long x = key[tid], y = key[p];
-        if ((x > y) == up) { key[tid] = y; key[p] = x; }
-      }
-      __syncthreads();
-    }
+  if (tid < Ck) {
+    const unsigned long long kv = key[tid];
+    int rank = 0;
+    for (int j = 0; j < Ck; ++j) rank += key[j] < kv;
+    order[rank] = tid;
   }
+  __syncthreads();
   const int* ko = B.koff + (size_t)bh * (D.Ck + 1);
-  const int b = (int)(key[tid] & 1023ull);
+  const int b = tid < Ck ? order[tid] : 0;
   const long long mass = tid < Ck ? u[b] : 0;
   const long long nk = tid < Ck ? (long long)(ko[b + 1] - ko[b]) : 0;
   long long t1, t2;
