@@ -5,7 +5,7 @@ One step = one whole call (plan: key and query k-means, masses, routing, probes;
 permutation, block-sparse attention, probe attention; ridge fit; apply) over all heads of
 the workload, on seeded synthetic inputs already resident in HBM. Prints ONE JSON line.
 
-  python bench.py [--steps K] [--warmup W] [--config c2] [--no-cpu-baseline]
+  python bench.py [--steps K] [--warmup W] [--config c2] [--density RHO] [--no-cpu-baseline]
   python bench.py --copy-calibration      # plain device copy of a known size (for PMC scaling)
 """
 from __future__ import annotations
@@ -59,6 +59,8 @@ def parse():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--config", default="c2")
+    ap.add_argument("--density", type=float, default=None,
+                    help="override the workload's executed-pair density (the stress workload's sweep)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-heads", type=int, default=2)
     ap.add_argument("--copy-calibration", action="store_true")
@@ -114,7 +116,9 @@ def main():
     from free_block_sparse_response_amd import configs, synth
     from free_block_sparse_response_amd.call import SparsePR, config_from_workload
 
-    w = configs.CONFIGS[args.config]
+    w = dict(configs.CONFIGS[args.config])
+    if args.density is not None:
+        w["density"] = args.density
     N, d, BH, M = configs.seq_len(w), w["head_dim"], w["batch"] * w["heads"], w["n_probes"]
     dev = torch.device("cuda:0")
     t0 = time.perf_counter()
@@ -204,7 +208,7 @@ def main():
     roofline = {"kernel": "k_bsfa_bf16 (block-sparse attention)" if w["dtype"] == "bf16" else "k_bsfa_f32",
                 "bound": "mfma" if w["dtype"] == "bf16" else "alu", "achieved": round(bsfa_tflops, 2),
                 "peak": BF16_MFMA_PEAK_TFLOPS if w["dtype"] == "bf16" else FP32_VECTOR_PEAK_TFLOPS,
-                "unit": "TFLOP/s", "frac": None, "traffic": recorded_traffic(args.config),
+                "unit": "TFLOP/s", "frac": None, "traffic": recorded_traffic(args.config) if args.density is None else None,
                 "flop_per_launch": bsfa_flop, "ms_per_launch": round(bsfa_ms, 4)}
     roofline["frac"] = round(roofline["achieved"] / roofline["peak"], 4)
     probe_flop = 4.0 * d * M * N * BH

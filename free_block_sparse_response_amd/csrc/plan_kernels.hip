@@ -1113,9 +1113,12 @@ __device__ inline f32x16 mfma_cols(const bf16* Yh, const bf16* Yl, int y0, const
 // Assignment of iteration t for 128*RS rows: each of the 4 waves owns RS sets of 32 rows, so
 // every centroid operand read from LDS feeds RS products. Centroid operands (G m_b in
 // bf16, plus its bf16 remainder when LO) are double-buffered in LDS 64 centroids at a time:
-// the next chunk's global loads are issued before the current chunk's products.
+// the next chunk's global loads are issued before the current chunk's products. The plan
+// runs RS = 1 (three waves per SIMD keep more row loads in flight) and RS = 2 with the
+// remainder operand.
 template <int DD, int RS, bool LO>
-__global__ __launch_bounds__(256, 2) void k_km_assign_bf16(const bf16* x, Dims D, Bufs B, int C, KmState* st, int t) {
+__global__ __launch_bounds__(256, RS == 1 ? 3 : 2) void k_km_assign_bf16(const bf16* x, Dims D, Bufs B, int C,
+                                                                           KmState* st, int t) {
   constexpr int CB = 64, KS = DD + 8, NB = kKmRows * RS;
   constexpr int NL = CB * DD / 8 / 256;  // 16-byte loads per thread per chunk and operand
   constexpr int NO = LO ? 2 : 1;
@@ -1190,10 +1193,10 @@ __global__ __launch_bounds__(256, 2) void k_km_assign_bf16(const bf16* x, Dims D
       f32x16 acc[RS], cinit[RS];
 #pragma unroll
       for (int rs = 0; rs < RS; ++rs) {
-        // with the remainder operand the registers are short: the start block is rebuilt
-        // per centroid block instead of being kept
+        // with the remainder operand, or one row set per wave (kept under 168 registers for
+        // three waves per SIMD), the start block is rebuilt per centroid block instead of kept
         float iv = ini[rs];
-        if (LO) asm volatile("" : "+v"(iv));
+        if (LO || RS == 1) asm volatile("" : "+v"(iv));
 #pragma unroll
         for (int v = 0; v < 16; ++v) cinit[rs][v] = iv;
       }
@@ -1861,7 +1864,7 @@ static void lloyd_iterations(const T* x, const Dims& D, const Bufs& B, int C, Km
         hipLaunchKernelGGL((k_km_assign_bf16<DD, 2, true>), dim3((D.nblk + 1) / 2, D.BH), dim3(256), 0, s, x, D, B, C,
                            st, t);
       else
-        hipLaunchKernelGGL((k_km_assign_bf16<DD, 2, false>), dim3((D.nblk + 1) / 2, D.BH), dim3(256), 0, s, x, D, B, C,
+        hipLaunchKernelGGL((k_km_assign_bf16<DD, 1, false>), dim3(D.nblk, D.BH), dim3(256), 0, s, x, D, B, C,
                            st, t);
     else
       hipLaunchKernelGGL((k_km_assign<T, DD>), dim3(D.nblk, D.BH), dim3(256), 0, s, x, D, B, C, st, t);
