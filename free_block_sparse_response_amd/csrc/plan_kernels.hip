@@ -792,9 +792,32 @@ __global__ __launch_bounds__(256) void k_km_update(const T* x, Dims D, Bufs B, K
   __shared__ int go;
   const int b = blockIdx.x, bh = blockIdx.y, tid = threadIdx.x;
   if (st[bh].done_iter < t) return;
+  // Independent loads first, so that their latencies overlap: the metric (for G m), the
+  // first window of the group's per-block counts, and (wave 0) the inertia partials, read 8
+  // at a time per lane and summed in the fixed order.
+  const float* G = B.metric + (size_t)bh * DD * DD;
+  constexpr int KH = 256 / DD;
+  const int i = tid % DD, part = tid / DD;
+  float gv[DD / KH];
+#pragma unroll
+  for (int kk = 0; kk < DD / KH; ++kk) gv[kk] = G[(size_t)(part + kk * KH) * DD + i];
+  const int* tab = B.tab + ((size_t)bh * D.C + b) * D.nblk;
+  int tv0[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int j = 4 * tid + q;
+    tv0[q] = j < D.nblk ? tab[j] : 0;
+  }
   if (tid < kWave) {
+    const double* ip = B.ipart + (size_t)bh * D.nblk;
     double sum = 0.0;
-    for (int i = tid; i < D.nblk; i += kWave) sum += B.ipart[(size_t)bh * D.nblk + i];
+    for (int i0 = tid; i0 < D.nblk; i0 += 8 * kWave) {
+      double pv[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) pv[u] = i0 + u * kWave < D.nblk ? ip[i0 + u * kWave] : 0.0;
+#pragma unroll
+      for (int u = 0; u < 8; ++u) sum += pv[u];
+    }
     sum = wave_sum(sum);
     if (tid == 0) {
       const double prev = st[bh].inertia[(t - 1) & 1];
@@ -811,15 +834,6 @@ __global__ __launch_bounds__(256) void k_km_update(const T* x, Dims D, Bufs B, K
   if (!go) return;
   const T* xb = x + (size_t)bh * D.N * DD;
   const float* alpha = B.alpha ? B.alpha + (size_t)bh * D.N : nullptr;
-  // G m: threads i and i + DD (, ...) take interleaved parts of k; combined in order. The
-  // metric's loads are issued before the gather so that the two latencies overlap.
-  const float* G = B.metric + (size_t)bh * DD * DD;
-  constexpr int KH = 256 / DD;
-  const int i = tid % DD, part = tid / DD;
-  float gv[DD / KH];
-#pragma unroll
-  for (int kk = 0; kk < DD / KH; ++kk) gv[kk] = G[(size_t)(part + kk * KH) * DD + i];
-  const int* tab = B.tab + ((size_t)bh * D.C + b) * D.nblk;
   const int* lp = B.lperm + (size_t)bh * D.N;
   const int slot = tid / LPR, c0 = (tid % LPR) * EV;
   float acc[EV];
@@ -837,7 +851,7 @@ __global__ __launch_bounds__(256) void k_km_update(const T* x, Dims D, Bufs B, K
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       const int j = j0 + 4 * tid + q;
-      const int v = j < D.nblk ? tab[j] : 0;
+      const int v = j0 == 0 ? tv0[q] : (j < D.nblk ? tab[j] : 0);
       cq[q] = v & 255;
       wbeg[4 * tid + q] = j * kKmRows + (v >> 8);
       run += cq[q];
@@ -1347,9 +1361,10 @@ __global__ __launch_bounds__(256) void k_group_mass_bf16(const bf16* q, Dims D, 
   load_row_operand<DD>(q + ((size_t)bh * D.N + tok) * DD, xr);
   const int Ck = B.kst[bh].c_final;
   const int* ko = B.koff + (size_t)bh * (D.Ck + 1);
-  for (int b = tid; b < Ck; b += 256) lg[b] = logf((float)(ko[b + 1] - ko[b]));
+  for (int b = tid; b < Ck; b += 256) lg[b] = log2f((float)(ko[b + 1] - ko[b]));  // log2 domain
   const bf16* Kh = B.kcent_h + (size_t)bh * D.Ck * DD;
   const bf16* Kl = B.kcent_l + (size_t)bh * D.Ck * DD;
+  const float sc2 = D.scale * 1.4426950408889634f;  // logits in the log2 domain
   float m = -INFINITY, ssum = 0.f;
   for (int c0 = 0; c0 < Ck; c0 += CB) {  // pass 1
     __syncthreads();
@@ -1362,20 +1377,20 @@ __global__ __launch_bounds__(256) void k_group_mass_bf16(const bf16* q, Dims D, 
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
         const int col = c0 + yb + acc_row(v);
-        z[v] = col < Ck ? fmaf(D.scale, acc[v], lg[col]) : -INFINITY;
+        z[v] = col < Ck ? fmaf(sc2, acc[v], lg[col]) : -INFINITY;
         mx = fmaxf(mx, z[v]);
       }
       float add = 0.f;
 #pragma unroll
-      for (int v = 0; v < 16; ++v) add += expf(z[v] - mx);
-      ssum = ssum * expf(m - mx) + add;
+      for (int v = 0; v < 16; ++v) add += __builtin_amdgcn_exp2f(z[v] - mx);
+      ssum = ssum * __builtin_amdgcn_exp2f(m - mx) + add;
       m = mx;
     }
   }
   {
     const float mo = __shfl_xor(m, 32, kWave), so = __shfl_xor(ssum, 32, kWave);
     const float mm = fmaxf(m, mo);
-    ssum = ssum * expf(m - mm) + so * expf(mo - mm);
+    ssum = ssum * __builtin_amdgcn_exp2f(m - mm) + so * __builtin_amdgcn_exp2f(mo - mm);
     m = mm;
   }
   const float inv = valid ? 1.f / ssum : 0.f;
@@ -1401,7 +1416,7 @@ __global__ __launch_bounds__(256) void k_group_mass_bf16(const bf16* q, Dims D, 
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
           const int r = 32 * w + acc_row(v);
-          cs += expf(fmaf(D.scale, acc[v], lgc) - rowm[r]) * rowinv[r];
+          cs += __builtin_amdgcn_exp2f(fmaf(sc2, acc[v], lgc) - rowm[r]) * rowinv[r];
         }
       }
       cs += xor32(cs);
