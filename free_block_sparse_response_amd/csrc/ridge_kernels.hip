@@ -430,8 +430,23 @@ __global__ __launch_bounds__(256) void k_apply_bf16(Dims D, Bufs B, const bf16* 
     }
 #pragma unroll
     for (int rs = 0; rs < RS; ++rs) {
+      // o's own entries for the output layout (dims jb + 8 g + 4 h + r) come from the operand
+      // registers: the 16 dims of chunk c sit 8 per lane half, and swapping dwords 0, 1 of
+      // the upper half with dwords 2, 3 of the lower one gives each lane its two runs of 4
+      uint32_t xo[2][4];
+#pragma unroll
+      for (int q = 0; q < 2; ++q) {
+        const bf16x8 xc = xr[rs][jb / 16 + q];
+        uint32_t dw[4];
+        __builtin_memcpy(dw, &xc, 16);
+        const auto s02 = __builtin_amdgcn_permlane32_swap(dw[0], dw[2], false, false);
+        const auto s13 = __builtin_amdgcn_permlane32_swap(dw[1], dw[3], false, false);
+        xo[q][0] = s02[0];
+        xo[q][1] = s13[0];
+        xo[q][2] = s02[1];
+        xo[q][3] = s13[1];
+      }
       if (row[rs] >= D.N) continue;
-      const bf16* orow = o_sp + ((size_t)bh * D.N + row[rs]) * DD;
       bf16* dst = out + ((size_t)bh * D.N + row[rs]) * DD;
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
@@ -441,7 +456,9 @@ __global__ __launch_bounds__(256) void k_apply_bf16(Dims D, Bufs B, const bf16* 
           const float4 dv = *reinterpret_cast<const float4*>(o_dn + ((size_t)bh * D.M + slot[rs]) * DD + j);
           ov[0] = (bf16)dv.x; ov[1] = (bf16)dv.y; ov[2] = (bf16)dv.z; ov[3] = (bf16)dv.w;
         } else {
-          const bf16x4 xv = *reinterpret_cast<const bf16x4*>(orow + j);
+          bf16x4 xv;
+          const uint32_t pr[2] = {xo[g >> 1][2 * (g & 1)], xo[g >> 1][2 * (g & 1) + 1]};
+          __builtin_memcpy(&xv, pr, 8);
 #pragma unroll
           for (int r = 0; r < 4; ++r) ov[r] = (bf16)((float)xv[r] + acc[rs][4 * g + r] + bias[j + r]);
         }
