@@ -502,9 +502,9 @@ __device__ void km_init_item(const T* x, const Dims& D, const Bufs& B, int C, co
     const size_t o = ((size_t)bh * D.C + b) * DD + i;
     B.cent[o] = v;
     B.cent_t[o] = t;
-    const bf16 th = (bf16)t;
+    const bf16 th = (bf16)(-2.f * t);  // the assignment's operand: -2 G m_b, hi / lo
     B.cent_h[o] = th;
-    B.cent_l[o] = (bf16)(t - (float)th);
+    B.cent_l[o] = (bf16)(-2.f * t - (float)th);
     p = v * t;
   }
   p = wave_sum(p);
@@ -920,9 +920,9 @@ __global__ __launch_bounds__(256) void k_km_update(const T* x, Dims D, Bufs B, K
       const size_t o = ((size_t)bh * D.C + b) * DD + i;
       B.cent[o] = m[i];
       B.cent_t[o] = tot;
-      const bf16 th = (bf16)tot;
+      const bf16 th = (bf16)(-2.f * tot);  // the assignment's operand: -2 G m_b, hi / lo
       B.cent_h[o] = th;
-      B.cent_l[o] = (bf16)(tot - (float)th);
+      B.cent_l[o] = (bf16)(-2.f * tot - (float)th);
       p = m[i] * tot;
     }
   }
@@ -959,9 +959,9 @@ __global__ __launch_bounds__(256) void k_km_warm_init(Dims D, Bufs B, const floa
     const size_t o = ((size_t)bh * D.C + b) * DD + i;
     B.cent[o] = m[i];
     B.cent_t[o] = t;
-    const bf16 th = (bf16)t;
+    const bf16 th = (bf16)(-2.f * t);  // the assignment's operand: -2 G m_b, hi / lo
     B.cent_h[o] = th;
-    B.cent_l[o] = (bf16)(t - (float)th);
+    B.cent_l[o] = (bf16)(-2.f * t - (float)th);
     p = m[i] * t;
   }
   p = wave_sum(p);
@@ -1148,21 +1148,44 @@ __global__ __launch_bounds__(256, RS == 1 ? 3 : 2) void k_km_assign_bf16(const b
   const int tid = threadIdx.x, w = tid / kWave, l32 = lane_id() & 31, h = lane_id() >> 5;
   const int r0 = sb0 * kKmRows;
   bf16x8 xr[RS][DD / 16];
-  // The products start from -rc / a2 (rc = alpha^2 x G x, the row constant), so that
-  // cn_b - a2 acc is the squared distance itself, >= 0 up to rounding. A distance's float
-  // bits then order like integers; its low 10 bits are replaced by the centroid index (the
-  // part shared by both lane halves), and one integer min per pair of candidates keeps the
-  // nearest, the lower index among distances equal in the kept bits.
-  float a2[RS], ini[RS];
+  // Every product is the squared distance divided by the row's scale alpha (> 0), whose
+  // argmin is the nearest centroid: d / alpha = x . (-2 G m_b) + m_b G m_b / alpha + rc / alpha
+  // (rc = alpha^2 x G x, the row constant). The first term is the main products (the
+  // centroid operand holds -2 G m_b); the other two come from one more product per 32
+  // centroids, of k-slots [cn_hi, cn_hi, cn_lo, 1, 1] (centroid side) and [ia_hi, ia_lo,
+  // ia_hi, rca_hi, rca_lo] (row side, ia = 1 / alpha, rca = rc / alpha, bf16 hi / lo pairs),
+  // so no vector op touches a product. The value is >= 0 up to rounding, so its float bits
+  // order like integers; the low 10 bits are replaced by the centroid index (the part shared
+  // by both lane halves), and one integer min per pair of candidates keeps the nearest, the
+  // lower index among distances equal in the kept bits. A row with alpha = 0 (its features
+  // are 0) takes a zero operand and scale 1: its value is m_b G m_b.
+  float sca[RS];  // alpha (1 for a zero row), to turn the kept value back into a distance
   int bkey[RS];
+  bf16x8 brow[RS];
 #pragma unroll
   for (int rs = 0; rs < RS; ++rs) {
     const int row = r0 + 128 * rs + 32 * w + l32;
     const bool valid = row < D.N;
     load_row_operand<DD>(x + ((size_t)bh * D.N + (valid ? row : D.N - 1)) * DD, xr[rs]);
-    a2[rs] = 2.f * (B.alpha ? B.alpha[(size_t)bh * D.N + (valid ? row : 0)] : 1.f);
+    const float al = B.alpha ? B.alpha[(size_t)bh * D.N + (valid ? row : 0)] : 1.f;
     const float rc = B.rowconst[(size_t)bh * D.N + (valid ? row : 0)];
-    ini[rs] = a2[rs] > 0.f ? -rc / a2[rs] : 0.f;
+    const bool zero = !(al > 0.f);
+    if (zero) {
+#pragma unroll
+      for (int c = 0; c < DD / 16; ++c) xr[rs][c] = bf16x8{};
+    }
+    const float ia = zero ? 1.f : 1.f / al, rca = zero ? 0.f : rc / al;
+    sca[rs] = zero ? 1.f : al;
+    const bf16 iah = (bf16)ia, rch = (bf16)rca;
+    const bf16 ial = (bf16)(ia - (float)iah), rcl = (bf16)(rca - (float)rch);
+    brow[rs] = bf16x8{};
+    if (h == 0) {
+      brow[rs][0] = iah;
+      brow[rs][1] = ial;
+      brow[rs][2] = iah;
+      brow[rs][3] = rch;
+      brow[rs][4] = rcl;
+    }
     bkey[rs] = 0x7fffffff;
   }
   const bf16* Cop[2] = {B.cent_h + (size_t)bh * D.C * DD, B.cent_l + (size_t)bh * D.C * DD};
@@ -1204,15 +1227,24 @@ __global__ __launch_bounds__(256, RS == 1 ? 3 : 2) void k_km_assign_bf16(const b
     if (more) load_chunk(c0 + CB);
 #pragma unroll
     for (int yb = 0; yb < CB; yb += 32) {
-      f32x16 acc[RS], cinit[RS];
+      // the centroid side of the bias product; a centroid past the last one has cn = +inf and
+      // takes [+inf, 0, ...], so its value is +inf (no inf x 0 product)
+      bf16x8 bcen = bf16x8{};
+      if (h == 0) {
+        const float cv = cns[cur][yb + l32];
+        const bf16 cvh = (bf16)cv;
+        const bool fin = cv < INFINITY;
+        bcen[0] = cvh;
+        bcen[1] = fin ? cvh : (bf16)0.f;
+        bcen[2] = fin ? (bf16)(cv - (float)cvh) : (bf16)0.f;
+        bcen[3] = fin ? (bf16)1.f : (bf16)0.f;
+        bcen[4] = bcen[3];
+      }
+      f32x16 acc[RS];
 #pragma unroll
       for (int rs = 0; rs < RS; ++rs) {
-        // with the remainder operand, or one row set per wave (kept under 168 registers for
-        // three waves per SIMD), the start block is rebuilt per centroid block instead of kept
-        float iv = ini[rs];
-        if (LO || RS == 1) asm volatile("" : "+v"(iv));
-#pragma unroll
-        for (int v = 0; v < 16; ++v) cinit[rs][v] = iv;
+        const f32x16 z = {};
+        acc[rs] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bcen, brow[rs], z, 0, 0, 0);
       }
 #pragma unroll
       for (int c = 0; c < DD / 16; ++c) {
@@ -1221,11 +1253,10 @@ __global__ __launch_bounds__(256, RS == 1 ? 3 : 2) void k_km_assign_bf16(const b
           const bf16x8 av = *reinterpret_cast<const bf16x8*>(&Y[cur][o][(yb + l32) * KS + 16 * c + 8 * h]);
 #pragma unroll
           for (int rs = 0; rs < RS; ++rs)
-            acc[rs] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, xr[rs][c], c == 0 && o == 0 ? cinit[rs] : acc[rs],
-                                                              0, 0, 0);
+            acc[rs] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, xr[rs][c], acc[rs], 0, 0, 0);
         }
       }
-      // Candidate key = distance bits with the low 10 replaced by c0 + yb + 8 (v / 4) + v % 4
+      // Candidate key = value bits with the low 10 replaced by c0 + yb + 8 (v / 4) + v % 4
       // (the index without the lane-half offset 4 h, which the merge of the halves restores).
       // (a bit-field insert per candidate: the mask is kept in a register)
       int im = 1023;
@@ -1234,11 +1265,9 @@ __global__ __launch_bounds__(256, RS == 1 ? 3 : 2) void k_km_assign_bf16(const b
       for (int rs = 0; rs < RS; ++rs)
 #pragma unroll
         for (int v = 0; v < 16; v += 2) {
-          const float d0 = fmaf(-a2[rs], acc[rs][v], cns[cur][yb + acc_row(v)]);
-          const float d1 = fmaf(-a2[rs], acc[rs][v + 1], cns[cur][yb + acc_row(v + 1)]);
           const int i0 = c0 + yb + 8 * (v >> 2) + (v & 3), i1 = i0 + 1;
-          const int k0 = (__float_as_int(d0) & ~im) | (i0 & im);
-          const int k1 = (__float_as_int(d1) & ~im) | (i1 & im);
+          const int k0 = (__float_as_int(acc[rs][v]) & ~im) | (i0 & im);
+          const int k1 = (__float_as_int(acc[rs][v + 1]) & ~im) | (i1 & im);
           bkey[rs] = min(min(bkey[rs], k0), k1);
         }
     }
@@ -1258,7 +1287,7 @@ __global__ __launch_bounds__(256, RS == 1 ? 3 : 2) void k_km_assign_bf16(const b
     const int wk = min(ok, myk);
     const int wh = ok < myk ? (h ^ 1) : (ok == myk ? 0 : h);
     const int bidx = (wk & 1023) + 4 * wh;
-    const float bestd = __int_as_float(wk & ~1023);
+    const float bestd = sca[rs] * __int_as_float(wk & ~1023);  // the squared distance
     const int row = r0 + 128 * rs + 32 * w + l32;
     const bool valid = h == 0 && row < D.N;
     lab[rs] = valid ? bidx : 0;
