@@ -75,6 +75,26 @@ __device__ V block_sum(V v, V* ws) {
   return t;
 }
 
+// The centroid side of the Lloyd assignment's bias product for cn = m_b G m_b (see
+// k_km_assign_bf16): k-slots [cn_hi, cn_hi, cn_lo, 1, 1] and zeros (16 slots, 32 bytes), so
+// that its product with the row side [1/alpha hi, lo, hi, rc/alpha hi, lo] is
+// cn / alpha + rc / alpha. A dead centroid (cn = +inf) takes [+inf, 0, ...]: its value is
+// +inf, with no inf x 0 term.
+__device__ inline void store_bias_operand(bf16* dst, float cn) {
+  const bf16 hi = (bf16)cn;
+  const bool fin = cn < INFINITY;
+  bf16x8 v = bf16x8{};
+  v[0] = hi;
+  if (fin) {
+    v[1] = hi;
+    v[2] = (bf16)(cn - (float)hi);
+    v[3] = (bf16)1.f;
+    v[4] = (bf16)1.f;
+  }
+  reinterpret_cast<bf16x8*>(dst)[0] = v;
+  reinterpret_cast<bf16x8*>(dst)[1] = bf16x8{};
+}
+
 // =====================================================================================
 // Selection of the m candidates with the smallest (hash, id), output in ascending id
 // order. Candidates are cand(0..n-1), ascending. Radix select over the 64-bit hash
@@ -514,6 +534,7 @@ __device__ void km_init_item(const T* x, const Dims& D, const Bufs& B, int C, co
     float sum = 0.f;
     for (int w = 0; w < DD / kWave; ++w) sum += red[w];
     B.cnorm[(size_t)bh * D.C + b] = sum;
+    store_bias_operand(B.cent_b + ((size_t)bh * D.C + b) * 16, sum);
     if (b == 0) {
       st[bh].done_iter = 0x7fffffff;
       st[bh].iters = 0;
@@ -933,6 +954,7 @@ __global__ __launch_bounds__(256) void k_km_update(const T* x, Dims D, Bufs B, K
     float sum = 0.f;
     for (int w = 0; w < DD / kWave; ++w) sum += red[w];
     B.cnorm[(size_t)bh * D.C + b] = sum;
+    store_bias_operand(B.cent_b + ((size_t)bh * D.C + b) * 16, sum);
   }
 }
 
@@ -971,6 +993,7 @@ __global__ __launch_bounds__(256) void k_km_warm_init(Dims D, Bufs B, const floa
     float sum = 0.f;
     for (int w = 0; w < DD / kWave; ++w) sum += red[w];
     B.cnorm[(size_t)bh * D.C + b] = live ? sum : INFINITY;
+    store_bias_operand(B.cent_b + ((size_t)bh * D.C + b) * 16, live ? sum : INFINITY);
   }
 }
 
@@ -1125,13 +1148,13 @@ __device__ inline f32x16 mfma_cols(const bf16* Yh, const bf16* Yl, int y0, const
 }
 
 // Assignment of iteration t for 128*RS rows: each of the 4 waves owns RS sets of 32 rows, so
-// every centroid operand read from LDS feeds RS products. Centroid operands (G m_b in
-// bf16, plus its bf16 remainder when LO) are double-buffered in LDS 64 centroids at a time:
-// the next chunk's global loads are issued before the current chunk's products. The plan
-// runs RS = 1 (three waves per SIMD keep more row loads in flight) up to 256 centroids, and
-// RS = 2 (half the LDS operand reads per product) beyond that and with the remainder operand.
+// every centroid operand read from LDS feeds RS products. Centroid operands (-2 G m_b in
+// bf16, plus its bf16 remainder when LO, and the bias operands) are double-buffered in LDS 64
+// centroids at a time: the next chunk's global loads are issued before the current chunk's
+// products. The plan runs RS = 1 (four waves per SIMD) up to 256 centroids, and RS = 2 (half
+// the LDS operand reads per product) beyond that and with the remainder operand.
 template <int DD, int RS, bool LO>
-__global__ __launch_bounds__(256, RS == 1 ? 3 : 2) void k_km_assign_bf16(const bf16* x, Dims D, Bufs B, int C,
+__global__ __launch_bounds__(256, RS == 1 ? 4 : 2) void k_km_assign_bf16(const bf16* x, Dims D, Bufs B, int C,
                                                                            KmState* st, int t) {
   constexpr int CB = 64, KS = DD + 8, NB = kKmRows * RS;
   constexpr int NL = CB * DD / 8 / 256;  // 16-byte loads per thread per chunk and operand
@@ -1141,7 +1164,7 @@ __global__ __launch_bounds__(256, RS == 1 ? 3 : 2) void k_km_assign_bf16(const b
   __shared__ __attribute__((aligned(16))) char smem[YB > CNB ? YB : CNB];
   auto Y = reinterpret_cast<bf16(*)[NO][CB * KS]>(smem);
   auto cnt = reinterpret_cast<int(*)[4][kMaxGroups]>(smem);
-  __shared__ float cns[2][CB];
+  __shared__ __attribute__((aligned(16))) bf16 Bs[2][CB * 16];  // bias operands of the chunk
   __shared__ double wpart[RS][4];
   const int sb0 = blockIdx.x * RS, bh = blockIdx.y;  // first 128-row sort block
   if (st[bh].done_iter < t) return;
@@ -1189,24 +1212,25 @@ __global__ __launch_bounds__(256, RS == 1 ? 3 : 2) void k_km_assign_bf16(const b
     bkey[rs] = 0x7fffffff;
   }
   const bf16* Cop[2] = {B.cent_h + (size_t)bh * D.C * DD, B.cent_l + (size_t)bh * D.C * DD};
-  const float* cn = B.cnorm + (size_t)bh * D.C;
-  bf16x8 pre[NO][NL];
-  float pcn = 0.f;
+  const bf16* Cb = B.cent_b + (size_t)bh * D.C * 16;
+  bf16x8 pre[NO][NL], pb;
+  // Centroids past the last one (the tail of the last chunk) re-read the last centroid's
+  // operand, so every load is unconditional; their bias operand is [+inf, 0, ...], which makes
+  // their value +inf, and they never win.
   auto load_chunk = [&](int c0) {
 #pragma unroll
     for (int o = 0; o < NO; ++o)
 #pragma unroll
       for (int i = 0; i < NL; ++i) {
         const int e = tid + 256 * i, r = e / (DD / 8), c8 = (e % (DD / 8)) * 8;
-        if (c0 + r < C) {
-          pre[o][i] = *reinterpret_cast<const bf16x8*>(Cop[o] + (size_t)(c0 + r) * DD + c8);
-        } else {
-#pragma unroll
-          for (int q = 0; q < 8; ++q) pre[o][i][q] = (bf16)0.f;
-        }
+        pre[o][i] = *reinterpret_cast<const bf16x8*>(Cop[o] + (size_t)min(c0 + r, C - 1) * DD + c8);
       }
-    // a centroid past the last one scores +inf and never wins the strict comparison below
-    pcn = (tid < CB && c0 + tid < C) ? cn[c0 + tid] : INFINITY;
+    // threads 0 .. 2 CB - 1: half tid % 2 of the bias operand of centroid c0 + tid / 2
+    pb = *reinterpret_cast<const bf16x8*>(Cb + (size_t)min(c0 + (tid & (2 * CB - 1)) / 2, C - 1) * 16 + 8 * (tid & 1));
+    if (c0 + (tid & (2 * CB - 1)) / 2 >= C) {
+      pb = bf16x8{};
+      if ((tid & 1) == 0) pb[0] = (bf16)INFINITY;
+    }
   };
   auto store_chunk = [&](int buf) {
 #pragma unroll
@@ -1216,7 +1240,7 @@ __global__ __launch_bounds__(256, RS == 1 ? 3 : 2) void k_km_assign_bf16(const b
         const int e = tid + 256 * i, r = e / (DD / 8), c8 = (e % (DD / 8)) * 8;
         *reinterpret_cast<bf16x8*>(&Y[buf][o][r * KS + c8]) = pre[o][i];
       }
-    if (tid < CB) cns[buf][tid] = pcn;
+    if (tid < 2 * CB) *reinterpret_cast<bf16x8*>(&Bs[buf][8 * tid]) = pb;
   };
   load_chunk(0);
   store_chunk(0);
@@ -1227,19 +1251,8 @@ __global__ __launch_bounds__(256, RS == 1 ? 3 : 2) void k_km_assign_bf16(const b
     if (more) load_chunk(c0 + CB);
 #pragma unroll
     for (int yb = 0; yb < CB; yb += 32) {
-      // the centroid side of the bias product; a centroid past the last one has cn = +inf and
-      // takes [+inf, 0, ...], so its value is +inf (no inf x 0 product)
-      bf16x8 bcen = bf16x8{};
-      if (h == 0) {
-        const float cv = cns[cur][yb + l32];
-        const bf16 cvh = (bf16)cv;
-        const bool fin = cv < INFINITY;
-        bcen[0] = cvh;
-        bcen[1] = fin ? cvh : (bf16)0.f;
-        bcen[2] = fin ? (bf16)(cv - (float)cvh) : (bf16)0.f;
-        bcen[3] = fin ? (bf16)1.f : (bf16)0.f;
-        bcen[4] = bcen[3];
-      }
+      // the centroid side of the bias product (k-slots 8 h .. 8 h + 7 of the 16)
+      const bf16x8 bcen = *reinterpret_cast<const bf16x8*>(&Bs[cur][(yb + l32) * 16 + 8 * h]);
       f32x16 acc[RS];
 #pragma unroll
       for (int rs = 0; rs < RS; ++rs) {

@@ -64,6 +64,7 @@ struct Bufs {
   float* cnorm;      // [BH][C]    m_b G m_b
   bf16* cent_h;      // [BH][C][d] -2 G m_b rounded to bf16 (the assignment's operand)
   bf16* cent_l;      // [BH][C][d] -2 G m_b minus its bf16 rounding, in bf16
+  bf16* cent_b;      // [BH][C][16] centroid side of the assignment's bias product (m_b G m_b)
   float* alpha;      // [BH][N]    row scales of the query features
   float* rowconst;   // [BH][N]    alpha^2 x G x
   int* rank;         // [BH][N]    stable rank inside a Lloyd row block

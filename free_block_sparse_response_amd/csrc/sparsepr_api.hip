@@ -82,6 +82,7 @@ Bufs carve(const Dims& D, void* base, size_t* total) {
   B.cnorm = c.take<float>(BH * C);
   B.cent_h = c.take<spr::bf16>(BH * C * d);
   B.cent_l = c.take<spr::bf16>(BH * C * d);
+  B.cent_b = c.take<spr::bf16>(BH * C * 16);
   B.alpha = c.take<float>(BH * N);
   B.rowconst = c.take<float>(BH * N);
   B.rank = c.take<int>(BH * N);
