@@ -813,15 +813,12 @@ __global__ __launch_bounds__(256) void k_km_update(const T* x, Dims D, Bufs B, K
   __shared__ int go;
   const int b = blockIdx.x, bh = blockIdx.y, tid = threadIdx.x;
   if (st[bh].done_iter < t) return;
-  // Independent loads first, so that their latencies overlap: the metric (for G m), the
-  // first window of the group's per-block counts, and (wave 0) the inertia partials, read 8
-  // at a time per lane and summed in the fixed order.
-  const float* G = B.metric + (size_t)bh * DD * DD;
+  // Independent loads first, so that their latencies overlap: the first window of the
+  // group's per-block counts and (wave 0) the inertia partials, read 8 at a time per lane and
+  // summed in the fixed order. (The metric column for G m is read after the gather, so that
+  // the gather runs with few registers and many workgroups per CU.)
   constexpr int KH = 256 / DD;
   const int i = tid % DD, part = tid / DD;
-  float gv[DD / KH];
-#pragma unroll
-  for (int kk = 0; kk < DD / KH; ++kk) gv[kk] = G[(size_t)(part + kk * KH) * DD + i];
   const int* tab = B.tab + ((size_t)bh * D.C + b) * D.nblk;
   int tv0[4];
 #pragma unroll
@@ -930,6 +927,10 @@ __global__ __launch_bounds__(256) void k_km_update(const T* x, Dims D, Bufs B, K
   __syncthreads();
   float p = 0.f;
   {
+    const float* G = B.metric + (size_t)bh * DD * DD;
+    float gv[DD / KH];
+#pragma unroll
+    for (int kk = 0; kk < DD / KH; ++kk) gv[kk] = G[(size_t)(part + kk * KH) * DD + i];
     float tt = 0.f;
 #pragma unroll
     for (int kk = 0; kk < DD / KH; ++kk) tt = fmaf(gv[kk], m[part + kk * KH], tt);
