@@ -1194,11 +1194,12 @@ __global__ __launch_bounds__(256, RS == 1 ? 4 : 2) void k_km_assign_bf16(const b
     const float al = B.alpha ? B.alpha[(size_t)bh * D.N + (valid ? row : 0)] : 1.f;
     const float rc = B.rowconst[(size_t)bh * D.N + (valid ? row : 0)];
     const bool zero = !(al > 0.f);
-    if (zero) {
+    if (__builtin_amdgcn_ballot_w64(zero)) {  // (rare; no register copies on the common path)
 #pragma unroll
-      for (int c = 0; c < DD / 16; ++c) xr[rs][c] = bf16x8{};
+      for (int c = 0; c < DD / 16; ++c) xr[rs][c] = zero ? bf16x8{} : xr[rs][c];
     }
-    const float ia = zero ? 1.f : 1.f / al, rca = zero ? 0.f : rc / al;
+    // 1 / alpha to within an ulp: its bf16 hi / lo pair below carries about 16 bits of it
+    const float ia = zero ? 1.f : __builtin_amdgcn_rcpf(al), rca = zero ? 0.f : rc * ia;
     sca[rs] = zero ? 1.f : al;
     const bf16 iah = (bf16)ia, rch = (bf16)rca;
     const bf16 ial = (bf16)(ia - (float)iah), rcl = (bf16)(rca - (float)rch);
