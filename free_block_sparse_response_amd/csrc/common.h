@@ -91,6 +91,17 @@ __device__ inline uint64_t wave_match(int key, bool valid, int bits) {
   return valid ? m : 0ull;
 }
 
+// The same among lanes 0 .. 31 only (a lane >= 32 must pass valid = false): 32-bit masks,
+// half the vector work per key bit.
+__device__ inline uint32_t wave_match_lo(int key, bool valid, int bits) {
+  uint32_t m = (uint32_t)__ballot(valid);
+  for (int b = 0; b < bits; ++b) {
+    const uint32_t one = (uint32_t)__ballot(valid && ((key >> b) & 1));
+    m &= one ^ (uint32_t)(((key >> b) & 1) - 1);  // one if my bit is set, else ~one
+  }
+  return valid ? m : 0u;
+}
+
 __device__ inline int ceil_div(int a, int b) { return (a + b - 1) / b; }
 
 // Value of lane l ^ 32 (the other half of the wave), by gfx950's v_permlane32_swap (a VALU

@@ -1293,7 +1293,7 @@ __global__ __launch_bounds__(256, RS == 1 ? 4 : 2) void k_km_assign_bf16(const b
   // Tail, one barrier: labels; the inertia partial of each sort block (wave sums, then the
   // four waves in order); the stable in-block rank = rank among the wave's rows with the same
   // label + the counts of that label in the earlier waves; the block's label histogram.
-  uint64_t mk[RS];
+  uint32_t mk[RS];  // lanes 0 .. 31 hold the rows
   int lab[RS];
 #pragma unroll
   for (int rs = 0; rs < RS; ++rs) {
@@ -1310,11 +1310,11 @@ __global__ __launch_bounds__(256, RS == 1 ? 4 : 2) void k_km_assign_bf16(const b
     double v = valid ? (double)bestd : 0.0;
     v = wave_sum(v);
     if (lane_id() == 0) wpart[rs][w] = v;
-    mk[rs] = wave_match(lab[rs], valid, 10);
+    mk[rs] = wave_match_lo(lab[rs], valid, 10);
     // this wave's counts (zeroed, then one leader per label writes; one wave, in order)
     int* cw = cnt[rs][w];
     for (int i = lane_id(); i < C; i += kWave) cw[i] = 0;
-    if (valid && __popcll(mk[rs] & lanemask_lt()) == 0) cw[lab[rs]] = __popcll(mk[rs]);
+    if (valid && __popc(mk[rs] & (uint32_t)lanemask_lt()) == 0) cw[lab[rs]] = __popc(mk[rs]);
   }
   __syncthreads();
   int rk[RS];
@@ -1322,7 +1322,7 @@ __global__ __launch_bounds__(256, RS == 1 ? 4 : 2) void k_km_assign_bf16(const b
   for (int rs = 0; rs < RS; ++rs) {
     const int sb = sb0 + rs;
     const int row = r0 + 128 * rs + 32 * w + l32;
-    rk[rs] = __popcll(mk[rs] & lanemask_lt());
+    rk[rs] = __popc(mk[rs] & (uint32_t)lanemask_lt());
     for (int w2 = 0; w2 < w; ++w2) rk[rs] += cnt[rs][w2][lab[rs]];
     if (h == 0 && row < D.N) B.rank[(size_t)bh * D.N + row] = rk[rs];
     if (tid == 0 && sb < D.nblk)
