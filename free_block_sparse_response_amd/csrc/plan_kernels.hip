@@ -1342,42 +1342,58 @@ __global__ __launch_bounds__(256, RS == 1 ? 4 : 2) void k_km_assign_bf16(const b
 }
 
 // Row constants (see k_rowquad) on the matrix cores: (G x)_i for 32 dims at a time, dotted
-// with x in the lane that owns the row.
+// with x in the lane that owns the row. G (bf16 hi / lo) is staged in LDS once per
+// workgroup, which then takes the 128-row blocks blockIdx.x, + gridDim.x, ... of its head;
+// the next block's rows are loaded while the current block's products run.
 template <int DD>
-__global__ __launch_bounds__(256) void k_rowquad_bf16(const bf16* x, Dims D, const bf16* Gsh, const bf16* Gsl,
-                                                      float* rowconst, float* alpha_out, const KmState* kst_for_c) {
+__global__ __launch_bounds__(256, 2) void k_rowquad_bf16(const bf16* x, Dims D, const bf16* Gsh, const bf16* Gsl,
+                                                         float* rowconst, float* alpha_out,
+                                                         const KmState* kst_for_c) {
   constexpr int KS = DD + 8;
   __shared__ __attribute__((aligned(16))) bf16 Gh[DD * KS];
   __shared__ __attribute__((aligned(16))) bf16 Gl[DD * KS];
-  const int blk = blockIdx.x, bh = blockIdx.y;
+  const int bh = blockIdx.y;
   const int w = threadIdx.x / kWave, l32 = lane_id() & 31, h = lane_id() >> 5;
-  const int row = blk * kKmRows + 32 * w + l32;
-  const bool valid = row < D.N;
-  const bf16* xrow = x + ((size_t)bh * D.N + (valid ? row : D.N - 1)) * DD;
+  const bf16* xb = x + (size_t)bh * D.N * DD;
+  auto row_of = [&](int blk) { return min(blk * kKmRows + 32 * w + l32, D.N - 1); };
   bf16x8 xr[DD / 16];
-  load_row_operand<DD>(xrow, xr);
+  load_row_operand<DD>(xb + (size_t)row_of(blockIdx.x) * DD, xr);
   copy_hilo<DD, DD>(Gsh + (size_t)bh * DD * DD, Gsl + (size_t)bh * DD * DD, 0, DD, Gh, Gl);
   __syncthreads();
-  float part = 0.f;
+  const float cf = alpha_out ? (float)kst_for_c[bh].c_final : 0.f;
+  for (int blk = blockIdx.x; blk < D.nblk; blk += gridDim.x) {
+    const int row = blk * kKmRows + 32 * w + l32;
+    const bf16* xrow = xb + (size_t)row_of(blk) * DD;
+    // (the G operand reads are the same every block: a zero offset the compiler cannot see
+    // through keeps them from being hoisted into registers)
+    int z = 0;
+    asm volatile("" : "+v"(z));
+    float part = 0.f;
 #pragma unroll
-  for (int ib = 0; ib < DD; ib += 32) {
-    const f32x16 acc = mfma_rows<DD>(Gh, Gl, ib, xr);
+    for (int ib = 0; ib < DD / 32; ++ib) {
+      const f32x16 acc = mfma_rows<DD>(Gh + z, Gl + z, 32 * ib, xr);
+      if (ib == DD / 32 - 1) {
+        // the last products are issued: the next block's rows replace the operand (past the
+        // last block the current rows are read again, so no branch goes around the loads)
+        const int nx = blk + gridDim.x;
+        load_row_operand<DD>(xb + (size_t)row_of(nx < D.nblk ? nx : blk) * DD, xr);
+      }
 #pragma unroll
-    for (int g = 0; g < 4; ++g) {
-      const bf16x4 xv = *reinterpret_cast<const bf16x4*>(xrow + ib + 8 * g + 4 * h);
+      for (int g = 0; g < 4; ++g) {
+        const bf16x4 xv = *reinterpret_cast<const bf16x4*>(xrow + 32 * ib + 8 * g + 4 * h);
 #pragma unroll
-      for (int r = 0; r < 4; ++r) part = fmaf(acc[4 * g + r], (float)xv[r], part);
+        for (int r = 0; r < 4; ++r) part = fmaf(acc[4 * g + r], (float)xv[r], part);
+      }
     }
-  }
-  part += __shfl_xor(part, 32, kWave);
-  if (h == 0 && valid) {
-    const size_t o = (size_t)bh * D.N + row;
-    if (alpha_out) {
-      const float cf = (float)kst_for_c[bh].c_final;
-      alpha_out[o] = part > 0.f ? sqrtf(cf / part) : 0.f;
-      rowconst[o] = part > 0.f ? cf : 0.f;
-    } else {
-      rowconst[o] = part;
+    part += __shfl_xor(part, 32, kWave);
+    if (h == 0 && row < D.N) {
+      const size_t o = (size_t)bh * D.N + row;
+      if (alpha_out) {
+        alpha_out[o] = part > 0.f ? sqrtf(cf / part) : 0.f;
+        rowconst[o] = part > 0.f ? cf : 0.f;
+      } else {
+        rowconst[o] = part;
+      }
     }
   }
 }
@@ -1950,11 +1966,14 @@ static void run_lloyd(const void* xv, const Dims& D, const Bufs& B, int C, const
 template <typename T, int DD>
 static void rowquad(const T* x, const Dims& D, const Bufs& B, const float* G, float* rowconst, float* alpha_out,
                     const KmState* kst, hipStream_t s) {
-  if constexpr (std::is_same<T, bf16>::value)
-    hipLaunchKernelGGL((k_rowquad_bf16<DD>), dim3(D.nblk, D.BH), dim3(256), 0, s, x, D, B.metric_h, B.metric_l,
-                       rowconst, alpha_out, kst);
-  else
+  if constexpr (std::is_same<T, bf16>::value) {
+    // about 2048 workgroups (eight per CU over the launch), each staging G once
+    const int per = std::max(1, D.nblk * D.BH / 2048);
+    hipLaunchKernelGGL((k_rowquad_bf16<DD>), dim3((D.nblk + per - 1) / per, D.BH), dim3(256), 0, s, x, D,
+                       B.metric_h, B.metric_l, rowconst, alpha_out, kst);
+  } else {
     hipLaunchKernelGGL((k_rowquad<T, DD>), dim3(D.nblk, D.BH), dim3(256), 0, s, x, D, G, rowconst, alpha_out, kst);
+  }
 }
 
 template <typename T, int DD>
