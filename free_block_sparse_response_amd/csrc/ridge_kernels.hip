@@ -138,13 +138,17 @@ __global__ __launch_bounds__(512) void k_ridge_solve(Dims D, Bufs B, float* coef
   int buf = 0;
   for (int j0 = 0; j0 < n; j0 += P, buf ^= 1) {
     const int pw = min(P, n - j0);
-    // owners publish the panel columns (rows >= j0) and the panel rows of the right-hand side
+    // owners publish the panel columns (rows >= j0) and the panel rows of the right-hand side.
+    // Here and below, a block of TY rows or TX columns that lies wholly before j0 is skipped:
+    // its entries are final (block-uniform branches).
 #pragma unroll
     for (int q = 0; q < QT; ++q) {
+      if (TX * q + TX <= j0) continue;
       const int pc = tx + TX * q - j0;
       if (pc >= 0 && pc < pw) {
 #pragma unroll
         for (int r = 0; r < RT; ++r) {
+          if (TY * r + TY <= j0) continue;
           const int i = ty + TY * r;
           if (i >= j0 && i < n) cb[buf][pc][i] = a[r][q];
         }
@@ -152,6 +156,7 @@ __global__ __launch_bounds__(512) void k_ridge_solve(Dims D, Bufs B, float* coef
     }
 #pragma unroll
     for (int r = 0; r < RT; ++r) {
+      if (TY * r + TY <= j0) continue;
       const int pr = ty + TY * r - j0;
       if (pr >= 0 && pr < pw) rb[buf][pr][tx] = b[r];
     }
@@ -186,6 +191,7 @@ __global__ __launch_bounds__(512) void k_ridge_solve(Dims D, Bufs B, float* coef
     double yq[QT][P];
 #pragma unroll
     for (int q = 0; q < QT; ++q) {
+      if (TX * q + TX <= j0) continue;  // (yq of such a block is never read)
       const int k = tx + TX * q;
       const bool tk = k >= j0 + pw && k < n;
       double y[P];
@@ -212,6 +218,7 @@ __global__ __launch_bounds__(512) void k_ridge_solve(Dims D, Bufs B, float* coef
     // its right-hand side; the panel rows of the right-hand side take z
 #pragma unroll
     for (int r = 0; r < RT; ++r) {
+      if (TY * r + TY <= j0) continue;
       const int i = ty + TY * r;
       const bool tr = i >= j0 + pw && i < n;
       double lf[P], li[P];
@@ -225,6 +232,7 @@ __global__ __launch_bounds__(512) void k_ridge_solve(Dims D, Bufs B, float* coef
       }
 #pragma unroll
       for (int q = 0; q < QT; ++q) {
+        if (TX * q + TX <= j0) continue;
         double v = a[r][q];
 #pragma unroll
         for (int p = 0; p < P; ++p) v -= li[p] * yq[q][p];
@@ -271,6 +279,7 @@ __global__ __launch_bounds__(512) void k_ridge_solve(Dims D, Bufs B, float* coef
     // owners publish the panel rows: right-hand side, and L1 left of the diagonal
 #pragma unroll
     for (int r = 0; r < RT; ++r) {
+      if (TY * r + TY <= j0 || TY * r >= j0 + pw) continue;
       const int i = ty + TY * r;
       const int pr = i - j0;
       if (pr >= 0 && pr < pw) {
@@ -294,6 +303,7 @@ __global__ __launch_bounds__(512) void k_ridge_solve(Dims D, Bufs B, float* coef
     }
 #pragma unroll
     for (int r = 0; r < RT; ++r) {
+      if (TY * r >= j0 + pw) continue;  // rows wholly after the panel are final
       const int i = ty + TY * r;
       double v = b[r];
       if (i < j0) {
