@@ -1152,8 +1152,8 @@ __device__ inline f32x16 mfma_cols(const bf16* Yh, const bf16* Yl, int y0, const
 // every centroid operand read from LDS feeds RS products. Centroid operands (-2 G m_b in
 // bf16, plus its bf16 remainder when LO, and the bias operands) are double-buffered in LDS 64
 // centroids at a time: the next chunk's global loads are issued before the current chunk's
-// products. The plan runs RS = 1 (four waves per SIMD) up to 256 centroids, and RS = 2 (half
-// the LDS operand reads per product) beyond that and with the remainder operand.
+// products. The plan runs RS = 1 (four waves per SIMD), and RS = 2 (half the LDS operand
+// reads per product) with the remainder operand.
 template <int DD, int RS, bool LO>
 __global__ __launch_bounds__(256, RS == 1 ? 4 : 2) void k_km_assign_bf16(const bf16* x, Dims D, Bufs B, int C,
                                                                            KmState* st, int t) {
@@ -1939,12 +1939,7 @@ static void lloyd_iterations(const T* x, const Dims& D, const Bufs& B, int C, Km
         hipLaunchKernelGGL((k_km_assign_bf16<DD, 2, true>), dim3((D.nblk + 1) / 2, D.BH), dim3(256), 0, s, x, D, B, C,
                            st, t);
       else
-        if (C > 256)
-          hipLaunchKernelGGL((k_km_assign_bf16<DD, 2, false>), dim3((D.nblk + 1) / 2, D.BH), dim3(256), 0, s, x, D, B,
-                             C, st, t);
-        else
-          hipLaunchKernelGGL((k_km_assign_bf16<DD, 1, false>), dim3(D.nblk, D.BH), dim3(256), 0, s, x, D, B, C,
-                             st, t);
+        hipLaunchKernelGGL((k_km_assign_bf16<DD, 1, false>), dim3(D.nblk, D.BH), dim3(256), 0, s, x, D, B, C, st, t);
     else
       hipLaunchKernelGGL((k_km_assign<T, DD>), dim3(D.nblk, D.BH), dim3(256), 0, s, x, D, B, C, st, t);
     hipLaunchKernelGGL((k_km_update<T, DD>), dim3(C, D.BH), dim3(256), 0, s, x, D, B, st, t);
