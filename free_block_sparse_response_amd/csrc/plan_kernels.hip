@@ -812,24 +812,37 @@ __global__ __launch_bounds__(256) void k_km_update(const T* x, Dims D, Bufs B, K
   __shared__ int wpre[kUpdWin], wbeg[kUpdWin], mlist[kUpdChunk], ws[4];
   __shared__ int go;
   const int b = blockIdx.x, bh = blockIdx.y, tid = threadIdx.x;
-  if (st[bh].done_iter < t) return;
-  // Independent loads first, so that their latencies overlap: the first window of the
-  // group's per-block counts and (wave 0) the inertia partials, read 8 at a time per lane and
-  // summed in the fixed order. (The metric column for G m is read after the gather, so that
-  // the gather runs with few registers and many workgroups per CU.)
+  // Independent loads first, so that their latencies overlap: the head's state, the first
+  // window of the group's per-block counts and (wave 0) the inertia partials, read 8 at a
+  // time per lane and summed in the fixed order; the state is tested once they are all in
+  // flight. (The metric column for G m is read after the gather, so that the gather runs
+  // with few registers and many workgroups per CU.)
+  const int done_iter = st[bh].done_iter;
+  const double prev = st[bh].inertia[(t - 1) & 1];  // (this launch writes the other slot)
   constexpr int KH = 256 / DD;
   const int i = tid % DD, part = tid / DD;
   const int* tab = B.tab + ((size_t)bh * D.C + b) * D.nblk;
+  // (clamped, unconditional loads, masked afterwards: no branch between them)
   int tv0[4];
 #pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    const int j = 4 * tid + q;
-    tv0[q] = j < D.nblk ? tab[j] : 0;
-  }
+  for (int q = 0; q < 4; ++q) tv0[q] = tab[min(4 * tid + q, D.nblk - 1)];
+  const double* ip = B.ipart + (size_t)bh * D.nblk;
+  double pv0[8];
+#pragma unroll
+  for (int u = 0; u < 8; ++u) pv0[u] = ip[min(lane_id() + u * kWave, D.nblk - 1)];
+  asm volatile("" ::: "memory");  // (keeps the loads above ahead of the test)
+  if (done_iter < t) return;
+#pragma unroll
+  for (int q = 0; q < 4; ++q)
+    if (4 * tid + q >= D.nblk) tv0[q] = 0;
+#pragma unroll
+  for (int u = 0; u < 8; ++u)
+    if (lane_id() + u * kWave >= D.nblk) pv0[u] = 0.0;
   if (tid < kWave) {
-    const double* ip = B.ipart + (size_t)bh * D.nblk;
     double sum = 0.0;
-    for (int i0 = tid; i0 < D.nblk; i0 += 8 * kWave) {
+#pragma unroll
+    for (int u = 0; u < 8; ++u) sum += pv0[u];
+    for (int i0 = tid + 8 * kWave; i0 < D.nblk; i0 += 8 * kWave) {
       double pv[8];
 #pragma unroll
       for (int u = 0; u < 8; ++u) pv[u] = i0 + u * kWave < D.nblk ? ip[i0 + u * kWave] : 0.0;
@@ -838,7 +851,6 @@ __global__ __launch_bounds__(256) void k_km_update(const T* x, Dims D, Bufs B, K
     }
     sum = wave_sum(sum);
     if (tid == 0) {
-      const double prev = st[bh].inertia[(t - 1) & 1];
       const bool done = (t > 1 && prev - sum <= (double)D.tol * prev) || t >= D.max_iter;
       if (b == 0) {
         st[bh].inertia[t & 1] = sum;
