@@ -109,6 +109,16 @@ def test_c2_full_call_error_matches_oracle(assign_precision):
     _error_stats_vs_oracle(w, list(range(w["heads"])), rows_per_head=2048, assign_precision=assign_precision)
 
 
+@pytest.mark.parametrize("assign_precision", [0, 1])
+def test_bf16_full_call_partial_centroid_chunks(assign_precision):
+    # group counts that are not multiples of the Lloyd assignment's 32-centroid blocks or
+    # 64-centroid chunks: the last chunk re-reads the last centroid and its padding centroids
+    # must never win (their bias operand scores +inf)
+    w = configs.with_overrides("c2", grid=(8, 16, 20), heads=2, n_sampled=128, n_key_groups=40,
+                               n_query_groups=24, n_probes=64, density=0.25)
+    _error_stats_vs_oracle(w, [0, 1], assign_precision=assign_precision)
+
+
 def test_c2_deterministic_bitwise():
     w = configs.CONFIGS["c2"]
     (tq, _), (tk, _), (tv, _) = inputs(w)
