@@ -43,6 +43,8 @@ class Bench:
         sp = SparsePR(config_from_workload(w), device=dev)
         dense = torch.empty_like(self.q)
         sp.dense(self.q, self.k, self.v, dense)
+        torch.cuda.synchronize()
+        sp.close()
         self.ref = dense.reshape(self.BH, self.N, self.d).float()
         self.ref_norm = self.ref.norm(dim=-1)
 
@@ -62,7 +64,7 @@ class Bench:
                     / (self.ref_norm + 1e-8))
         res = dict(err=rows_err, probes=sp.export("PROBES").long(), weights=sp.export("PROBE_WEIGHTS").clone(),
                    density=density)
-        del sp
+        sp.close()
         return res
 
     def unprobed(self, runs):

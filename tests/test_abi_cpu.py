@@ -135,3 +135,58 @@ def test_status_strings(lib):
     for s in range(7):
         assert lib.sparsepr_status_string(s)
     assert b"positive definite" in lib.sparsepr_status_string(L.SPARSEPR_ERR_NUMERICAL)
+
+
+# ---------------------------------------------------------------- argument checks of the binding
+def _t(shape, dtype=None, **kw):
+    import torch
+
+    return torch.zeros(shape, dtype=dtype or torch.bfloat16, **kw)
+
+
+def test_binding_accepts_the_documented_layout():
+    import torch
+
+    from free_block_sparse_response_amd.call import check_tensor
+
+    t = _t((1, 2, 8, 4))
+    assert check_tensor(t, "q", [(1, 2, 8, 4)], torch.bfloat16, "cpu") is t
+    lab = _t((2, 8), torch.int32)
+    check_tensor(lab, "key_labels", [(2, 8), (1, 2, 8)], torch.int32, "cpu")
+
+
+@pytest.mark.parametrize("case", ["device", "dtype", "shape", "transposed view", "not a tensor"])
+def test_binding_refuses_what_the_kernels_would_misread(case):
+    import torch
+
+    from free_block_sparse_response_amd.call import check_tensor
+
+    shape = [(1, 2, 8, 4)]
+    if case == "device":           # a host tensor where a device pointer is expected
+        t, dev = _t((1, 2, 8, 4)), "cuda"
+    elif case == "dtype":          # float16 data for a bfloat16 configuration
+        t, dev = _t((1, 2, 8, 4), torch.float16), "cpu"
+    elif case == "shape":          # too few rows: the kernels would read past the allocation
+        t, dev = _t((1, 2, 7, 4)), "cpu"
+    elif case == "transposed view":  # the [B, N, H, d] activations of a video transformer
+        t, dev = _t((1, 8, 2, 4)).transpose(1, 2), "cpu"
+    else:
+        t, dev = [[0.0]], "cpu"
+    with pytest.raises(ValueError):
+        check_tensor(t, "q", shape, torch.bfloat16, dev)
+
+
+@pytest.mark.parametrize("dtype_name", ["int64 labels", "float weights as float64", "int32 masses"])
+def test_binding_refuses_wrong_integer_and_weight_types(dtype_name):
+    import torch
+
+    from free_block_sparse_response_amd.call import check_tensor
+
+    if dtype_name == "int64 labels":
+        t, want, shape = _t((2, 8), torch.int64), torch.int32, (2, 8)
+    elif dtype_name == "float weights as float64":
+        t, want, shape = _t((2, 5), torch.float64), torch.float32, (2, 5)
+    else:
+        t, want, shape = _t((2, 3, 3), torch.int32), torch.int64, (2, 3, 3)
+    with pytest.raises(ValueError):
+        check_tensor(t, "x", [shape], want, "cpu")

@@ -375,6 +375,32 @@ def test_select_probes_stratified_weights():
         pos += m[a]
 
 
+def test_select_probes_group_weight_is_the_group_share_of_queries():
+    # [T4] "query group stratified" probes with a weighted ridge: each group's probes
+    # together stand for that group's share of the queries, so a group's total weight
+    # w_a * m_a is proportional to its size n_q[a] (here groups whose size-to-probe ratio
+    # n_q[a] / m_a differs, so an inverted ratio m_a / n_q[a] would fail)
+    sizes = np.array([120, 7, 33, 61, 3, 250, 26])
+    N, M = int(sizes.sum()), 17
+    rng = np.random.default_rng(31)
+    lab = rng.permutation(np.repeat(np.arange(len(sizes)), sizes))
+    perm, off, cnt = O.group_permutation(lab, len(sizes))
+    m = O.allocate_probes(cnt, M, N)
+    covered = m > 0
+    ratio = cnt[covered] / m[covered]
+    assert ratio.max() > 1.2 * ratio.min()            # the ratio really varies
+    idx, w = O.select_probes(0, 3, perm, off, cnt, M, N)
+    assert np.isclose(w.sum(), M)
+    group_of = lab[idx]
+    total = np.array([w[group_of == a].sum() for a in range(len(sizes))])
+    assert np.all(total[~covered] == 0)
+    # total weight of a group / all weight == its queries / all queries of covered groups
+    np.testing.assert_allclose(total[covered] / M, cnt[covered] / cnt[covered].sum(), rtol=1e-12)
+    # and every probe of a group weighs the same
+    for a in np.flatnonzero(covered):
+        assert np.ptp(w[group_of == a]) == 0
+
+
 # ---------------------------------------------------------------- ridge
 def test_ridge_matches_lstsq_on_augmented_system():
     rng = np.random.default_rng(14)
@@ -401,6 +427,30 @@ def test_ridge_recovers_planted_affine_map():
     o_dn = o_sp + o_sp @ theta[:d] + theta[d]
     got = O.ridge_fit(o_sp, o_dn, rng.uniform(0.5, 2, M), 1e-12)
     np.testing.assert_allclose(got, theta, atol=1e-9)
+
+
+def test_planted_affine_residual_is_removed_end_to_end():
+    # [abstract]: the residual of every unprobed row is predicted by the affine map fitted
+    # on the probes. Dense outputs planted as o + o A + b (A not symmetric, so a transposed
+    # map fails) are recovered for every row through ridge_fit then apply_residual, and the
+    # probe rows return their given dense rows exactly.
+    rng = np.random.default_rng(32)
+    N, d, M = 400, 12, 40
+    o_sp = rng.standard_normal((N, d))
+    A = rng.standard_normal((d, d))
+    assert np.abs(A - A.T).max() > 1.0
+    b = rng.standard_normal(d)
+    o_dn = np.empty_like(o_sp)
+    for i in range(N):                     # the planted map, row by row
+        for j in range(d):
+            o_dn[i, j] = o_sp[i, j] + sum(o_sp[i, kk] * A[kk, j] for kk in range(d)) + b[j]
+    probes = np.sort(rng.choice(N, M, replace=False))
+    theta = O.ridge_fit(o_sp[probes], o_dn[probes], rng.uniform(0.5, 2.0, M), 1e-12)
+    out = O.apply_residual(o_sp, probes, o_dn[probes], theta)
+    np.testing.assert_allclose(out, o_dn, rtol=0, atol=1e-9)
+    assert np.array_equal(out[probes], o_dn[probes])
+    # the map is not the identity correction: without it the error is large
+    assert np.abs(o_sp - o_dn).max() > 1.0
 
 
 def test_ridge_interpolates_when_underdetermined():
