@@ -25,7 +25,7 @@ SPARSEPR_BF16 = 1
 
 EXPORT = dict(SAMPLED=0, KEY_LABELS=1, QUERY_LABELS=2, KEY_PERM=3, QUERY_PERM=4, KEY_OFFSETS=5,
               QUERY_OFFSETS=6, ROUTE_ROWPTR=7, ROUTE_COLS=8, PROBES=9, PROBE_WEIGHTS=10, GROUP_MASS=11,
-              KEY_CENTROIDS=12)
+              KEY_CENTROIDS=12, KEY_SEEDS=13, QUERY_SEEDS=14)
 
 
 class sparsepr_config(ctypes.Structure):

@@ -1452,16 +1452,19 @@ __global__ __launch_bounds__(256) void k_group_mass_bf16(const bf16* q, Dims D, 
         z[v] = col < Ck ? fmaf(sc2, acc[v], lg[col]) : -INFINITY;
         mx = fmaxf(mx, z[v]);
       }
+      // a lane half whose 16 centroids are all past the last group (C_k' <= 4) has no
+      // score yet: shift by 0 instead of -inf, so its terms are exp2(-inf) = 0, not NaN
+      const float sh = mx == -INFINITY ? 0.f : mx;
       float add = 0.f;
 #pragma unroll
-      for (int v = 0; v < 16; ++v) add += __builtin_amdgcn_exp2f(z[v] - mx);
-      ssum = ssum * __builtin_amdgcn_exp2f(m - mx) + add;
+      for (int v = 0; v < 16; ++v) add += __builtin_amdgcn_exp2f(z[v] - sh);
+      ssum = ssum * __builtin_amdgcn_exp2f(m - sh) + add;
       m = mx;
     }
   }
   {
     const float mo = __shfl_xor(m, 32, kWave), so = __shfl_xor(ssum, 32, kWave);
-    const float mm = fmaxf(m, mo);
+    const float mm = fmaxf(m, mo);  // finite: lane half 0 holds centroid 0
     ssum = ssum * __builtin_amdgcn_exp2f(m - mm) + so * __builtin_amdgcn_exp2f(mo - mm);
     m = mm;
   }

@@ -519,6 +519,8 @@ static bool export_region(sparsepr_plan_t p, int which, const Bufs& B, const voi
     case SPARSEPR_EXPORT_PROBE_WEIGHTS: *src = B.pweights; *bytes = BH * D.M * 4; return true;
     case SPARSEPR_EXPORT_GROUP_MASS: *src = B.u; *bytes = BH * D.Cq * D.Ck * 8; return true;
     case SPARSEPR_EXPORT_KEY_CENTROIDS: *src = B.kcent; *bytes = BH * D.Ck * D.d * 4; return true;
+    case SPARSEPR_EXPORT_KEY_SEEDS: *src = B.init_k; *bytes = BH * D.Ck * 4; return true;
+    case SPARSEPR_EXPORT_QUERY_SEEDS: *src = B.init_q; *bytes = BH * D.Cq * 4; return true;
   }
   return false;
 }

@@ -128,7 +128,11 @@ typedef enum {
   SPARSEPR_EXPORT_PROBES = 9,        /* [M] probe rows, group-major, ascending token id   */
   SPARSEPR_EXPORT_PROBE_WEIGHTS = 10,/* [M] float ridge weights, summing to M             */
   SPARSEPR_EXPORT_GROUP_MASS = 11,   /* [C_q*C_k] int64 masses u (row stride C_k)         */
-  SPARSEPR_EXPORT_KEY_CENTROIDS = 12 /* [C_k*d] float key-space centroids (row stride d)  */
+  SPARSEPR_EXPORT_KEY_CENTROIDS = 12,/* [C_k*d] float key-space centroids (row stride d)  */
+  SPARSEPR_EXPORT_KEY_SEEDS = 13,    /* [C_k] Forgy seed rows of the key k-means, ascending */
+  SPARSEPR_EXPORT_QUERY_SEEDS = 14   /* [C_q] Forgy seed rows of the query k-means;        */
+                                     /*   both written by sparsepr_plan only (a warm or    */
+                                     /*   labels-given plan leaves them as they were)      */
 } sparsepr_export_kind;
 
 /* Validates cfg and creates a plan handle. Host only: touches no device. */

@@ -134,24 +134,26 @@ def test_c2_deterministic_bitwise():
 
 
 # ------------------------------------------------------------------- full-size parity
-def _rule_labels(N, C, seed, contiguous):
-    if contiguous:                       # equal contiguous chunks of the raster order
-        return (np.arange(N) * C // N).astype(np.int64)
-    rng = np.random.default_rng(seed)    # uneven random groups, every id used
-    lab = rng.integers(0, C, N)
-    lab[rng.choice(N, C, replace=False)] = np.arange(C)
-    return lab.astype(np.int64)
+def _forgy_labels(x, C, seed, stream, head):
+    """One Lloyd assignment from C Forgy seed rows: spatially coherent groups whose ids are
+    scattered over the grid, as the method's partitions are (so the selected key groups of a
+    query group form many short key runs, not a few long ones)."""
+    seeds = O.select_smallest(seed, stream, head, np.arange(x.shape[0]), C)
+    return np.argmin(O.sq_dists(x, x[seeds]), axis=1).astype(np.int64)
 
 
-@pytest.mark.parametrize("name", ["c3", "c4", "c5"])
-def test_full_size_labels_given_sampled_rows(name):
+@pytest.mark.parametrize("name,rho", [("c3", None), ("c4", None), ("c5", 0.10), ("c5", 0.16), ("c5", 0.22),
+                                      ("c5", 0.26)])
+def test_full_size_labels_given_sampled_rows(name, rho):
     """All heads in the benchmark's launch configuration; two heads carry the seeded
     workload inputs and are checked against the oracle on sampled rows (the oracle is too
     slow for every row of every head); the others carry filler values."""
-    w = configs.CONFIGS[name]
+    w = dict(configs.CONFIGS[name])
+    if rho is not None:
+        w["density"] = rho
     N, d, H, M = configs.seq_len(w), w["head_dim"], w["heads"], w["n_probes"]
     checked = [0, H - 1]
-    say(f"case: full-size {name} N={N} H={H} checked heads {checked}")
+    say(f"case: full-size {name} rho={w['density']} N={N} H={H} checked heads {checked}")
     (cq, q64), (ck, k64), (cv, v64) = inputs(w, checked)
     g = torch.Generator(device=DEV).manual_seed(7)
     tq, tk, tv = (torch.randn((1, H, N, d), generator=g, device=DEV, dtype=torch.float32).to(torch.bfloat16)
@@ -159,21 +161,24 @@ def test_full_size_labels_given_sampled_rows(name):
     for j, h in enumerate(checked):
         tq[0, h], tk[0, h], tv[0, h] = cq[0, j], ck[0, j], cv[0, j]
     p = O.call_params(w)
-    kl = _rule_labels(N, w["n_key_groups"], 0, True)
-    ql = _rule_labels(N, w["n_query_groups"], 1, False)
-    plans = {}
+    s = p["scale"]
+    plans, kls, qls = {}, {}, {}
     for j, h in enumerate(checked):
-        hp = O.HeadPlan(key_labels=kl.copy(), query_labels=ql.copy())
+        qs = q64[j][O.select_smallest(w["seed"], O.STREAM_SAMPLED, h, np.arange(N), w["n_sampled"])]
+        kls[h] = _forgy_labels(O.key_features(k64[j], qs, s), w["n_key_groups"], 0, O.STREAM_KEY_INIT, h)
+        qls[h] = _forgy_labels(q64[j], w["n_query_groups"], 0, O.STREAM_QUERY_INIT, h)
+        hp = O.HeadPlan(key_labels=kls[h].copy(), query_labels=qls[h].copy())
         plans[h] = O.finish_plan(q64[j], k64[j], p, h, hp)
     Ck, Cq = w["n_key_groups"], w["n_query_groups"]
     u = np.zeros((H, Cq, Ck), dtype=np.int64)
+    KL = np.zeros((H, N), np.int32)
+    QL = np.zeros((H, N), np.int32)
     for h in range(H):
-        src = plans[h] if h in plans else plans[checked[0]]
-        u[h, :src.u.shape[0], :src.u.shape[1]] = src.u
+        src = h if h in plans else checked[0]
+        u[h, :plans[src].u.shape[0], :plans[src].u.shape[1]] = plans[src].u
+        KL[h], QL[h] = kls[src], qls[src]
     sp = SparsePR(config_from_workload(w), device=DEV)
-    KL = torch.from_numpy(np.tile(kl.astype(np.int32), (H, 1))).to(DEV)
-    QL = torch.from_numpy(np.tile(ql.astype(np.int32), (H, 1))).to(DEV)
-    sp.plan(tq, tk, KL, QL, torch.from_numpy(u).to(DEV))
+    sp.plan(tq, tk, torch.from_numpy(KL).to(DEV), torch.from_numpy(QL).to(DEV), torch.from_numpy(u).to(DEV))
     sp.attend(tq, tk, tv)
     sp.fit_residual()
     sp.apply()
@@ -194,9 +199,12 @@ def test_full_size_labels_given_sampled_rows(name):
         e_psp = max_rel(np_(sp.o_probe_sparse[0, h]), ref["o_probe_sparse"])
         e_pdn = max_rel(np_(sp.o_probe[0, h]), ref["o_probe_dense"])
         e_out = max_rel(np_(sp.out[0, h])[rows], ref["out"])
-        say(f"  head {h}: density {hp.pairs / N ** 2:.4f} o_sparse {e_sp:.2e} probe sparse {e_psp:.2e} "
-            f"probe dense {e_pdn:.2e} out {e_out:.2e}")
+        runs = np.mean([len(np.flatnonzero(np.diff(hp.route.cols[hp.route.row_ptr[a]:hp.route.row_ptr[a + 1]]) != 1)) + 1
+                        for a in range(hp.Cq)])
+        say(f"  head {h}: density {hp.pairs / N ** 2:.4f} ({runs:.1f} key runs per query group) o_sparse {e_sp:.2e} "
+            f"probe sparse {e_psp:.2e} probe dense {e_pdn:.2e} out {e_out:.2e}")
         assert max(e_sp, e_psp, e_pdn, e_out) <= 2e-2
+    sp.close()
 
 
 # ------------------------------------------------------------------- edge cases

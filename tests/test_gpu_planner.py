@@ -1,0 +1,285 @@
+"""GPU planner parity at the group counts the full workloads use (several 64-centroid chunks
+of the Lloyd assignment and of the group masses), against the CPU oracle:
+
+* the sampled queries and both Forgy seed sets, bit for bit, at the 8-head and the
+  40-head, 93,600-token sizes;
+* one Lloyd assignment fed the oracle's centroids (512 groups): labels equal the oracle's
+  argmin on every row whose two best distances differ by more than the error bound of
+  the assignment's bf16 products;
+* the group masses u computed from given labels, entry by entry, and the route cells
+  they select;
+* the library's own plan with 256 and 512 groups: unprobed error, partition quality
+  (inertia), label agreement and iteration counts against stated bounds.
+"""
+import numpy as np
+import pytest
+import torch
+
+from free_block_sparse_response_amd import configs
+from free_block_sparse_response_amd.call import SparsePR, config_from_workload
+from oracle import sparsepr_oracle as O
+
+from gpu_helpers import DEV, inputs, np_, say
+
+pytestmark = pytest.mark.gpu
+
+# Lloyd assignment error bounds (relative to the magnitude of the terms of a distance), from
+# the arithmetic of the bf16 products: the centroid operand -2 G m_b is rounded to bf16
+# (relative error <= 2^-9 per element) with assign_precision 0, or carried as bf16 hi + lo
+# (<= 2^-17) with 1; the distance's low 10 mantissa bits hold the centroid index (2^-13);
+# the metric and the means come from fp32 sums. A factor of 2 over the first-order bound.
+ASSIGN_EPS = {0: 2.0 ** -8, 1: 2.0 ** -12}
+
+# group masses: logits from bf16 hi/lo products (~2^-16 relative), the hardware exp2
+# (~2^-22), fp32 sums over a tile's rows and a double sum over tiles
+MASS_RTOL = 2e-3
+MASS_ATOL = 2.0 ** -22          # in units of P (probability mass)
+
+
+def forgy_labels(x, C, seed, stream, head):
+    """One Lloyd assignment from C Forgy seed rows (a cheap, spatially coherent partition
+    with scattered group ids, the shape the method's partitions have)."""
+    seeds = O.select_smallest(seed, stream, head, np.arange(x.shape[0]), C)
+    return np.argmin(O.sq_dists(x, x[seeds]), axis=1).astype(np.int64)
+
+
+def _workload(C, heads=2, **kw):
+    return configs.with_overrides("c2", heads=heads, n_key_groups=C, n_query_groups=C, **kw)
+
+
+# ---------------------------------------------------------------- (d) sampled and seed ids
+@pytest.mark.parametrize("name", ["c2", "c5"])
+def test_sampled_queries_and_seed_rows_bit_exact(name):
+    # the selections depend only on (seed, stream, head, N): random device inputs suffice
+    w = configs.CONFIGS[name]
+    N, H, d = configs.seq_len(w), w["heads"], w["head_dim"]
+    say(f"case: sampled / seed ids, {name} N={N} H={H}")
+    g = torch.Generator(device=DEV).manual_seed(3)
+    tq, tk = (torch.randn((1, H, N, d), generator=g, device=DEV).to(torch.bfloat16) for _ in range(2))
+    sp = SparsePR(config_from_workload(w, kmeans_max_iter=1), device=DEV)
+    sp.plan(tq, tk)
+    torch.cuda.synchronize()
+    ex = {k: np_(sp.export(k)) for k in ("SAMPLED", "KEY_SEEDS", "QUERY_SEEDS")}
+    for h in sorted({0, 1, H // 2, H - 1}):
+        for kind, stream, m in (("SAMPLED", O.STREAM_SAMPLED, w["n_sampled"]),
+                                ("KEY_SEEDS", O.STREAM_KEY_INIT, w["n_key_groups"]),
+                                ("QUERY_SEEDS", O.STREAM_QUERY_INIT, w["n_query_groups"])):
+            want = O.select_smallest(w["seed"], stream, h, np.arange(N), m)
+            assert np.array_equal(ex[kind][h], want), (kind, h)
+    sp.close()
+
+
+# ---------------------------------------------------------------- (b) one assignment, given centroids
+def _near_tie_free(dist, A, bias, eps):
+    """Rows whose best and second-best distances differ by more than the assignment's error
+    bound eps * (cross-term magnitudes + centroid and row constants of both)."""
+    order = np.argsort(dist, axis=1, kind="stable")
+    r = np.arange(dist.shape[0])
+    b1, b2 = order[:, 0], order[:, 1]
+    gap = dist[r, b2] - dist[r, b1]
+    thr = eps * (A[r, b1] + A[r, b2] + bias[0][r] + bias[1][r, b1] + bias[1][r, b2])
+    return gap > thr, b1
+
+
+def _metric_terms(x, G, m):
+    """Magnitude of the cross terms 2 |x_i (G m_b)_i| summed over i, and |m G m|, |x G x|."""
+    Gm = m @ G                                   # G symmetric
+    A = 2.0 * (np.abs(x) @ np.abs(Gm).T)
+    cn = np.abs(np.einsum("bi,bi->b", m, Gm))
+    rc = np.abs(np.einsum("ji,ji->j", x @ G, x))
+    return A, (rc, np.broadcast_to(cn[None, :], A.shape))
+
+
+@pytest.mark.parametrize("assign_precision", [0, 1])
+def test_one_lloyd_assignment_from_given_centroids(assign_precision):
+    # a labels-given plan followed by a warm plan limited to one iteration: the warm plan's
+    # first assignment starts from the given partition's centroids (key side: mean keys;
+    # query side: means of alpha q), so its labels are an argmin against known centroids
+    C = 512
+    w = _workload(C, assign_precision=assign_precision, n_sampled=256)
+    heads = [0, 1]
+    say(f"case: one assignment from given centroids, C={C}, precision {assign_precision}")
+    (tq, q64), (tk, k64), (tv, v64) = inputs(w, heads)
+    p = O.call_params(w)
+    s = p["scale"]
+    N = configs.seq_len(w)
+    prev, kl0, ql0 = [], [], []
+    for i in range(len(heads)):
+        qs = q64[i][O.select_smallest(w["seed"], O.STREAM_SAMPLED, i, np.arange(N), w["n_sampled"])]
+        kl0.append(forgy_labels(O.key_features(k64[i], qs, s), C, 11, O.STREAM_KEY_INIT, i))
+        ql0.append(forgy_labels(q64[i], C, 11, O.STREAM_QUERY_INIT, i))
+        prev.append(O.finish_plan(q64[i], k64[i], p, i, O.HeadPlan(key_labels=kl0[i].copy(),
+                                                                 query_labels=ql0[i].copy())))
+    sp = SparsePR(config_from_workload(w, heads=len(heads), warm_iters=1), device=DEV)
+    KL = torch.from_numpy(np.stack(kl0).astype(np.int32)).to(DEV)
+    QL = torch.from_numpy(np.stack(ql0).astype(np.int32)).to(DEV)
+    sp.plan(tq, tk, KL, QL)
+    sp.plan(tq, tk, warm=True)
+    torch.cuda.synchronize()
+    info = sp.info()
+    g_kl, g_ql = np_(sp.export("KEY_LABELS")), np_(sp.export("QUERY_LABELS"))
+    eps = ASSIGN_EPS[assign_precision]
+    for i, hp0 in enumerate(prev):
+        assert info[i]["key_iters"] == 1 and info[i]["query_iters"] == 1
+        ref = O.plan_head_warm(q64[i], k64[i], p, i, hp0, max_iter=1, tol=1e-4)
+        # key side: distances in response space, error terms in the metric form
+        qs = q64[i][ref.sampled]
+        X = O.key_features(k64[i], qs, s)
+        dist = O.sq_dists(X, O.key_features(hp0.key_centroids, qs, s))
+        G = s * s * qs.T @ qs
+        A, bias = _metric_terms(k64[i], G, hp0.key_centroids)
+        ok, best = _near_tie_free(dist, A, bias, eps)
+        kmap = np.cumsum(np.bincount(best, minlength=hp0.Ck) > 0) - 1   # compaction of the argmin
+        mism = int(np.sum(g_kl[i][ok] != kmap[best[ok]]))
+        agree = float(np.mean(g_kl[i] == ref.key_labels))
+        say(f"  head {i} keys: {ok.mean():.4f} of rows outside the near-tie bound, {mism} of them differ; "
+            f"all-row agreement {agree:.4f}; groups gpu {info[i]['key_groups']} oracle {ref.Ck}")
+        assert ok.mean() >= 0.5 and mism == 0
+        assert np.array_equal(ref.key_labels, kmap[best])                # the oracle is this argmin
+        # query side: only comparable row by row when both sides hold the same key groups
+        if np.array_equal(g_kl[i], ref.key_labels):
+            L, F = O.query_features(q64[i], ref.key_centroids, s)
+            Z = hp0.query_reps @ ref.key_centroids.T
+            dist = O.sq_dists(F, Z)
+            rms = np.sqrt((L * L).mean(axis=1))
+            alpha = np.where(rms > 0, s / np.where(rms > 0, rms, 1.0), 0.0)
+            Gk = ref.key_centroids.T @ ref.key_centroids
+            A, bias = _metric_terms(alpha[:, None] * q64[i], Gk, hp0.query_reps)
+            ok, best = _near_tie_free(dist, A, bias, eps)
+            qmap = np.cumsum(np.bincount(best, minlength=hp0.Cq) > 0) - 1
+            mism = int(np.sum(g_ql[i][ok] != qmap[best[ok]]))
+            say(f"  head {i} queries: {ok.mean():.4f} of rows outside the near-tie bound, {mism} of them differ; "
+                f"all-row agreement {np.mean(g_ql[i] == ref.query_labels):.4f}")
+            assert ok.mean() >= 0.5 and mism == 0
+        else:
+            qa = float(np.mean(g_ql[i] == ref.query_labels))
+            say(f"  head {i} queries: key labels differ on near ties; query agreement {qa:.4f}")
+            assert qa >= 0.98
+    sp.close()
+
+
+# ---------------------------------------------------------------- (c) group masses from labels
+@pytest.mark.parametrize("case", ["c2 64 groups", "512 groups", "bf16 1 key group", "bf16 2 key groups",
+                                  "bf16 4 key groups", "fp32 4 key groups"])
+def test_group_masses_from_labels_match_oracle(case):
+    if case.startswith("bf16") and "key group" in case:
+        # C_k' <= 4: one half of each lane's centroid block holds no live key group
+        w = configs.with_overrides("c2", heads=2, grid=(4, 16, 16), n_key_groups=int(case.split()[1]),
+                                   n_query_groups=16, n_sampled=64, n_probes=32)
+    elif case.startswith("fp32"):
+        w = configs.with_overrides("c1", n_key_groups=4)
+    elif case == "512 groups":
+        w = _workload(512)
+    else:
+        w = configs.with_overrides("c2", heads=2)
+    heads = list(range(w["heads"]))
+    N, M = configs.seq_len(w), w["n_probes"]
+    say(f"case: group masses from labels, {case} ({w['dtype']}, N={N})")
+    (tq, q64), (tk, k64), (tv, v64) = inputs(w, heads)
+    p = O.call_params(w)
+    s = p["scale"]
+    plans, kls, qls = [], [], []
+    for i in heads:
+        qs = q64[i][O.select_smallest(w["seed"], O.STREAM_SAMPLED, i, np.arange(N), w["n_sampled"])]
+        kl = forgy_labels(O.key_features(k64[i], qs, s), w["n_key_groups"], 5, O.STREAM_KEY_INIT, i)
+        ql = forgy_labels(q64[i], w["n_query_groups"], 5, O.STREAM_QUERY_INIT, i)
+        kls.append(kl)
+        qls.append(ql)
+        plans.append(O.finish_plan(q64[i], k64[i], p, i, O.HeadPlan(key_labels=kl.copy(), query_labels=ql.copy())))
+    sp = SparsePR(config_from_workload(w, heads=len(heads)), device=DEV)
+    sp.plan(tq, tk, torch.from_numpy(np.stack(kls).astype(np.int32)).to(DEV),
+            torch.from_numpy(np.stack(qls).astype(np.int32)).to(DEV), None)
+    torch.cuda.synchronize()
+    u = np_(sp.export("GROUP_MASS")).reshape(len(heads), w["n_query_groups"], w["n_key_groups"])
+    rp, cols = np_(sp.export("ROUTE_ROWPTR")), np_(sp.export("ROUTE_COLS"))
+    info = sp.info()
+    for i, hp in enumerate(plans):
+        ug = u[i, :hp.Cq, :hp.Ck].astype(np.float64) / 2.0 ** 32
+        uo = hp.P
+        err = np.abs(ug - uo)
+        bad = err > MASS_RTOL * uo + MASS_ATOL
+        # each query group's masses are a mean of softmax rows: they sum to one
+        rows = np.abs(ug.sum(axis=1) - 1.0).max()
+        say(f"  head {i}: C_k' {hp.Ck} C_q' {hp.Cq}; max |dP| {err.max():.2e}, max rel "
+            f"{(err / np.maximum(uo, 1e-300))[uo > 1e-6].max() if (uo > 1e-6).any() else 0:.2e}; "
+            f"{int(bad.sum())} entries outside tolerance; max |row sum - 1| {rows:.2e}")
+        assert np.isfinite(ug).all() and not bad.any() and rows <= 1e-4 * max(hp.Ck, 1)
+        # the cells selected with the GPU's masses against the oracle's selection
+        sel_g = {(a, b) for a in range(hp.Cq) for b in cols[i][rp[i][a]:rp[i][a + 1]]}
+        sel_o = {(a, b) for a in range(hp.Cq) for b in hp.route.cols[hp.route.row_ptr[a]:hp.route.row_ptr[a + 1]]}
+        diff = len(sel_g ^ sel_o)
+        say(f"  head {i}: route cells gpu {len(sel_g)} oracle {len(sel_o)}, {diff} differ; "
+            f"density gpu {info[i]['executed_pairs'] / N ** 2:.5f} oracle {hp.pairs / N ** 2:.5f}")
+        # tau moves with the masses only by their error: a few marginal cells may change
+        assert diff <= max(4, 0.01 * len(sel_o))
+        assert info[i]["budget_exceeded"] or info[i]["executed_pairs"] <= np.floor(w["density"] * N * N)
+    sp.close()
+
+
+# ---------------------------------------------------------------- (a) own plan with many groups
+def _inertia(x, labels):
+    C = int(labels.max()) + 1
+    m = O.group_means(x, labels, C)
+    return float(((x - m[labels]) ** 2).sum())
+
+
+_ORACLE_CACHE = {}
+
+
+def _oracle_plans(w, q64, k64, v64, heads):
+    key = (w["n_key_groups"], tuple(heads))
+    if key not in _ORACLE_CACHE:
+        p = O.call_params(w)
+        _ORACLE_CACHE[key] = [O.sparsepr_head(q64[i], k64[i], v64[i], p, head=i) for i in range(len(heads))]
+    return _ORACLE_CACHE[key]
+
+
+@pytest.mark.parametrize("C", [256, 512])
+def test_own_plan_with_many_groups(C):
+    w = _workload(C, n_sampled=256)
+    heads = [0, 1]
+    N, M = configs.seq_len(w), w["n_probes"]
+    (tq, q64), (tk, k64), (tv, v64) = inputs(w, heads)
+    refs = _oracle_plans(w, q64, k64, v64, heads)
+    p = O.call_params(w)
+    s = p["scale"]
+    rng = np.random.default_rng(4)
+    for prec in (0, 1):
+        say(f"case: own plan, C_k = C_q = {C}, precision {prec}")
+        sp = SparsePR(config_from_workload(w, heads=len(heads), assign_precision=prec), device=DEV)
+        sp(tq, tk, tv)
+        torch.cuda.synchronize()
+        info = sp.info()
+        ex = {k: np_(sp.export(k)) for k in ("KEY_LABELS", "QUERY_LABELS", "PROBES")}
+        out = np_(sp.out[0])
+        g_err, o_err = [], []
+        for i, r in enumerate(refs):
+            hp = r.plan
+            qs = q64[i][hp.sampled]
+            X = O.key_features(k64[i], qs, s)
+            ik_g, ik_o = _inertia(X, ex["KEY_LABELS"][i]), _inertia(X, hp.key_labels)
+            _, Fg = O.query_features(q64[i], O.group_means(k64[i], ex["KEY_LABELS"][i], info[i]["key_groups"]), s)
+            iq_g, iq_o = _inertia(Fg, ex["QUERY_LABELS"][i]), _inertia(O.query_features(q64[i], hp.key_centroids, s)[1],
+                                                                      hp.query_labels)
+            ka, qa = np.mean(ex["KEY_LABELS"][i] == hp.key_labels), np.mean(ex["QUERY_LABELS"][i] == hp.query_labels)
+            say(f"  head {i}: iters gpu {info[i]['key_iters']}/{info[i]['query_iters']} oracle "
+                f"{hp.key_iters}/{hp.query_iters}; groups gpu {info[i]['key_groups']}/{info[i]['query_groups']} "
+                f"oracle {hp.Ck}/{hp.Cq}; agreement key {ka:.3f} query {qa:.3f}; inertia ratio gpu/oracle "
+                f"key {ik_g / ik_o:.4f} query {iq_g / iq_o:.4f}")
+            # Lloyd from the same seeds: the runs may part on near ties but must reach
+            # partitions as tight as the oracle's, in a comparable number of iterations
+            assert ik_g <= 1.01 * ik_o and iq_g <= 1.01 * iq_o
+            assert 2 <= info[i]["key_iters"] <= 25 and 2 <= info[i]["query_iters"] <= 25
+            assert abs(info[i]["key_iters"] - hp.key_iters) <= 10 and abs(info[i]["query_iters"] - hp.query_iters) <= 10
+            assert ka >= 0.5 and qa >= 0.3
+            mask = np.ones(N, bool)
+            mask[hp.probes] = False
+            mask[ex["PROBES"][i]] = False
+            rows = np.sort(rng.choice(np.flatnonzero(mask), 2048, replace=False))
+            dn = O.dense_attention(q64[i][rows], k64[i], v64[i], s)
+            g_err.append(O.rel_l2(out[i][rows], dn))
+            o_err.append(O.rel_l2(r.out[rows], dn))
+        g, o = np.concatenate(g_err), np.concatenate(o_err)
+        say(f"  mean unprobed error gpu {g.mean():.4f} oracle {o.mean():.4f}")
+        assert abs(g.mean() - o.mean()) <= 0.05 * o.mean()
+        sp.close()
