@@ -19,6 +19,10 @@ SPARSEPR_ERR_WORKSPACE = 3
 SPARSEPR_ERR_HIP = 4
 SPARSEPR_ERR_NUMERICAL = 5
 SPARSEPR_ERR_STATE = 6
+SPARSEPR_ERR_TOO_LARGE = 7
+
+# include/sparsepr.h SPARSEPR_STATIC_WORKSPACE_BYTES
+STATIC_WORKSPACE_BYTES = 128 << 20
 
 SPARSEPR_F32 = 0
 SPARSEPR_BF16 = 1
@@ -54,6 +58,7 @@ _SIGS = {
     "sparsepr_workspace_bytes": (_SZ, [_P]),
     "sparsepr_plan": (ctypes.c_int, [_P, _P, _P, _P, _SZ, _P]),
     "sparsepr_plan_warm": (ctypes.c_int, [_P, _P, _P, _P, _SZ, _P]),
+    "sparsepr_plan_static": (ctypes.c_int, [_P, _P, _P, _P]),
     "sparsepr_plan_set_probes": (ctypes.c_int, [_P, _P, _P, _P, _SZ, _P]),
     "sparsepr_plan_from_labels": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _P, _SZ, _P]),
     "sparsepr_attend": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _P, _P]),
@@ -153,6 +158,10 @@ def sparsepr_workspace_bytes(plan):
 def sparsepr_plan(plan, q, k, workspace, stream=None):
     _check("sparsepr_plan", lib().sparsepr_plan(plan, _ptr(q), _ptr(k), _ptr(workspace),
                                                 workspace.numel() * workspace.element_size(), _stream(stream)))
+
+
+def sparsepr_plan_static(plan, q, k, stream=None):
+    _check("sparsepr_plan_static", lib().sparsepr_plan_static(plan, _ptr(q), _ptr(k), _stream(stream)))
 
 
 def sparsepr_plan_warm(plan, q, k, workspace, stream=None):

@@ -13,7 +13,8 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 OUT = os.path.join(HERE, "libsparsepr.so")
 BUILD_DIR = os.path.join(HERE, "_build")
-SOURCES = ["plan_kernels.hip", "attn_kernels.hip", "ridge_kernels.hip", "sparsepr_api.hip"]
+SOURCES = ["plan_kernels.hip", "attn_kernels.hip", "ridge_kernels.hip", "sparsepr_api.hip",
+           "static_workspace.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-result",
          # keep the compiler from forming packed fp32 vector ops

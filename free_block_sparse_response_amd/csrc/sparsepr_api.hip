@@ -165,6 +165,7 @@ const char* sparsepr_status_string(sparsepr_status s) {
     case SPARSEPR_ERR_HIP: return "HIP runtime error";
     case SPARSEPR_ERR_NUMERICAL: return "ridge system not positive definite";
     case SPARSEPR_ERR_STATE: return "call out of order";
+    case SPARSEPR_ERR_TOO_LARGE: return "plan needs more device state than the static workspace holds";
   }
   return "unknown status";
 }

@@ -56,7 +56,9 @@ typedef enum {
   SPARSEPR_ERR_WORKSPACE = 3,     /* workspace missing or smaller than required             */
   SPARSEPR_ERR_HIP = 4,           /* a HIP runtime call failed                              */
   SPARSEPR_ERR_NUMERICAL = 5,     /* ridge system not positive definite (device status)    */
-  SPARSEPR_ERR_STATE = 6          /* calls out of order (e.g. attend before plan)           */
+  SPARSEPR_ERR_STATE = 6,         /* calls out of order (e.g. attend before plan)           */
+  SPARSEPR_ERR_TOO_LARGE = 7      /* sparsepr_plan_static: the plan needs more device state */
+                                  /* than SPARSEPR_STATIC_WORKSPACE_BYTES                   */
 } sparsepr_status;
 
 typedef enum { SPARSEPR_F32 = 0, SPARSEPR_BF16 = 1 } sparsepr_dtype;
@@ -146,6 +148,22 @@ size_t sparsepr_workspace_bytes(sparsepr_plan_t plan);
  * q, k: [B,H,N,d] of cfg.dtype. Binds `workspace` to the plan. */
 sparsepr_status sparsepr_plan(sparsepr_plan_t plan, const void* q, const void* k,
                               void* workspace, size_t workspace_bytes, void* stream);
+
+/* For callers that cannot allocate device memory (code under HIP graph capture, tight
+ * serving loops, harnesses that forbid hipMalloc): sparsepr_plan with the plan's device
+ * state placed in a library-owned static device array of SPARSEPR_STATIC_WORKSPACE_BYTES
+ * per GPU instead of a caller workspace. The caller still passes q, k and, later, every
+ * output buffer. Calls no hipMalloc, hipFree or other allocating routine. Returns
+ * SPARSEPR_ERR_TOO_LARGE, before anything is enqueued, when sparsepr_workspace_bytes(plan)
+ * exceeds the limit (128 MiB holds, e.g., 8 heads x 16,384 tokens, d = 128, 64 groups).
+ * Later sparsepr_attend / _fit_residual / _apply / _plan_info / _plan_export /
+ * _plan_set_probes on the handle use the array (on the GPU current at this call);
+ * sparsepr_plan_warm and sparsepr_dense_attention need a caller workspace.
+ * Sharing: every handle planned this way on one GPU uses the one array, which keeps the
+ * last call's contents, so a later sparsepr_plan_static on that GPU replaces the state of
+ * earlier handles; calls that overlap on one GPU (other streams or threads) race. */
+#define SPARSEPR_STATIC_WORKSPACE_BYTES (128u << 20)
+sparsepr_status sparsepr_plan_static(sparsepr_plan_t plan, const void* q, const void* k, void* stream);
 
 /* Warm-started planning for a subsequent call (paper Table C.1: the first k-means runs up
  * to 25 iterations, subsequent ones up to 2). Both k-means start from the groups the
