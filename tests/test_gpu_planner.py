@@ -30,9 +30,11 @@ pytestmark = pytest.mark.gpu
 # the metric and the means come from fp32 sums. A factor of 2 over the first-order bound.
 ASSIGN_EPS = {0: 2.0 ** -8, 1: 2.0 ** -12}
 
-# group masses: logits from bf16 hi/lo products (~2^-16 relative), the hardware exp2
-# (~2^-22), fp32 sums over a tile's rows and a double sum over tiles
-MASS_RTOL = 2e-3
+# group masses: logits from bf16 hi/lo products of the key centroids (the lo part carries
+# the centroid to ~2^-17, so a logit of magnitude |L| <= ~16 in the log2 domain is off by
+# <= ~2^-13, i.e. p by <= ~1e-4 relative), the hardware exp2 (~2^-22), fp32 sums over a
+# tile's rows and a double sum over tiles
+MASS_RTOL = 2e-4
 MASS_ATOL = 2.0 ** -22          # in units of P (probability mass)
 
 
@@ -225,6 +227,12 @@ def _inertia(x, labels):
 
 _ORACLE_CACHE = {}
 
+# label agreement with the oracle's own plan (key, query) at 256 and 512 groups: near ties of
+# the bf16 assignment products send a few rows elsewhere, and Lloyd then moves on from
+# slightly different centroids; measured 0.94-0.96 / 0.87-0.89 (precision 0) and
+# 0.98-1.00 / 0.90-0.94 (precision 1)
+AGREE = {0: (0.90, 0.80), 1: (0.95, 0.85)}
+
 
 def _oracle_plans(w, q64, k64, v64, heads):
     key = (w["n_key_groups"], tuple(heads))
@@ -266,12 +274,13 @@ def test_own_plan_with_many_groups(C):
                 f"{hp.key_iters}/{hp.query_iters}; groups gpu {info[i]['key_groups']}/{info[i]['query_groups']} "
                 f"oracle {hp.Ck}/{hp.Cq}; agreement key {ka:.3f} query {qa:.3f}; inertia ratio gpu/oracle "
                 f"key {ik_g / ik_o:.4f} query {iq_g / iq_o:.4f}")
-            # Lloyd from the same seeds: the runs may part on near ties but must reach
-            # partitions as tight as the oracle's, in a comparable number of iterations
-            assert ik_g <= 1.01 * ik_o and iq_g <= 1.01 * iq_o
+            # Lloyd from the same seeds: the runs may part on near ties (bf16 products) but
+            # must reach partitions as tight as the oracle's, in a comparable number of
+            # iterations, keeping most labels (bounds of the design notes)
+            assert ik_g <= 1.005 * ik_o and iq_g <= 1.005 * iq_o
             assert 2 <= info[i]["key_iters"] <= 25 and 2 <= info[i]["query_iters"] <= 25
-            assert abs(info[i]["key_iters"] - hp.key_iters) <= 10 and abs(info[i]["query_iters"] - hp.query_iters) <= 10
-            assert ka >= 0.5 and qa >= 0.3
+            assert abs(info[i]["key_iters"] - hp.key_iters) <= 5 and abs(info[i]["query_iters"] - hp.query_iters) <= 5
+            assert ka >= AGREE[prec][0] and qa >= AGREE[prec][1]
             mask = np.ones(N, bool)
             mask[hp.probes] = False
             mask[ex["PROBES"][i]] = False
