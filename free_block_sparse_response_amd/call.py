@@ -41,7 +41,8 @@ class SparsePR:
     ``cfg`` keys: batch, heads, seq_len, head_dim, dtype ("f32" / "bf16"), n_sampled,
     n_key_groups, n_query_groups, n_probes, density, ridge_lambda, seed and optionally
     kmeans_max_iter, kmeans_tol, penalize_bias, softmax_scale, assign_precision, warm_iters,
-    partition, correction, probe_selector (comparison settings; 0 = the method), key_rank.
+    partition, correction, probe_selector (comparison settings; 0 = the method), key_rank,
+    attn_tile_rows (128 / 256; 0 = chosen by the average query-group size).
     """
 
     def __init__(self, cfg, device="cuda"):
@@ -55,7 +56,8 @@ class SparsePR:
                                  c.get("kmeans_max_iter", 25), c.get("kmeans_tol", 1e-4), c.get("ridge_lambda", 1e-3),
                                  c.get("penalize_bias", 0), c.get("seed", 0), c.get("softmax_scale", 0.0),
                                  c.get("assign_precision", 0), c.get("warm_iters", 2), c.get("partition", 0),
-                                 c.get("correction", 0), c.get("probe_selector", 0), c.get("key_rank", 0))
+                                 c.get("correction", 0), c.get("probe_selector", 0), c.get("key_rank", 0),
+                                 c.get("attn_tile_rows", 0))
         self.plan_h = L.sparsepr_plan_create(self._cc)
         self.ws = torch.empty(L.sparsepr_workspace_bytes(self.plan_h), dtype=torch.uint8, device=device)
         shape = (c["batch"], c["heads"], self.N, self.d)
@@ -177,7 +179,7 @@ def config_from_workload(w, **over):
              n_probes=w["n_probes"], density=w["density"], ridge_lambda=w["ridge_lambda"], seed=w["seed"],
              kmeans_max_iter=KMEANS_MAX_ITER, kmeans_tol=KMEANS_TOL,
              softmax_scale=w.get("scale", 1.0 / math.sqrt(w["head_dim"])))
-    for key in ("partition", "correction", "probe_selector", "key_rank"):
+    for key in ("partition", "correction", "probe_selector", "key_rank", "attn_tile_rows"):
         if key in w:
             c[key] = w[key]
     c.update(over)

@@ -117,63 +117,78 @@ struct TileWalk {
 };
 
 // -------------------------------------------------------------------------------------
-// bf16 MFMA kernel. MODE 0: block-sparse tiles from the tile table, bf16 output in token
-// order (plus float rows for probes). MODE 1: probe rows (128 per block) over one chunk of
-// all keys, partial outputs for the chunk combine. MODE 2: the same code as MODE 0 under its
-// own symbol, used by the dense reference call so that traces keep the two apart.
+// bf16 MFMA kernel, W waves of 32 query rows per workgroup (a tile of up to 32 W rows of one
+// query group), KT keys per step (a multiple of 32). MODE 0: block-sparse tiles from the
+// attention tile table, bf16 output in token order (plus float rows for probes). MODE 1:
+// probe rows (32 W per block) over one chunk of all keys, partial outputs for the chunk
+// combine. MODE 2: the same code as MODE 0 under its own symbol, used by the dense
+// reference call so that traces keep the two apart.
 //
-// Tiles of 32 keys move HBM -> registers -> LDS, two steps ahead: a step issues the global
-// loads of K(j+2) and V(j+1) and stores K(j+1) and V(j), loaded a step earlier, at its end
-// (direct-to-LDS loads were tried: while they are in flight the operand reads of every wave
-// on the CU stall). Rows carry an XOR swizzle of their 16-byte chunks so that the operand
-// reads are bank-conflict free without padding.
+// Tiles of KT keys move HBM -> registers -> LDS, STG steps ahead: a step issues the global
+// loads of K(j+STG) and V(j+STG-1) and stores, at its end, the K and V tiles it loaded STG-1
+// steps earlier (direct-to-LDS loads were tried: while they are in flight the operand reads
+// of every wave on the CU stall). Rows carry an XOR swizzle of their 16-byte chunks so that
+// the operand reads are bank-conflict free without padding (16 lanes of a 128-bit read
+// cover the 64 banks).
 //
-// Step j (one barrier): S(j) = K(j) Q^T on the matrix cores; then O += V(j-1) P(j-1), each
+// Step j (one barrier): S(j) = K(j) Q^T on the matrix cores, one 32-key sub-block per
+// accumulator, the sub-blocks' product chains interleaved; then O += V(j-1) P(j-1), each
 // MFMA followed by a slice of the softmax that turns S(j) into P(j) (P is double-buffered in
-// registers). The K rows of a 32-key block are read in the order pi (bits 2 and 3 of the row
-// swapped), which makes the eight scores a lane holds for one 16-key chunk eight consecutive
-// keys, so the V^T operand is a single 16-byte read per MFMA.
+// registers). The K rows of a 32-key block are read in the order pi (bits 2 and 3 of the
+// row swapped), which makes the eight scores a lane holds for one 16-key chunk eight
+// consecutive keys, so the V^T operand is a single 16-byte read per MFMA. Operand reads run
+// PF products ahead.
 // The reference max is lazy: a tile is exponentiated against the running max, and only a
 // tile whose numerators could exceed 2^16 is redone against its exact max (then the
 // accumulator is rescaled before the next PV product).
 // -------------------------------------------------------------------------------------
 __device__ inline int swap_bits23(int x) { return (x & ~12) | ((x & 4) << 1) | ((x & 8) >> 1); }
 
-template <int DD, int MODE>
-__global__ __launch_bounds__(256, 2) void k_bsfa_bf16(const bf16* __restrict__ q, Dims D, Bufs B, void* out,
-                                                        float* psp) {
-  constexpr int KT = 32;                // keys per tile
-  constexpr int KRB = DD * 2;           // K row bytes (256 or 128)
-  constexpr int KW = KRB / 16;          // 16-byte slots per K row (16 or 8)
-  constexpr int KR = 64 / KW;           // K rows per wave-wide 1 KB load
-  constexpr int KI = KT * KRB / 4096;   // 1 KB loads per wave per K tile (4 waves)
-  constexpr int VI = DD * KT * 2 / 4096;  // and per V^T tile (rows of 64 bytes)
-  constexpr int NC = DD / 16;           // k-chunks of the QK^T product
-  constexpr int ND = DD / 32;           // 32-wide d blocks of the output
-  static_assert((DD == 64 || DD == 128) && KI >= 1 && VI >= 1, "tile shape");
-  __shared__ __attribute__((aligned(1024))) bf16 Kb0[KT * DD], Kb1[KT * DD], Vb0[DD * KT], Vb1[DD * KT];
+template <int DD, int MODE, int W, int KT, int STG>
+__global__ __launch_bounds__(64 * W, W == 4 ? 2 : 1) void k_bsfa_bf16(const bf16* __restrict__ q, Dims D, Bufs B,
+                                                                       void* out, float* psp) {
+  constexpr int KRB = DD * 2;                // K row bytes (256 or 128)
+  constexpr int KW = KRB / 16;               // 16-byte slots per K row (16 or 8)
+  constexpr int KR = 64 / KW;                // K rows per wave-wide 1 KB load
+  constexpr int KI = KT * KRB / (1024 * W);  // 1 KB loads per wave per K tile
+  constexpr int VRB = KT * 2;                // V^T row bytes (keys of one dim)
+  constexpr int VW = VRB / 16;               // 16-byte slots per V^T row
+  constexpr int VR = 1024 / VRB;             // V^T rows per wave-wide 1 KB load
+  constexpr int VI = DD * VRB / (1024 * W);  // 1 KB loads per wave per V^T tile
+  constexpr int NC = DD / 16;                // k-chunks of the QK^T product
+  constexpr int ND = DD / 32;                // 32-wide d blocks of the output
+  constexpr int SB = KT / 32;                // 32-key sub-blocks per tile
+  constexpr int NCC = KT / 16;               // 16-key chunks of P per tile
+  constexpr int NPV = NCC * ND;              // PV products per step
+  constexpr int NPAIR = 8 * SB;              // score pairs per lane per step
+  constexpr int PF = 4;                      // operand reads ahead of their product
+  constexpr int QT = 32 * W;                 // query rows per tile
+  static_assert((DD == 64 || DD == 128) && KI >= 1 && VI >= 1 && (KT == 32 || KT == 64), "tile shape");
+  static_assert(STG == 1 || STG == 2, "staging depth");
+  __shared__ __attribute__((aligned(1024))) bf16 Kb[2][KT * DD];
+  __shared__ __attribute__((aligned(1024))) bf16 Vb[2][DD * KT];
   __shared__ int2 runs_s[kMaxGroups];
 
   const int nb = gridDim.x;
   const int bid = xcd_remap(blockIdx.x, nb);
   int bh, rows, a = 0, pos0 = 0;
   if (MODE != 1) {
-    bh = bid / D.max_tiles;
-    const int t = bid % D.max_tiles;
-    if (t >= B.ntiles[bh]) return;
-    const int2 tl = B.tiles[(size_t)bh * D.max_tiles + t];
+    bh = bid / D.max_atiles;
+    const int t = bid % D.max_atiles;
+    if (t >= B.antiles[bh]) return;
+    const int2 tl = B.atiles[(size_t)bh * D.max_atiles + t];
     a = tl.x;
     pos0 = tl.y;
     const int end = B.qoff[(size_t)bh * (D.Cq + 1) + a + 1];
-    rows = min(D.qt, end - pos0);
+    rows = min(QT, end - pos0);
   } else {
-    // probe rows: (head, 128-row tile, key chunk)
-    const int per = ((D.M + kAttnQT - 1) / kAttnQT) * D.pch;
+    // probe rows: (head, QT-row tile, key chunk)
+    const int per = ((D.M + QT - 1) / QT) * D.pch;
     bh = bid / per;
     const int rem = bid % per;
-    pos0 = (rem / D.pch) * kAttnQT;
+    pos0 = (rem / D.pch) * QT;
     a = rem % D.pch;  // key chunk
-    rows = min(kAttnQT, D.M - pos0);
+    rows = min(QT, D.M - pos0);
   }
   const int tid = threadIdx.x, l = lane_id(), h = l >> 5, l32 = l & 31;
   const int w = __builtin_amdgcn_readfirstlane(tid / kWave);
@@ -202,92 +217,100 @@ __global__ __launch_bounds__(256, 2) void k_bsfa_bf16(const bf16* __restrict__ q
   const bf16* vtb = (const bf16*)B.vpt + (size_t)bh * DD * D.Npad;
 
   // Tile layout in LDS, no padding: 16-byte slot s of row r holds chunk s ^ swz(r), with
-  // swz(r) = r & 15 for 16-slot K rows, (r >> 1) & 7 for 8-slot K rows and (r >> 2) & 3 for
-  // the 4-slot V^T rows, so the 16 rows one operand read touches fall on distinct bank groups.
-  // Each wave stages whole 1 KB row blocks; the chunk a lane fetches depends on its lane and
-  // wave only, so its source is one lane offset plus a per-load scalar.
+  // swz(r) = r & 15 for 16-slot rows and (r >> 1) & 7 for 8-slot rows (K rows of d = 64,
+  // V^T rows of 64 keys), (r >> 2) & 3 for the 4-slot V^T rows of 32 keys, so the 16 rows one
+  // 16-lane group of an operand read touches fall on distinct banks. Each wave stages whole
+  // 1 KB row blocks; the chunk a lane fetches depends on its lane and wave only, so its
+  // source is one lane offset plus a per-load scalar.
   auto kswz = [](int r) { return KW == 16 ? (r & 15) : ((r >> 1) & 7); };
-  auto vswz = [](int r) { return (r >> 2) & 3; };
+  auto vswz = [](int r) { return VW == 4 ? ((r >> 2) & 3) : (VW == 8 ? ((r >> 1) & 7) : (r & 15)); };
   unsigned klane, vlane;
   {
-    const int r = KR * w + l / KW;  // row of this lane in the wave's first load (load g = 4 i + w)
+    const int r = KR * w + l / KW;  // row of this lane in the wave's first load (load g = W i + w)
     klane = (unsigned)(r * KRB + 16 * ((l % KW) ^ kswz(r)));
-    const int rv = 16 * w + l / 4;
-    vlane = (unsigned)(rv * 2 * D.Npad + 16 * ((l % 4) ^ vswz(rv)));
+    const int rv = VR * w + l / VW;
+    vlane = (unsigned)(rv * 2 * D.Npad + 16 * ((l % VW) ^ vswz(rv)));
   }
-  // Tile staging through registers, two steps deep: the global loads issued in one step are
-  // stored to LDS at the end of the next, so a load has about two steps to arrive. Every step
-  // issues the same loads (past the last tile they re-read the current one, unused), so the
-  // count of loads in flight is the same on every path and the wait before a store covers
-  // only the loads of the step before.
+  // Every step issues the same loads (past the last tile they re-read the current one,
+  // unused), so the count of loads in flight is the same on every path and the wait before
+  // a store covers only the loads issued STG - 1 steps before.
   struct Stage {
     bf16x8 k[KI], v[VI];
   };
   auto load_k = [&](Stage& st, int k0) {
     const char* src = (const char*)(kpb + (size_t)k0 * DD);
 #pragma unroll
-    for (int i = 0; i < KI; ++i) st.k[i] = *reinterpret_cast<const bf16x8*>(src + i * 4 * KR * KRB + klane);
+    for (int i = 0; i < KI; ++i) st.k[i] = *reinterpret_cast<const bf16x8*>(src + i * W * KR * KRB + klane);
   };
   auto load_v = [&](Stage& st, int k0) {
     const char* src = (const char*)(vtb + k0);
 #pragma unroll
-    for (int i = 0; i < VI; ++i) st.v[i] = *reinterpret_cast<const bf16x8*>(src + (size_t)i * 128 * D.Npad + vlane);
+    for (int i = 0; i < VI; ++i)
+      st.v[i] = *reinterpret_cast<const bf16x8*>(src + (size_t)i * W * VR * 2 * D.Npad + vlane);
   };
   auto store_k = [&](const Stage& st, bf16* dst) {
 #pragma unroll
-    for (int i = 0; i < KI; ++i) *reinterpret_cast<bf16x8*>(dst + (4 * i + w) * 512 + 8 * l) = st.k[i];
+    for (int i = 0; i < KI; ++i) *reinterpret_cast<bf16x8*>(dst + (W * i + w) * 512 + 8 * l) = st.k[i];
   };
   auto store_v = [&](const Stage& st, bf16* dst) {
 #pragma unroll
-    for (int i = 0; i < VI; ++i) *reinterpret_cast<bf16x8*>(dst + (4 * i + w) * 512 + 8 * l) = st.v[i];
+    for (int i = 0; i < VI; ++i) *reinterpret_cast<bf16x8*>(dst + (W * i + w) * 512 + 8 * l) = st.v[i];
   };
 
-  // operand reads. K: row pi(l32), chunk 2c + h -> byte kaddr ^ 32c;
+  // operand reads. K: row 32 sb + pi(l32), chunk 2c + h -> byte sb * 32 rows + (kaddr ^ 32c);
   // V^T: row 32 db + l32, chunk 2cc + h -> byte (vaddr ^ 32cc) + db * 32 rows.
   const int prow = swap_bits23(l32);
   const unsigned kaddr = (unsigned)(prow * KRB + 16 * (h ^ kswz(prow)));
-  const unsigned vaddr = (unsigned)(l32 * 64 + 16 * (h ^ vswz(l32)));
-  // The per-chunk addresses are formed where they are used (one v_xor each): an empty asm
-  // makes the base opaque so that the compiler does not keep all of them live across the loop.
-  auto kread = [&](const bf16* Kc, unsigned kb, int c) {
-    return *reinterpret_cast<const bf16x8*>((const char*)Kc + (kb ^ (32u * c)));
+  const unsigned vaddr = (unsigned)(l32 * VRB + 16 * (h ^ vswz(l32)));
+  auto kread = [&](const bf16* Kc, unsigned kb, int i) {  // i = sb * NC + c
+    const int sb = i / NC, c = i % NC;
+    return *reinterpret_cast<const bf16x8*>((const char*)Kc + sb * 32 * KRB + (kb ^ (32u * c)));
   };
   auto vread = [&](const bf16* Vc, unsigned vb, int i) {  // i = cc * ND + db
     const int cc = i / ND, db = i % ND;
-    return *reinterpret_cast<const bf16x8*>((const char*)Vc + db * 32 * 64 + (vb ^ (32u * cc)));
+    return *reinterpret_cast<const bf16x8*>((const char*)Vc + db * 32 * VRB + (vb ^ (32u * cc)));
   };
-  // S^T = K Q^T of one tile; K operands read two k-chunks ahead
-  auto qk = [&](const bf16* Kc, f32x16& s) {
+  // S^T = K Q^T of one tile: product j is chunk j / SB of sub-block j % SB, so consecutive
+  // products feed different accumulators. The per-chunk addresses are formed where they are
+  // used (one v_xor each): an empty asm makes the base opaque so that the compiler does not
+  // keep all of them live across the loop.
+  auto qk = [&](const bf16* Kc, f32x16 (&s)[SB]) {
     unsigned kb = kaddr;
     asm volatile("" : "+v"(kb));
-    bf16x8 ka[NC];
-    ka[0] = kread(Kc, kb, 0);
-    ka[1] = kread(Kc, kb, 1);
+    constexpr int NI = NC * SB;
+    auto idx = [](int j) { return (j % SB) * NC + j / SB; };
+    bf16x8 ka[NI];
 #pragma unroll
-    for (int c = 0; c < NC; ++c) {
+    for (int j = 0; j < PF; ++j) ka[j] = kread(Kc, kb, idx(j));
+#pragma unroll
+    for (int j = 0; j < NI; ++j) {
+      const int sb = j % SB, c = j / SB;
       if (c == 0) {
         const f32x16 z = {};
-        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[0], qreg[0], z, 0, 0, 0);
+        s[sb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[j], qreg[0], z, 0, 0, 0);
       } else {
-        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[c], qreg[c], s, 0, 0, 0);
+        s[sb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[j], qreg[c], s[sb], 0, 0, 0);
       }
-      if (c + 2 < NC) ka[c + 2] = kread(Kc, kb, c + 2);
+      if (j + PF < NI) ka[j + PF] = kread(Kc, kb, idx(j + PF));
       __builtin_amdgcn_sched_barrier(0);
     }
   };
-  // keys outside [lo, hi) of an edge tile get score -inf; score v is key
-  // 16 (v >> 3) + 8 h + (v & 7) of the tile (pi order)
-  auto mask = [&](f32x16& s, int k0, int lo, int hi) {
-    const int vlo = lo - k0 - 8 * h, vhi = hi - k0 - 8 * h;
-    if (lo > k0) {
+  // keys outside [lo, hi) of an edge tile get score -inf; score v of sub-block sb is key
+  // 32 sb + 16 (v >> 3) + 8 h + (v & 7) of the tile (pi order)
+  auto mask = [&](f32x16 (&s)[SB], int k0, int lo, int hi) {
 #pragma unroll
-      for (int v = 0; v < 16; ++v)
-        if (16 * (v >> 3) + (v & 7) < vlo) s[v] = -INFINITY;
-    }
-    if (hi < k0 + KT) {
+    for (int sb = 0; sb < SB; ++sb) {
+      const int vlo = lo - k0 - 32 * sb - 8 * h, vhi = hi - k0 - 32 * sb - 8 * h;
+      if (lo > k0 + 32 * sb) {
 #pragma unroll
-      for (int v = 0; v < 16; ++v)
-        if (16 * (v >> 3) + (v & 7) >= vhi) s[v] = -INFINITY;
+        for (int v = 0; v < 16; ++v)
+          if (16 * (v >> 3) + (v & 7) < vlo) s[sb][v] = -INFINITY;
+      }
+      if (hi < k0 + 32 * sb + 32) {
+#pragma unroll
+        for (int v = 0; v < 16; ++v)
+          if (16 * (v >> 3) + (v & 7) >= vhi) s[sb][v] = -INFINITY;
+      }
     }
   };
   auto max16 = [&](const f32x16& s) {  // max of the 16 scores (v_max3 tree)
@@ -311,12 +334,14 @@ __global__ __launch_bounds__(256, 2) void k_bsfa_bf16(const bf16* __restrict__ q
   // Softmax numerators of one tile against the reference max mu, in pairs of scores: scale
   // and shift, exponentiate, pack to bf16 and add the packed pair to the row sum (one
   // v_dot2 with (1, 1), so the sum is of the same rounded values that enter PV). Pair g
-  // goes through a three-slice pipeline (shift in slice g, exp in g+1, pack in g+2); slices
-  // 0-7 each follow one MFMA of the previous tile's PV product, 8 and 9 close the pipeline.
+  // (scores 2g, 2g + 1 of sub-block g / 8) goes through a three-slice pipeline (shift in
+  // slice g, exp in g+1, pack in g+2) and lands in P chunk g / 4; the slices follow the
+  // MFMAs of the previous tile's PV product, the last two close the pipeline.
   const bf16x2 ones = {(bf16)1.f, (bf16)1.f};
-  auto soft_slice = [&](const f32x16& s, int i, float mu, float& ps, float (&xe)[16], bf16x8 (&pn)[2]) {
+  auto soft_slice = [&](const f32x16 (&s)[SB], int i, float mu, float& ps, float (&xe)[2 * NPAIR],
+                        bf16x8 (&pn)[NCC]) {
     const int gp = i - 2, ge = i - 1, gf = i;
-    if (gp >= 0 && gp < 8) {
+    if (gp >= 0 && gp < NPAIR) {
       bf16x2 pr;
       pr[0] = (bf16)xe[2 * gp];
       pr[1] = (bf16)xe[2 * gp + 1];
@@ -324,13 +349,14 @@ __global__ __launch_bounds__(256, 2) void k_bsfa_bf16(const bf16* __restrict__ q
       pn[gp >> 2][2 * (gp & 3) + 1] = pr[1];
       ps = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, ps, false);
     }
-    if (ge >= 0 && ge < 8) {
+    if (ge >= 0 && ge < NPAIR) {
       xe[2 * ge] = __builtin_amdgcn_exp2f(xe[2 * ge]);
       xe[2 * ge + 1] = __builtin_amdgcn_exp2f(xe[2 * ge + 1]);
     }
-    if (gf < 8) {
-      xe[2 * gf] = fmaf(s[2 * gf], c2, -mu);
-      xe[2 * gf + 1] = fmaf(s[2 * gf + 1], c2, -mu);
+    if (gf < NPAIR) {
+      const int sb = gf / 8, v = 2 * (gf % 8);
+      xe[2 * gf] = fmaf(s[sb][v], c2, -mu);
+      xe[2 * gf + 1] = fmaf(s[sb][v + 1], c2, -mu);
     }
   };
   // The reference max is kept lazily: numerators are formed against the running max, and
@@ -338,62 +364,63 @@ __global__ __launch_bounds__(256, 2) void k_bsfa_bf16(const bf16* __restrict__ q
   // large, or infinite) is the tile redone against its exact max; the first tile of a work
   // item, with no max yet, always is. Every numerator kept is therefore <= 2^16: far from
   // overflow in fp32, and bf16 keeps its relative precision at any magnitude.
-  auto soft_exact = [&](const f32x16& s, float& mu, float& ps, bf16x8 (&pn)[2]) {
-    const float mt = max16(s);
+  auto soft_exact = [&](const f32x16 (&s)[SB], float& mu, float& ps, bf16x8 (&pn)[NCC]) {
+    float mt = max16(s[0]);
+#pragma unroll
+    for (int sb = 1; sb < SB; ++sb) mt = fmaxf(mt, max16(s[sb]));
     mu = fmaxf(mu, fmaxf(mt, xor32(mt)) * c2);
     ps = 0.f;
-    float xe[16];
+    float xe[2 * NPAIR];
 #pragma unroll
-    for (int i = 0; i < 10; ++i) soft_slice(s, i, mu, ps, xe, pn);
+    for (int i = 0; i < NPAIR + 2; ++i) soft_slice(s, i, mu, ps, xe, pn);
   };
-  auto check = [&](const f32x16& s, float& mu, float& ps, bf16x8 (&pn)[2]) {
+  auto check = [&](const f32x16 (&s)[SB], float& mu, float& ps, bf16x8 (&pn)[NCC]) {
     if (__builtin_amdgcn_ballot_w64(!(ps <= 65536.f))) soft_exact(s, mu, ps, pn);
   };
-  // O^T += V^T P^T of the previous tile (V operands two MFMAs ahead) interleaved with the
-  // softmax numerators of the current tile
-  auto pv_soft = [&](const bf16* Vp, const bf16x8 (&pp)[2], const f32x16& s, float& mu, float& ps,
-                     bf16x8 (&pn)[2]) {
-    constexpr int NI = 2 * ND;
+  // O^T += V^T P^T of the previous tile interleaved with the softmax numerators of the
+  // current tile
+  auto pv_soft = [&](const bf16* Vp, const bf16x8 (&pp)[NCC], const f32x16 (&s)[SB], float& mu, float& ps,
+                     bf16x8 (&pn)[NCC]) {
     unsigned vb = vaddr;
     asm volatile("" : "+v"(vb));
-    bf16x8 va[NI];
-    va[0] = vread(Vp, vb, 0);
-    va[1] = vread(Vp, vb, 1);
-    float xe[16];
-    ps = 0.f;
+    bf16x8 va[NPV];
 #pragma unroll
-    for (int i = 0; i < 10; ++i) {
-      if (i < NI) {
+    for (int j = 0; j < PF; ++j) va[j] = vread(Vp, vb, j);
+    float xe[2 * NPAIR];
+    ps = 0.f;
+    constexpr int NS = NPV > NPAIR + 2 ? NPV : NPAIR + 2;
+#pragma unroll
+    for (int i = 0; i < NS; ++i) {
+      if (i < NPV) {
         const int cc = i / ND, db = i % ND;
         o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[i], pp[cc], o[db], 0, 0, 0);
-        if (i + 2 < NI) va[i + 2] = vread(Vp, vb, i + 2);
+        if (i + PF < NPV) va[i + PF] = vread(Vp, vb, i + PF);
       }
-      soft_slice(s, i, mu, ps, xe, pn);
+      if (i < NPAIR + 2) soft_slice(s, i, mu, ps, xe, pn);
       __builtin_amdgcn_sched_barrier(0);
     }
     check(s, mu, ps, pn);
   };
-  auto pv = [&](const bf16* Vp, const bf16x8 (&pp)[2]) {
-    constexpr int NI = 2 * ND;
+  auto pv = [&](const bf16* Vp, const bf16x8 (&pp)[NCC]) {
     unsigned vb = vaddr;
     asm volatile("" : "+v"(vb));
-    bf16x8 va[NI];
-    va[0] = vread(Vp, vb, 0);
-    va[1] = vread(Vp, vb, 1);
+    bf16x8 va[NPV];
 #pragma unroll
-    for (int i = 0; i < NI; ++i) {
+    for (int j = 0; j < PF; ++j) va[j] = vread(Vp, vb, j);
+#pragma unroll
+    for (int i = 0; i < NPV; ++i) {
       const int cc = i / ND, db = i % ND;
       o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[i], pp[cc], o[db], 0, 0, 0);
-      if (i + 2 < NI) va[i + 2] = vread(Vp, vb, i + 2);
+      if (i + PF < NPV) va[i + PF] = vread(Vp, vb, i + PF);
       __builtin_amdgcn_sched_barrier(0);
     }
   };
   TileWalk<KT> ts;
-  bool has;  // the next tile exists
+  bool has;  // the first tile exists
   if (MODE != 1) {
     const int2* rg = B.runs + (size_t)bh * D.Cq * D.Ck + B.row_ptr[(size_t)bh * (D.Cq + 1) + a];
     const int nr = __builtin_amdgcn_readfirstlane(B.nruns[(size_t)bh * D.Cq + a]);  // <= C_k <= kMaxGroups
-    for (int i = tid; i < nr; i += 256) runs_s[i] = rg[i];
+    for (int i = tid; i < nr; i += 64 * W) runs_s[i] = rg[i];
     __syncthreads();
     ts.runs = runs_s;
     ts.nr = nr;
@@ -402,82 +429,106 @@ __global__ __launch_bounds__(256, 2) void k_bsfa_bf16(const bf16* __restrict__ q
     const int clo = a * D.pkc;
     has = ts.first_single(clo, min(D.N, clo + D.pkc));
   }
-  // Tile j: K(j) sits in K buffer j%2 and V(j) in V buffer j%2. Step j (j >= 1) loads K(j+1)
-  // and V(j) into registers, forms S(j), runs O += V(j-1) P(j-1) while it turns S(j) into
-  // P(j), and stores the loaded tiles at its end. P is double-buffered in registers (pa, pb
-  // by parity); the max and row sum of P(j) are applied (rescale, sum) at the start of step
-  // j+1, after P(j-1) has entered O. Tile 0 is handled before the loop and the last PV after
-  // it, so every step runs the same code and O never changes registers.
-  bf16x8 pp[2];  // P^T operands of the pending tile
+  // Tile j: K(j) sits in K buffer j%2 and V(j) in V buffer j%2. Step j (j >= 1) loads K(j+STG)
+  // and V(j+STG-1) into registers, forms S(j), runs O += V(j-1) P(j-1) while it turns S(j)
+  // into P(j), and stores at its end K(j+1) and V(j), loaded STG-1 steps earlier. P is
+  // double-buffered in registers; the max and row sum of P(j) are applied (rescale, sum) at
+  // the start of step j+1, after P(j-1) has entered O. Tile 0 is handled before the loop and
+  // the last PV after it, so every step runs the same code and O never changes registers.
+  // Tile descriptors (k0, lo, hi) run STG steps ahead of the compute.
+  bf16x8 pp[NCC];  // P^T operands of the pending tile
   float mu = -INFINITY, ps = 0.f;
   if (has) {
-    // tile descriptors: j (current), j+1, j+2
     int k0c = ts.k0, loc = ts.lo, hic = ts.hi;
     bool has1 = ts.next();
     int k01 = ts.k0, lo1 = ts.lo, hi1 = ts.hi;
-    bool has2 = has1 && ts.next();
-    int k02 = ts.k0;
-    Stage sa, sb;  // sa: K(j+1), V(j) (stored at the end of step j); sb: K(j+2), V(j+1)
-    load_k(sa, k0c);
-    store_k(sa, Kb0);
-    load_k(sa, has1 ? k01 : k0c);
-    load_v(sa, k0c);
-    // Step j: K(j) is in K buffer j%2, V(j-1) in V buffer (j-1)%2. Load K(j+2) and V(j+1);
-    // S(j) = K(j) Q^T; O += V(j-1) P(j-1) while S(j) turns into P(j); store K(j+1) and V(j).
-    // Step 0 has no PV; one loop body serves both parities, so O keeps its registers.
-    __syncthreads();
-    load_k(sb, has2 ? k02 : k0c);
-    load_v(sb, has1 ? k01 : k0c);
-    if (wave_active) {
-      f32x16 s;
-      qk(Kb0, s);
-      if (loc > k0c || hic < k0c + KT) mask(s, k0c, loc, hic);
-      soft_exact(s, mu, ps, pp);
-    }
-    if (has1) store_k(sa, Kb1);
-    store_v(sa, Vb0);
-    int par = 0;  // parity of the last tile
-    // step of tile j; `cur` holds K(j+1), V(j) (loaded a step ago), `nxt` receives K(j+2), V(j+1)
-    auto step = [&](Stage& cur, Stage& nxt) {
-      k0c = k01; loc = lo1; hic = hi1;
-      has1 = has2;
-      k01 = k02; lo1 = ts.lo; hi1 = ts.hi;
-      has2 = has2 && ts.next();
-      k02 = ts.k0;
-      par ^= 1;
-      const bf16* Kc = par ? Kb1 : Kb0;
-      bf16* Kn = par ? Kb0 : Kb1;
-      const bf16* Vp = par ? Vb0 : Vb1;
-      bf16* Vc = par ? Vb1 : Vb0;
-      __syncthreads();
-      load_k(nxt, has2 ? k02 : k0c);
-      load_v(nxt, has1 ? k01 : k0c);
+    bool has2 = STG == 2 && has1 && ts.next();  // STG 2 only: the tile after next
+    int k02 = STG == 2 ? ts.k0 : 0;
+    int par = 0;  // parity of the current tile
+    auto compute_first = [&]() {
+      if (wave_active) {
+        f32x16 s[SB];
+        qk(Kb[0], s);
+        if (loc > k0c || hic < k0c + KT) mask(s, k0c, loc, hic);
+        soft_exact(s, mu, ps, pp);
+      }
+    };
+    auto compute_step = [&]() {
       if (wave_active) {
         rescale(mu);
         l_half += ps;
-        f32x16 s;
-        qk(Kc, s);
+        f32x16 s[SB];
+        qk(Kb[par], s);
         if (loc > k0c || hic < k0c + KT) mask(s, k0c, loc, hic);
-        bf16x8 pn[2];
-        pv_soft(Vp, pp, s, mu, ps, pn);
-        pp[0] = pn[0];
-        pp[1] = pn[1];
+        bf16x8 pn[NCC];
+        pv_soft(Vb[par ^ 1], pp, s, mu, ps, pn);
+#pragma unroll
+        for (int c = 0; c < NCC; ++c) pp[c] = pn[c];
       }
-      if (has1) store_k(cur, Kn);
-      store_v(cur, Vc);
     };
-    // whole pairs of steps (stages swap roles twice), then at most one more step
-    while (has1 && has2) {
-      step(sb, sa);
-      step(sa, sb);
+    if (STG == 2) {
+      Stage sa, sb;  // sa: K(j+1), V(j) (stored at the end of step j); sb: K(j+2), V(j+1)
+      load_k(sa, k0c);
+      store_k(sa, Kb[0]);
+      load_k(sa, has1 ? k01 : k0c);
+      load_v(sa, k0c);
+      __syncthreads();
+      load_k(sb, has2 ? k02 : k0c);
+      load_v(sb, has1 ? k01 : k0c);
+      compute_first();
+      if (has1) store_k(sa, Kb[1]);
+      store_v(sa, Vb[0]);
+      // step of tile j; `cur` holds K(j+1), V(j) (loaded a step ago), `nxt` receives K(j+2), V(j+1)
+      auto step = [&](Stage& cur, Stage& nxt) {
+        k0c = k01; loc = lo1; hic = hi1;
+        has1 = has2;
+        k01 = k02; lo1 = ts.lo; hi1 = ts.hi;
+        has2 = has2 && ts.next();
+        k02 = ts.k0;
+        par ^= 1;
+        __syncthreads();
+        load_k(nxt, has2 ? k02 : k0c);
+        load_v(nxt, has1 ? k01 : k0c);
+        compute_step();
+        if (has1) store_k(cur, Kb[par ^ 1]);
+        store_v(cur, Vb[par]);
+      };
+      // whole pairs of steps (stages swap roles twice), then at most one more step
+      while (has1 && has2) {
+        step(sb, sa);
+        step(sa, sb);
+      }
+      if (has1) step(sb, sa);
+    } else {
+      Stage sa;  // K(j+1), V(j): loaded at the start of step j, stored at its end
+      load_k(sa, k0c);
+      store_k(sa, Kb[0]);
+      __syncthreads();
+      load_k(sa, has1 ? k01 : k0c);
+      load_v(sa, k0c);
+      compute_first();
+      if (has1) store_k(sa, Kb[1]);
+      store_v(sa, Vb[0]);
+      while (has1) {
+        const int k0v = k01;  // V(j) of the step below
+        k0c = k01; loc = lo1; hic = hi1;
+        has1 = ts.next();
+        k01 = ts.k0; lo1 = ts.lo; hi1 = ts.hi;
+        par ^= 1;
+        __syncthreads();
+        load_k(sa, has1 ? k01 : k0c);
+        load_v(sa, k0v);
+        compute_step();
+        if (has1) store_k(sa, Kb[par ^ 1]);
+        store_v(sa, Vb[par]);
+      }
     }
-    if (has1) step(sb, sa);
     // O += V(T-1) P(T-1), V(T-1) in V buffer par
     __syncthreads();
     if (wave_active) {
       rescale(mu);
       l_half += ps;
-      pv(par ? Vb1 : Vb0, pp);
+      pv(Vb[par], pp);
     }
   }
 
@@ -656,22 +707,30 @@ __global__ __launch_bounds__(128) void k_bsfa_f32(const float* __restrict__ q, D
   }
 }
 
+template <int DD, int MODE>
+static void launch_bsfa(const Dims& D, const Bufs& B, const bf16* q, void* out, float* psp, int nb, hipStream_t s) {
+  // 64 keys per step; 8-wave tiles stage two steps ahead, 4-wave tiles (two workgroups per
+  // CU, half the registers each) one step ahead
+  if (D.attn_w == 8)
+    hipLaunchKernelGGL((k_bsfa_bf16<DD, MODE, 8, 64, 2>), dim3(nb), dim3(512), 0, s, q, D, B, out, psp);
+  else
+    hipLaunchKernelGGL((k_bsfa_bf16<DD, MODE, 4, 64, 1>), dim3(nb), dim3(256), 0, s, q, D, B, out, psp);
+}
+
 void launch_attend_sparse(const void* q, const Dims& D, const Bufs& B, void* o_sparse, float* o_psp, hipStream_t s,
                           bool dense) {
-  const int nb = D.BH * D.max_tiles;
   if (D.dtype == 1) {
+    const int nb = D.BH * D.max_atiles;
+    const bf16* qb = (const bf16*)q;
     if (D.d == 128) {
-      if (dense)
-        hipLaunchKernelGGL((k_bsfa_bf16<128, 2>), dim3(nb), dim3(256), 0, s, (const bf16*)q, D, B, o_sparse, o_psp);
-      else
-        hipLaunchKernelGGL((k_bsfa_bf16<128, 0>), dim3(nb), dim3(256), 0, s, (const bf16*)q, D, B, o_sparse, o_psp);
+      if (dense) launch_bsfa<128, 2>(D, B, qb, o_sparse, o_psp, nb, s);
+      else launch_bsfa<128, 0>(D, B, qb, o_sparse, o_psp, nb, s);
     } else {
-      if (dense)
-        hipLaunchKernelGGL((k_bsfa_bf16<64, 2>), dim3(nb), dim3(256), 0, s, (const bf16*)q, D, B, o_sparse, o_psp);
-      else
-        hipLaunchKernelGGL((k_bsfa_bf16<64, 0>), dim3(nb), dim3(256), 0, s, (const bf16*)q, D, B, o_sparse, o_psp);
+      if (dense) launch_bsfa<64, 2>(D, B, qb, o_sparse, o_psp, nb, s);
+      else launch_bsfa<64, 0>(D, B, qb, o_sparse, o_psp, nb, s);
     }
   } else {
+    const int nb = D.BH * D.max_tiles;
     if (D.d == 128)
       hipLaunchKernelGGL((k_bsfa_f32<128, 0>), dim3(nb), dim3(128), 0, s, (const float*)q, D, B, o_sparse, o_psp);
     else
@@ -681,18 +740,21 @@ void launch_attend_sparse(const void* q, const Dims& D, const Bufs& B, void* o_s
 
 void launch_attend_probes(const void* q, const Dims& D, const Bufs& B, float* o_pdn, hipStream_t s) {
   if (D.M == 0 || !o_pdn) return;
-  const int nb = D.BH * ((D.M + kAttnQT - 1) / kAttnQT);
   float* none = nullptr;
   if (D.dtype == 1) {
-    const int nbk = nb * D.pch;
+    // probe rows in 128-row tiles (4 waves), each over one key chunk
+    Dims Dp = D;
+    Dp.attn_w = 4;
+    const int nbk = D.BH * ((D.M + kAttnQT - 1) / kAttnQT) * D.pch;
     if (D.d == 128) {
-      hipLaunchKernelGGL((k_bsfa_bf16<128, 1>), dim3(nbk), dim3(256), 0, s, (const bf16*)q, D, B, (void*)o_pdn, none);
+      launch_bsfa<128, 1>(Dp, B, (const bf16*)q, (void*)o_pdn, none, nbk, s);
       hipLaunchKernelGGL((k_probe_combine<128>), dim3(D.M, D.BH), dim3(128), 0, s, D, B, o_pdn);
     } else {
-      hipLaunchKernelGGL((k_bsfa_bf16<64, 1>), dim3(nbk), dim3(256), 0, s, (const bf16*)q, D, B, (void*)o_pdn, none);
+      launch_bsfa<64, 1>(Dp, B, (const bf16*)q, (void*)o_pdn, none, nbk, s);
       hipLaunchKernelGGL((k_probe_combine<64>), dim3(D.M, D.BH), dim3(64), 0, s, D, B, o_pdn);
     }
   } else {
+    const int nb = D.BH * ((D.M + kAttnQT - 1) / kAttnQT);
     if (D.d == 128)
       hipLaunchKernelGGL((k_bsfa_f32<128, 1>), dim3(nb), dim3(128), 0, s, (const float*)q, D, B, (void*)o_pdn, none);
     else

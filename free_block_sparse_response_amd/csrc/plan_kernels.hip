@@ -1840,17 +1840,20 @@ __global__ void k_fill_i32(int* p, long long n, int v) {
 }
 
 // =====================================================================================
-// Attention tiles: kAttnQT consecutive positions of one query group.
+// Tiles of consecutive positions of one query group: 128 rows for the group masses
+// (tiles / ntiles / tstart) and 32 * attn_w rows for the block-sparse attention (atiles /
+// antiles).
 // =====================================================================================
 __global__ __launch_bounds__(1024) void k_build_tiles(Dims D, Bufs B) {
   __shared__ int ws[16];
-  __shared__ int tstart[kMaxGroups + 1];
+  __shared__ int tstart[kMaxGroups + 1], astart[kMaxGroups + 1];
   const int bh = blockIdx.x, a = threadIdx.x;
   const int Cq = B.qst[bh].c_final;
   const int* qo = B.qoff + (size_t)bh * (D.Cq + 1);
-  const int nt = a < Cq ? ceil_div(qo[a + 1] - qo[a], D.qt) : 0;
-  int tot;
-  const int s = block_excl_scan<1024, int>(nt, &tot, ws);
+  const int aqt = 32 * D.attn_w;
+  const int n = a < Cq ? qo[a + 1] - qo[a] : 0;
+  int tot, atot;
+  const int s = block_excl_scan<1024, int>(ceil_div(n, D.qt), &tot, ws);
   tstart[a] = s;
   if (a < Cq) B.tstart[(size_t)bh * (D.Cq + 1) + a] = s;
   if (a == 0) B.tstart[(size_t)bh * (D.Cq + 1) + Cq] = tot;
@@ -1859,11 +1862,17 @@ __global__ __launch_bounds__(1024) void k_build_tiles(Dims D, Bufs B) {
     B.ntiles[bh] = tot;
   }
   __syncthreads();
+  astart[a] = block_excl_scan<1024, int>(ceil_div(n, aqt), &atot, ws);
+  if (a == 0) B.antiles[bh] = atot;
+  __syncthreads();
   const int w = threadIdx.x / kWave, l = lane_id();
   int2* tiles = B.tiles + (size_t)bh * D.max_tiles;
+  int2* atiles = B.atiles + (size_t)bh * D.max_atiles;
   for (int g = w; g < Cq; g += 16) {
-    const int n = ceil_div(qo[g + 1] - qo[g], D.qt);
-    for (int t = l; t < n; t += kWave) tiles[tstart[g] + t] = make_int2(g, qo[g] + t * D.qt);
+    const int rows = qo[g + 1] - qo[g];
+    const int nt = ceil_div(rows, D.qt), na = ceil_div(rows, aqt);
+    for (int t = l; t < nt; t += kWave) tiles[tstart[g] + t] = make_int2(g, qo[g] + t * D.qt);
+    for (int t = l; t < na; t += kWave) atiles[astart[g] + t] = make_int2(g, qo[g] + t * aqt);
   }
 }
 

@@ -32,7 +32,9 @@ struct Dims {
   int nblk;       // Lloyd row blocks per head (kKmRows rows each)
   int Npad;       // padded key count of the permuted K / transposed V
   int qt;         // query rows per attention tile
-  int max_tiles;  // attention tiles per head, upper bound
+  int max_tiles;  // 128-row tiles per head (group masses), upper bound
+  int attn_w;     // waves (32 query rows each) per block-sparse attention tile: 4 or 8
+  int max_atiles; // attention tiles of 32 * attn_w rows per head, upper bound
   int pch;        // key chunks of the probe attention (split over keys)
   int pkc;        // keys per probe chunk (multiple of the key tile)
   int dtype;      // 0 f32, 1 bf16
@@ -107,8 +109,10 @@ struct Bufs {
   int* pslot;        // [BH][N] probe slot of a token or -1
   void* kp;          // [BH][Npad][d] keys in key-group order
   void* vpt;         // [BH][d][Npad] values in key-group order, transposed
-  int2* tiles;       // [BH][max_tiles] (query group, first position)
+  int2* tiles;       // [BH][max_tiles] (query group, first position), 128-row tiles
   int* ntiles;       // [BH]
+  int2* atiles;      // [BH][max_atiles] (query group, first position), attention tiles
+  int* antiles;      // [BH]
   int* tstart;       // [BH][Cq+1] first tile of each query group
   float* mass_part;  // [BH][max_tiles][Ck] per-tile column sums of the group masses
   float* pp_o;       // [BH][M][pch][d] probe attention partial outputs (unnormalised)

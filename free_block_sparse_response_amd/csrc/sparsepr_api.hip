@@ -126,6 +126,8 @@ Bufs carve(const Dims& D, void* base, size_t* total) {
   B.vpt = c.take<char>(BH * D.Npad * d * esz);
   B.tiles = c.take<int2>(BH * D.max_tiles);
   B.ntiles = c.take<int>(BH);
+  B.atiles = c.take<int2>(BH * D.max_tiles);  // max_atiles <= max_tiles for either tile height
+  B.antiles = c.take<int>(BH);
   B.tstart = c.take<int>(BH * (D.Cq + 1));
   B.mass_part = c.take<float>(BH * D.max_tiles * D.Ck);
   B.pp_o = c.take<float>(BH * D.M * D.pch * d);
@@ -195,6 +197,7 @@ sparsepr_status sparsepr_plan_create(const sparsepr_config* cfg, sparsepr_plan_t
   if (c.correction < 0 || c.correction > 2) return SPARSEPR_ERR_INVALID_ARG;
   if (c.probe_selector < 0 || c.probe_selector > 2) return SPARSEPR_ERR_INVALID_ARG;
   if (c.key_rank < 0) return SPARSEPR_ERR_INVALID_ARG;
+  if (c.attn_tile_rows != 0 && c.attn_tile_rows != 128 && c.attn_tile_rows != 256) return SPARSEPR_ERR_INVALID_ARG;
 
   sparsepr_plan_s* p = new (std::nothrow) sparsepr_plan_s();
   if (!p) return SPARSEPR_ERR_INVALID_ARG;
@@ -212,6 +215,13 @@ sparsepr_status sparsepr_plan_create(const sparsepr_config* cfg, sparsepr_plan_t
   D.Npad = (N + 63) / 64 * 64 + 64;
   D.qt = spr::kAttnQT;
   D.max_tiles = (N + spr::kAttnQT - 1) / spr::kAttnQT + D.Cq;
+  // Attention tiles of 256 rows (8 waves: each staged key tile feeds twice the queries) when
+  // the call has enough of them to fill the GPU several times over (at least 1,024 full tiles,
+  // four per CU); small calls take 128-row tiles (4 waves, two workgroups per CU), whose
+  // shorter tail keeps every CU busy to the end.
+  if (c.attn_tile_rows == 128 || c.attn_tile_rows == 256) D.attn_w = c.attn_tile_rows / 32;
+  else D.attn_w = (long long)D.BH * N >= 1024ll * 256 ? 8 : 4;
+  D.max_atiles = (N + 32 * D.attn_w - 1) / (32 * D.attn_w) + D.Cq;
   {
     // split the probe rows' keys so that about 1024 workgroups share the probe attention
     const int ptiles = (D.M + spr::kAttnQT - 1) / spr::kAttnQT;
@@ -460,9 +470,13 @@ sparsepr_status sparsepr_dense_attention(sparsepr_plan_t p, const void* q, const
   p->ws = ws;
   p->planned = 0;  // the identity partition replaces any plan in this workspace
   Bufs B = carve(p->D, ws, nullptr);
-  spr::launch_identity_plan(p->D, B, s);
-  spr::launch_permute_kv(k, v, p->D, B, s);
-  spr::launch_attend_sparse(q, p->D, B, out, nullptr, s, true);
+  // one query group of N rows: full 256-row attention tiles
+  Dims Dd = p->D;
+  Dd.attn_w = 8;
+  Dd.max_atiles = (Dd.N + 255) / 256 + Dd.Cq;
+  spr::launch_identity_plan(Dd, B, s);
+  spr::launch_permute_kv(k, v, Dd, B, s);
+  spr::launch_attend_sparse(q, Dd, B, out, nullptr, s, true);
   return hip_status();
 }
 

@@ -99,6 +99,10 @@ typedef struct {
                                            /*   directions of the sampled queries (metric  */
                                            /*   G truncated to its r_K largest eigenvalues)*/
                                            /*   applied when 0 < r_K < min(d, S)           */
+  int32_t attn_tile_rows;                  /* query rows per block-sparse attention tile: */
+                                           /*   128 or 256; 0 = 256 when B*H*N >= 1024*256 */
+                                           /*   (enough tiles to fill the GPU), else 128;   */
+                                           /*   outputs do not depend on it                */
 } sparsepr_config;
 
 typedef struct sparsepr_plan_s* sparsepr_plan_t;

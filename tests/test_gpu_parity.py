@@ -174,3 +174,19 @@ def test_caller_probes_from_labels():
         e_out, e_pr = max_rel(out[i], r.out), max_rel(o_pr[i], r.o_probe_dense)
         say(f"  head {heads[i]}: out {e_out:.2e} probe dense {e_pr:.2e}")
         assert e_out <= TOL["bf16"] and e_pr <= TOL["bf16"]
+
+
+# ------------------------------------------------------------- attention tile heights
+@pytest.mark.parametrize("rows", [128, 256])
+@pytest.mark.parametrize("case", ["c2", "d64 ragged"])
+def test_both_attention_tile_heights(case, rows):
+    # 4-wave (128-row) and 8-wave (256-row) block-sparse tiles: the library picks one by the
+    # size of the call; both must give the oracle's output (groups larger than a tile, last
+    # tiles partly filled, ragged key runs)
+    if case == "c2":
+        w, heads = configs.CONFIGS["c2"], [2, 7]
+    else:
+        w = configs.with_overrides("c2", grid=(5, 13, 19), head_dim=64, heads=3, n_sampled=64, n_key_groups=24,
+                                   n_query_groups=6, n_probes=40, density=0.3)
+        heads = [0, 1, 2]
+    _parity_from_labels(w, heads, attn_tile_rows=rows)
