@@ -42,7 +42,8 @@ class SparsePR:
     n_key_groups, n_query_groups, n_probes, density, ridge_lambda, seed and optionally
     kmeans_max_iter, kmeans_tol, penalize_bias, softmax_scale, assign_precision, warm_iters,
     partition, correction, probe_selector (comparison settings; 0 = the method), key_rank,
-    attn_tile_rows (128 / 256; 0 = chosen by the average query-group size).
+    attn_tile_rows (128 / 256; 0 = chosen by the size of the call), output_rank (residual fit
+    truncated to that many probe-residual directions; 0 = none).
     """
 
     def __init__(self, cfg, device="cuda"):
@@ -57,7 +58,7 @@ class SparsePR:
                                  c.get("penalize_bias", 0), c.get("seed", 0), c.get("softmax_scale", 0.0),
                                  c.get("assign_precision", 0), c.get("warm_iters", 2), c.get("partition", 0),
                                  c.get("correction", 0), c.get("probe_selector", 0), c.get("key_rank", 0),
-                                 c.get("attn_tile_rows", 0))
+                                 c.get("attn_tile_rows", 0), c.get("output_rank", 0))
         self.plan_h = L.sparsepr_plan_create(self._cc)
         self.ws = torch.empty(L.sparsepr_workspace_bytes(self.plan_h), dtype=torch.uint8, device=device)
         shape = (c["batch"], c["heads"], self.N, self.d)
@@ -179,7 +180,7 @@ def config_from_workload(w, **over):
              n_probes=w["n_probes"], density=w["density"], ridge_lambda=w["ridge_lambda"], seed=w["seed"],
              kmeans_max_iter=KMEANS_MAX_ITER, kmeans_tol=KMEANS_TOL,
              softmax_scale=w.get("scale", 1.0 / math.sqrt(w["head_dim"])))
-    for key in ("partition", "correction", "probe_selector", "key_rank", "attn_tile_rows"):
+    for key in ("partition", "correction", "probe_selector", "key_rank", "attn_tile_rows", "output_rank"):
         if key in w:
             c[key] = w[key]
     c.update(over)

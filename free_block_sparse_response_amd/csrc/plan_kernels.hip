@@ -2005,16 +2005,19 @@ static void group_mass(const T* q, const Dims& D, const Bufs& B, hipStream_t s) 
   }
 }
 
-// Key response rank (paper Table C.1, r_K): the key metric G = s^2 Q_S^T Q_S is replaced
-// by its truncation to the r_K largest eigenvalues, G_r = sum_i lambda_i u_i u_i^T, which
-// is the metric of the key responses projected on the sampled queries' r_K leading
-// response directions. One block per head: cyclic two-sided Jacobi in LDS (float),
-// round-robin pairings so that the n/2 rotations of a round act on disjoint index pairs
-// and are applied together, 2 x 2 block by 2 x 2 block; sweeps until the off-diagonal
-// mass is below 1e-14 of the total (at most 15). The r_K largest diagonal entries (ties
-// to the lower index) select the eigenvectors.
-template <int DD>
-__global__ __launch_bounds__(1024) void k_metric_rank(Dims D, Bufs B) {
+// Leading eigen-directions of a symmetric d x d matrix per head, by cyclic two-sided Jacobi
+// in LDS (float), round-robin pairings so that the n/2 rotations of a round act on disjoint
+// index pairs and are applied together, 2 x 2 block by 2 x 2 block; sweeps until the
+// off-diagonal mass is below 1e-14 of the total (at most 15). The `rank` largest diagonal
+// entries (ties to the lower index) select the eigenvectors u_i, and the output is either the
+// truncated matrix sum_i lambda_i u_i u_i^T (with its bf16 hi / lo split when out_h is given)
+// or, with PROJ, the orthogonal projector sum_i u_i u_i^T.
+// Uses: the key response rank (paper Table C.1, r_K: the key metric G = s^2 Q_S^T Q_S
+// truncated to its r_K largest eigenvalues, the metric of the key responses projected on the
+// sampled queries' r_K leading response directions), and the output truncation of the
+// residual fit (the probe residuals' leading directions).
+template <int DD, bool PROJ>
+__global__ __launch_bounds__(1024) void k_top_rank(const float* in, float* out, bf16* out_h, bf16* out_l, int keep) {
   constexpr int n = DD, H2 = DD / 2, LD = DD + 1;
   __shared__ float A[DD * LD], V[DD * LD];
   __shared__ float cs_c[H2], cs_s[H2];
@@ -2022,7 +2025,7 @@ __global__ __launch_bounds__(1024) void k_metric_rank(Dims D, Bufs B) {
   __shared__ float red[2][16];
   __shared__ int sel[DD];
   const int bh = blockIdx.x, tid = threadIdx.x;
-  float* G = B.metric + (size_t)bh * DD * DD;
+  const float* G = in + (size_t)bh * DD * DD;
   for (int e = tid; e < n * n; e += 1024) {
     const int i = e / n, j = e % n;
     A[i * LD + j] = G[e];
@@ -2103,19 +2106,21 @@ __global__ __launch_bounds__(1024) void k_metric_rank(Dims D, Bufs B) {
       const float lj = A[j * LD + j];
       rank += (lj > li) || (lj == li && j < tid);
     }
-    sel[tid] = rank < D.key_rank;
+    sel[tid] = rank < keep;
   }
   __syncthreads();
   for (int e = tid; e < n * n; e += 1024) {
     const int a = e / n, b = e % n;
     float g = 0.f;
     for (int i = 0; i < n; ++i)
-      if (sel[i]) g = fmaf(A[i * LD + i] * V[a * LD + i], V[b * LD + i], g);
+      if (sel[i]) g = fmaf(PROJ ? V[a * LD + i] : A[i * LD + i] * V[a * LD + i], V[b * LD + i], g);
     const size_t o = (size_t)bh * DD * DD + e;
-    B.metric[o] = g;
-    const bf16 gh = (bf16)g;
-    B.metric_h[o] = gh;
-    B.metric_l[o] = (bf16)(g - (float)gh);
+    out[o] = g;
+    if (out_h) {
+      const bf16 gh = (bf16)g;
+      out_h[o] = gh;
+      out_l[o] = (bf16)(g - (float)gh);
+    }
   }
 }
 
@@ -2131,7 +2136,8 @@ static void key_metric(const Dims& D, const Bufs& B, hipStream_t s) {
                      D.scale * D.scale, B.metric, B.metric_h, B.metric_l);
   // rank reduction only below the rank of Q_S (at most min(d, S))
   if (D.key_rank > 0 && D.key_rank < DD && D.key_rank < D.S)
-    hipLaunchKernelGGL((k_metric_rank<DD>), dim3(D.BH), dim3(1024), 0, s, D, B);
+    hipLaunchKernelGGL((k_top_rank<DD, false>), dim3(D.BH), dim3(1024), 0, s, (const float*)B.metric, B.metric,
+                       B.metric_h, B.metric_l, D.key_rank);
 }
 
 // Metric, row constants and row scales of the query side: responses to the key centroids,
@@ -2274,6 +2280,16 @@ static void permute_impl(const void* k, const void* v, const Dims& D, const Bufs
 
 void launch_permute_kv(const void* k, const void* v, const Dims& D, const Bufs& B, hipStream_t s) {
   SPR_DISPATCH(D.dtype, D.d, permute_impl, k, v, D, B, s);
+}
+
+void launch_residual_projector(const Dims& D, const Bufs& B, hipStream_t s) {
+  bf16* none = nullptr;
+  if (D.d == 128)
+    hipLaunchKernelGGL((k_top_rank<128, true>), dim3(D.BH), dim3(1024), 0, s, (const float*)B.rcov, B.rproj, none, none,
+                       D.output_rank);
+  else
+    hipLaunchKernelGGL((k_top_rank<64, true>), dim3(D.BH), dim3(1024), 0, s, (const float*)B.rcov, B.rproj, none, none,
+                       D.output_rank);
 }
 
 void launch_fill_i32(int* p, long long n, int v, hipStream_t s) {

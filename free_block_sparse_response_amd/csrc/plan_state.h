@@ -52,6 +52,7 @@ struct Dims {
   int correction; // 0 weighted ridge, 1 mean-only, 2 none
   int probe_sel;  // 0 query-group stratified, 1 random, 2 uniform in token order
   int key_rank;   // key response rank r_K (0: full)
+  int output_rank;  // residual fit truncated to this many probe-residual directions (0: none)
   uint64_t seed;
 };
 
@@ -118,6 +119,8 @@ struct Bufs {
   float* pp_o;       // [BH][M][pch][d] probe attention partial outputs (unnormalised)
   float2* pp_ml;     // [BH][M][pch] probe attention partial (max, sum), log2 domain
   double* gram;      // [BH][d+1][2d+1]  [A | B] of the ridge normal equations
+  float* rcov;       // [BH][d][d] weighted second moment R^T W R of the probe residuals
+  float* rproj;      // [BH][d][d] projector on its output_rank leading eigenvectors
   bf16* theta_h;     // [BH][d][d] Theta^T (output dim major) rounded to bf16, for the apply
   bf16* theta_l;     // [BH][d][d] Theta^T minus its bf16 rounding
   int* status;       // [BH]

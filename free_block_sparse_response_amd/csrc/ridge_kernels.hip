@@ -478,6 +478,68 @@ __global__ __launch_bounds__(256) void k_apply_bf16(Dims D, Bufs B, const bf16* 
   }
 }
 
+// Output truncation of the fit: C = R^T W R (d x d) of the probe residuals R = o_dense -
+// o_sparse, in 32 x 32 tiles, float64 sums over the probes in order.
+template <int DD>
+__global__ __launch_bounds__(256) void k_resid_cov(Dims D, Bufs B, const float* o_psp, const float* o_dn,
+                                                   const float* weights) {
+  constexpr int PC = 32;  // probes per chunk
+  __shared__ double Ri[PC][33];
+  __shared__ double Rj[PC][33];
+  __shared__ double wv[PC];
+  const int i0 = blockIdx.x * 32, j0 = blockIdx.y * 32, bh = blockIdx.z;
+  const int tx = threadIdx.x % 32, ty = threadIdx.x / 32;  // 8 row groups of 4
+  double acc[4] = {0, 0, 0, 0};
+  const float* wp = weights ? weights + (size_t)bh * D.M : B.pweights + (size_t)bh * D.M;
+  const float* zs = o_psp + (size_t)bh * D.M * DD;
+  const float* zd = o_dn + (size_t)bh * D.M * DD;
+  for (int p0 = 0; p0 < D.M; p0 += PC) {
+    __syncthreads();
+    for (int e = threadIdx.x; e < PC * 32; e += 256) {
+      const int p = e / 32, c = e % 32;
+      const bool pv = p0 + p < D.M;
+      const size_t o = (size_t)(p0 + p) * DD;
+      Ri[p][c] = pv ? (double)zd[o + i0 + c] - (double)zs[o + i0 + c] : 0.0;
+      Rj[p][c] = pv ? (double)zd[o + j0 + c] - (double)zs[o + j0 + c] : 0.0;
+    }
+    if (threadIdx.x < PC) wv[threadIdx.x] = p0 + threadIdx.x < D.M ? (double)wp[p0 + threadIdx.x] : 0.0;
+    __syncthreads();
+    for (int p = 0; p < PC; ++p) {
+      const double rj = wv[p] * Rj[p][tx];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) acc[r] = fma(Ri[p][ty * 4 + r], rj, acc[r]);
+    }
+  }
+  float* C = B.rcov + (size_t)bh * DD * DD;
+#pragma unroll
+  for (int r = 0; r < 4; ++r) C[(size_t)(i0 + ty * 4 + r) * DD + j0 + tx] = (float)acc[r];
+}
+
+// Theta <- Theta P in place (rows of [(d+1) x d] Theta times the d x d projector): the
+// predicted residual [o, 1] Theta lands in the probe residuals' leading directions.
+template <int DD>
+__global__ __launch_bounds__(256) void k_theta_project(Dims D, Bufs B, float* coeffs) {
+  constexpr int RB = 8;  // rows of Theta per block
+  __shared__ float P[DD * DD];
+  __shared__ float T[RB][DD];
+  const int r0 = blockIdx.x * RB, bh = blockIdx.y;
+  const float* Pg = B.rproj + (size_t)bh * DD * DD;
+  float* Th = coeffs + (size_t)bh * (DD + 1) * DD;
+  for (int e = threadIdx.x; e < DD * DD; e += 256) P[e] = Pg[e];
+  for (int e = threadIdx.x; e < RB * DD; e += 256) {
+    const int r = r0 + e / DD;
+    T[e / DD][e % DD] = r <= DD ? Th[(size_t)r * DD + e % DD] : 0.f;
+  }
+  __syncthreads();
+  for (int e = threadIdx.x; e < RB * DD; e += 256) {
+    const int rr = e / DD, j = e % DD, r = r0 + rr;
+    if (r > DD) continue;
+    float acc = 0.f;
+    for (int k = 0; k < DD; ++k) acc = fmaf(T[rr][k], P[k * DD + j], acc);
+    Th[(size_t)r * DD + j] = acc;
+  }
+}
+
 // Correction families other than the ridge (paper Table 4 "Mean-only"; repair disabled in
 // the Table 2 partition rows): Theta = 0 except the bias row, which is the weighted mean
 // probe residual (mean-only) or zero (none). Probes summed in order; fp64 accumulation.
@@ -512,6 +574,11 @@ static void fit_impl(const Dims& D, const Bufs& B, const float* o_psp, const flo
     hipLaunchKernelGGL((k_ridge_gram<DD>), g, dim3(256), 0, s, D, B, o_psp, o_dn, w);
   }
   hipLaunchKernelGGL((k_ridge_solve<DD>), dim3((DD + 31) / 32, D.BH), dim3(512), 0, s, D, B, coeffs);
+  if (D.output_rank > 0 && D.M > 0) {
+    hipLaunchKernelGGL((k_resid_cov<DD>), dim3(DD / 32, DD / 32, D.BH), dim3(256), 0, s, D, B, o_psp, o_dn, w);
+    launch_residual_projector(D, B, s);
+    hipLaunchKernelGGL((k_theta_project<DD>), dim3((DD + 1 + 7) / 8, D.BH), dim3(256), 0, s, D, B, coeffs);
+  }
 }
 
 template <typename T, int DD>

@@ -133,6 +133,8 @@ Bufs carve(const Dims& D, void* base, size_t* total) {
   B.pp_o = c.take<float>(BH * D.M * D.pch * d);
   B.pp_ml = c.take<float2>(BH * D.M * D.pch);
   B.gram = c.take<double>(BH * (d + 1) * (2 * d + 1));
+  B.rcov = c.take<float>(BH * d * d);
+  B.rproj = c.take<float>(BH * d * d);
   B.theta_h = c.take<spr::bf16>(BH * d * d);
   B.theta_l = c.take<spr::bf16>(BH * d * d);
   B.status = c.take<int>(BH);
@@ -198,6 +200,7 @@ sparsepr_status sparsepr_plan_create(const sparsepr_config* cfg, sparsepr_plan_t
   if (c.probe_selector < 0 || c.probe_selector > 2) return SPARSEPR_ERR_INVALID_ARG;
   if (c.key_rank < 0) return SPARSEPR_ERR_INVALID_ARG;
   if (c.attn_tile_rows != 0 && c.attn_tile_rows != 128 && c.attn_tile_rows != 256) return SPARSEPR_ERR_INVALID_ARG;
+  if (c.output_rank < 0) return SPARSEPR_ERR_INVALID_ARG;
 
   sparsepr_plan_s* p = new (std::nothrow) sparsepr_plan_s();
   if (!p) return SPARSEPR_ERR_INVALID_ARG;
@@ -247,6 +250,7 @@ sparsepr_status sparsepr_plan_create(const sparsepr_config* cfg, sparsepr_plan_t
   D.correction = c.correction;
   D.probe_sel = c.probe_selector;
   D.key_rank = c.key_rank;
+  D.output_rank = c.output_rank < c.head_dim ? c.output_rank : 0;  // rank >= d keeps the whole span
   D.seed = c.seed;
   carve(D, nullptr, &p->ws_bytes);
   p->ws = nullptr;

@@ -2,7 +2,8 @@
 
 Rows mirror the paper's Table 2 (partition construction with repair disabled, and the
 partition-repair interaction), Table 4 (probe selection and correction family) and
-Table D.2(a) (probe count at fixed lambda), plus a ridge-lambda sweep. Each entry is the
+Table D.2(a) (probe count at fixed lambda), plus a ridge-lambda sweep and an output-truncation
+sweep (the residual fit restricted to the probe residuals' leading directions). Each entry is the
 mean / p99 rel-L2 error ||O_i - O_i^dense|| / (||O_i^dense|| + 1e-8) over unprobed rows,
 with the dense output from the library's own dense kernel on the same inputs.
 
@@ -96,6 +97,8 @@ def main(argv=None):
     ap.add_argument("--table4-lambda", type=float, default=1.0, help="lambda of the Table 4 / D.2 panels (paper: 1)")
     ap.add_argument("--probe-counts", default="16,32,64,128", help="M values of the Table D.2(a) panel")
     ap.add_argument("--lambdas", default="1e-3,1e-1,1,10,100", help="lambda values of the ridge sweep")
+    ap.add_argument("--output-ranks", default="1,4,16,64,0",
+                    help="output truncation ranks of the residual fit (0: none, the method)")
     ap.add_argument("--json", default=None, help="also write the panels to this file")
     args = ap.parse_args(argv)
 
@@ -132,6 +135,12 @@ def main(argv=None):
     # ridge lambda at the workload's probe count
     tl = {f"lambda={lam:g}": b.run(ridge_lambda=lam) for lam in (float(x) for x in args.lambdas.split(","))}
     panels.append(_panel(b, f"lambda sweep (M={w['n_probes']})", tl))
+
+    # output truncation of the residual fit at the workload's M and lambda ([D.2] "no output
+    # truncation" is the method's setting, rank 0 here)
+    tr = {(f"rank {r}" if r else "no truncation"): b.run(output_rank=r)
+          for r in (int(x) for x in args.output_ranks.split(","))}
+    panels.append(_panel(b, f"output truncation (M={w['n_probes']}, lambda={w['ridge_lambda']})", tr))
 
     for p in panels:
         print(f"\n{p['panel']} - mean / p99 unprobed rel-L2 over {p['eval_rows']} shared rows")

@@ -103,6 +103,12 @@ typedef struct {
                                            /*   128 or 256; 0 = 256 when B*H*N >= 1024*256 */
                                            /*   (enough tiles to fill the GPU), else 128;   */
                                            /*   outputs do not depend on it                */
+  int32_t output_rank;                     /* output truncation of the residual fit (paper */
+                                           /*   Table D.2 holds "no output truncation"): 0 */
+                                           /*   none; 0 < r < d projects the predicted     */
+                                           /*   residual on the r leading eigenvectors of  */
+                                           /*   R^T W R of the probe residuals; r >= d is  */
+                                           /*   the whole observed span (no change)        */
 } sparsepr_config;
 
 typedef struct sparsepr_plan_s* sparsepr_plan_t;
@@ -217,7 +223,9 @@ sparsepr_status sparsepr_plan_set_probes(sparsepr_plan_t plan, const int32_t* pr
  * (lambda on the bias too if cfg.penalize_bias). probe_weights [B,H,M] float overrides
  * the plan's weights when non-NULL. Solved in float64; a pivot at or below 1e-12 x the
  * largest diagonal entry sets the head's status to SPARSEPR_ERR_NUMERICAL and writes
- * zero coefficients. With M = 0 the coefficients are zero. */
+ * zero coefficients. With M = 0 the coefficients are zero. With cfg.output_rank = r
+ * (0 < r < d), Theta is then replaced by Theta P, P the orthogonal projector on the r
+ * leading eigenvectors of R^T W R (website PFRR panel: a low-rank probe-residual subspace). */
 sparsepr_status sparsepr_fit_residual(sparsepr_plan_t plan, const float* o_probe_sparse,
                                       const float* o_probe_dense, const float* probe_weights,
                                       float* coeffs, void* stream);

@@ -461,6 +461,27 @@ def ridge_fit(o_sp_probe, o_dn_probe, weights, lam, penalize_bias=False):
     return solve_upper(L.T, solve_lower(L, B))
 
 
+def residual_projector(o_sp_probe, o_dn_probe, weights, rank):
+    """Orthogonal projector (d x d) onto the `rank` leading directions of the probe residuals.
+
+    [method] PFRR panel: the affine correction acts in a low-rank probe-residual subspace;
+    [D.2](a) holds "no output truncation" fixed, so truncation is a setting. Reading: the
+    subspace is spanned by the `rank` eigenvectors of largest eigenvalue (ties: lower index)
+    of the weighted residual second moment R^T W R (R = O_dense - O_sparse on the probes,
+    W = diag(w), uncentred, the ridge's own weighting); the fitted map's predicted residual
+    is projected onto it. rank >= rank(R) keeps the whole observed span (the untruncated
+    fit); rank 0 removes the correction.
+    """
+    R = np.asarray(o_dn_probe, dtype=np.float64) - np.asarray(o_sp_probe, dtype=np.float64)
+    d = R.shape[1]
+    w = np.asarray(weights, dtype=np.float64)[:, None]
+    C = R.T @ (w * R)
+    evals, evecs = np.linalg.eigh(C)
+    order = np.lexsort((np.arange(d), -evals))[:max(0, min(rank, d))]
+    U = evecs[:, order]
+    return U @ U.T
+
+
 CORRECTION_RIDGE = 0      # full weighted ridge (the method)
 CORRECTION_MEAN_ONLY = 1  # [T4] "Mean-only": add the weighted mean probe residual
 CORRECTION_NONE = 2       # repair disabled ([T2] partition rows): sparse output kept
@@ -469,6 +490,8 @@ CORRECTION_NONE = 2       # repair disabled ([T2] partition rows): sparse output
 def fit_correction(o_sp_probe, o_dn_probe, weights, p):
     """Theta of the correction family p["correction"] (ridge by default).
 
+    With p["output_rank"] = r > 0 the ridge's prediction is truncated to the r leading
+    directions of the probe residuals (residual_projector); 0 or absent: no truncation.
     Mean-only is the lam -> infinity limit of the ridge with the bias unpenalised:
     Theta = [0; sum_p w_p r_p / sum_p w_p]. With repair disabled Theta = 0, so unprobed
     rows keep their sparse output (probe rows still return the exact output).
@@ -476,7 +499,13 @@ def fit_correction(o_sp_probe, o_dn_probe, weights, p):
     mode = p.get("correction", CORRECTION_RIDGE)
     M, d = o_sp_probe.shape
     if mode == CORRECTION_RIDGE:
-        return ridge_fit(o_sp_probe, o_dn_probe, weights, p["ridge_lambda"], p.get("penalize_bias", False))
+        theta = ridge_fit(o_sp_probe, o_dn_probe, weights, p["ridge_lambda"], p.get("penalize_bias", False))
+        r = p.get("output_rank", 0)
+        if r and M > 0:
+            # output truncation: the predicted residual [o, 1] Theta projected on the probe
+            # residuals' r leading directions
+            theta = theta @ residual_projector(o_sp_probe, o_dn_probe, weights, r)
+        return theta
     theta = np.zeros((d + 1, d))
     if mode == CORRECTION_MEAN_ONLY and M > 0:
         w = np.asarray(weights, dtype=np.float64)
@@ -703,7 +732,7 @@ def call_params(cfg):
                 partition=cfg.get("partition", PARTITION_RESPONSE),
                 correction=cfg.get("correction", CORRECTION_RIDGE),
                 probe_selector=cfg.get("probe_selector", PROBES_STRATIFIED),
-                key_rank=cfg.get("key_rank", 0))
+                key_rank=cfg.get("key_rank", 0), output_rank=cfg.get("output_rank", 0))
 
 
 def sparsepr_head(q, k, v, p, head, max_iter=25, tol=1e-4):

@@ -190,3 +190,12 @@ def test_binding_refuses_wrong_integer_and_weight_types(dtype_name):
         t, want, shape = _t((2, 3, 3), torch.int32), torch.int64, (2, 3, 3)
     with pytest.raises(ValueError):
         check_tensor(t, "x", [shape], want, "cpu")
+
+
+def test_output_rank_and_tile_rows_are_validated(lib):
+    for over, want in ((dict(output_rank=-1), L.SPARSEPR_ERR_INVALID_ARG), (dict(attn_tile_rows=96), L.SPARSEPR_ERR_INVALID_ARG),
+                       (dict(output_rank=8, attn_tile_rows=256), L.SPARSEPR_OK)):
+        st, h = _create(lib, _cfg(**over))
+        assert st == want
+        if st == L.SPARSEPR_OK:
+            lib.sparsepr_plan_destroy(h)

@@ -190,3 +190,29 @@ def test_both_attention_tile_heights(case, rows):
                                    n_query_groups=6, n_probes=40, density=0.3)
         heads = [0, 1, 2]
     _parity_from_labels(w, heads, attn_tile_rows=rows)
+
+
+# ------------------------------------------------------------- output truncation ([D.2](a))
+@pytest.mark.parametrize("name,rank", [("c1", 4), ("c1", 16), ("c2", 8), ("c2", 32)])
+def test_output_truncation_from_labels(name, rank):
+    # the fitted map's predicted residual projected on the probe residuals' `rank` leading
+    # directions (Jacobi in float on the GPU, eigh in the oracle): outputs and coefficients
+    # within the workload tolerance; the cut falls in a spectral gap (else the subspace, and
+    # with it the reference, is not unique)
+    w = configs.CONFIGS[name]
+    heads = [0] if name == "c1" else [1, 6]
+    sp, refs = _parity_from_labels(w, heads, output_rank=rank)
+    th = np_(sp.coeffs[0])
+    for i, r in enumerate(refs):
+        hp = r.plan
+        R = r.o_probe_dense - r.o_sparse[hp.probes]
+        ev = np.sort(np.linalg.eigvalsh(R.T @ (hp.weights[:, None] * R)))[::-1]
+        say(f"  head {heads[i]}: eigenvalues at the cut {ev[rank - 1]:.4g} / {ev[rank]:.4g}")
+        assert ev[rank - 1] > 1.05 * ev[rank]
+        scale = np.abs(r.theta).max()
+        err = np.abs(th[i] - r.theta).max() / scale
+        say(f"  head {heads[i]}: max |Theta - Theta_oracle| / max |Theta_oracle| = {err:.2e}")
+        assert err <= TOL[w["dtype"]]
+        # the map's output lies in the truncated subspace: Theta P = Theta
+        P = O.residual_projector(r.o_sparse[hp.probes], r.o_probe_dense, hp.weights, rank)
+        assert np.abs(r.theta - r.theta @ P).max() <= 1e-9 * scale

@@ -829,3 +829,71 @@ def test_low_key_rank_drops_weak_response_directions():
         full_ok += _planted_same_as(O.plan_head(q, k, p, head, 50, 0.0).key_labels, lab)
         low_ok += _planted_same_as(O.plan_head(q, k, dict(p, key_rank=d - 1), head, 50, 0.0).key_labels, lab)
     assert full_ok >= 2 and low_ok == 0
+
+
+# ---------------------------------------------------------------- output truncation ([D.2](a))
+def _probe_fit_case(rng, M, d, noise=0.3):
+    o_sp = rng.standard_normal((M, d))
+    o_dn = o_sp + noise * rng.standard_normal((M, d))
+    w = rng.uniform(0.5, 2.0, M)
+    return o_sp, o_dn, w
+
+
+def test_residual_projector_is_the_leading_right_singular_subspace():
+    # a different routine: the top right singular vectors of diag(sqrt w) R (SVD, not eigh)
+    rng = np.random.default_rng(41)
+    o_sp, o_dn, w = _probe_fit_case(rng, 50, 12)
+    R = o_dn - o_sp
+    for r in (1, 3, 7):
+        P = O.residual_projector(o_sp, o_dn, w, r)
+        V = np.linalg.svd(np.sqrt(w)[:, None] * R)[2][:r].T
+        np.testing.assert_allclose(P, V @ V.T, atol=1e-10)
+        np.testing.assert_allclose(P @ P, P, atol=1e-10)
+        assert abs(np.trace(P) - r) < 1e-10
+
+
+def test_truncation_at_or_above_the_residual_rank_is_the_plain_ridge():
+    # fewer probes than dimensions: the residuals span M <= d directions, so any rank >= M
+    # keeps the whole observed span and the prediction is unchanged
+    rng = np.random.default_rng(42)
+    d = 10
+    for M in (6, 30):
+        o_sp, o_dn, w = _probe_fit_case(rng, M, d)
+        p = dict(ridge_lambda=0.1, penalize_bias=False)
+        plain = O.fit_correction(o_sp, o_dn, w, p)
+        for r in (min(M, d), d):
+            cut = O.fit_correction(o_sp, o_dn, w, dict(p, output_rank=r))
+            np.testing.assert_allclose(cut, plain, atol=1e-9)
+        assert np.abs(O.fit_correction(o_sp, o_dn, w, dict(p, output_rank=2)) - plain).max() > 1e-3
+
+
+def test_truncation_to_rank_zero_is_no_repair():
+    rng = np.random.default_rng(43)
+    N, d, M = 80, 6, 20
+    o_sp_all = rng.standard_normal((N, d))
+    probes = np.sort(rng.choice(N, M, replace=False))
+    o_dn = o_sp_all[probes] + 0.5 * rng.standard_normal((M, d))
+    w = np.ones(M)
+    th = O.ridge_fit(o_sp_all[probes], o_dn, w, 0.1) @ O.residual_projector(o_sp_all[probes], o_dn, w, 0)
+    assert np.all(th == 0)
+    out = O.apply_residual(o_sp_all, probes, o_dn, th)
+    none = O.apply_residual(o_sp_all, probes, o_dn, O.fit_correction(o_sp_all[probes], o_dn, w,
+                                                                      dict(correction=O.CORRECTION_NONE)))
+    np.testing.assert_array_equal(out, none)
+
+
+def test_truncated_prediction_stays_in_the_planted_residual_subspace():
+    # residuals confined to a planted 3-dimensional subspace U plus weak noise: rank 3 finds U
+    # and every predicted residual lies in it
+    rng = np.random.default_rng(44)
+    M, d, r = 60, 16, 3
+    U = np.linalg.qr(rng.standard_normal((d, r)))[0]
+    o_sp = rng.standard_normal((M, d))
+    o_dn = o_sp + (rng.standard_normal((M, r)) * [3.0, 2.0, 1.5]) @ U.T + 1e-4 * rng.standard_normal((M, d))
+    w = rng.uniform(0.5, 2.0, M)
+    P = O.residual_projector(o_sp, o_dn, w, r)
+    np.testing.assert_allclose(P, U @ U.T, atol=1e-3)
+    th = O.fit_correction(o_sp, o_dn, w, dict(ridge_lambda=1e-3, output_rank=r))
+    pred = rng.standard_normal((5, d)) @ th[:d] + th[d]
+    np.testing.assert_allclose(pred - pred @ P, 0.0, atol=1e-9)            # in the fitted subspace
+    np.testing.assert_allclose(pred - pred @ U @ U.T, 0.0, atol=1e-3 * np.abs(pred).max())  # ~ planted
