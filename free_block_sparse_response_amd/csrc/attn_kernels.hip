@@ -15,6 +15,8 @@
 //                 place (no shuffles); A = V^T comes from the transposed V layout that the
 //                 permutation pass writes, one 16-byte LDS read per operand.
 // exp2 with the log2(e) factor folded into the score scale.
+#include <type_traits>
+
 #include "common.h"
 #include "plan_state.h"
 #include "launch.h"
@@ -31,7 +33,8 @@ __device__ inline int xcd_remap(int bid, int nblocks) {
   return base + slot;
 }
 
-// Walks the key runs of a query group: consecutive selected key groups merge into one run.
+// Walks the key runs of a query group: consecutive selected key groups merge into one run
+// (the fp32 kernel reads the route directly).
 struct RunIter {
   const int* cols;
   const int* koff;
@@ -44,35 +47,6 @@ struct RunIter {
     ++c;
     while (c < cend && cols[c] == e + 1) { ++e; ++c; }
     hi = koff[e + 1];
-    return true;
-  }
-};
-
-// Sequence of 64-key tiles over the key runs of one work item. A run [lo, hi) starts its
-// first tile at lo rounded down to 8 keys (16-byte aligned rows of the transposed V); keys
-// outside [lo, hi) are masked.
-struct TileSeq {
-  RunIter it;
-  int lo, hi, k0;
-  bool single, used;
-  __device__ bool first(int mode_lo, int mode_hi) {
-    if (single) {
-      lo = mode_lo;
-      hi = mode_hi;
-      used = true;
-      k0 = lo & ~7;
-      return lo < hi;
-    }
-    if (!it.next(lo, hi)) return false;
-    k0 = lo & ~7;
-    return true;
-  }
-  __device__ bool next() {
-    k0 += kKeyTile;
-    if (k0 < hi) return true;
-    if (single) return false;
-    if (!it.next(lo, hi)) return false;
-    k0 = lo & ~7;
     return true;
   }
 };
@@ -114,6 +88,34 @@ struct TileWalk {
     set_run();
     return true;
   }
+  // Tiles of one run (its first starts at lo rounded down to 8 keys).
+  __device__ static int run_tiles(int2 v) { return (v.y - (v.x & ~7) + KT - 1) / KT; }
+  // Tiles of the whole item; the wave's lanes share the runs (wave-uniform result).
+  __device__ int count() const {
+    int c = 0;
+    for (int i = lane_id(); i < nr; i += kWave) c += run_tiles(runs[i]);
+    return __builtin_amdgcn_readfirstlane(wave_sum_i(c));
+  }
+  // Positions the walk on tile t (0-based over the item's runs, t below count()): the lanes
+  // scan 64 runs at a time for the first run whose tiles reach past t.
+  __device__ void seek(int t) {
+    int base = 0;  // tiles of the runs before this chunk
+    for (int i0 = 0; i0 < nr; i0 += kWave) {
+      const int i = i0 + lane_id();
+      const int c = i < nr ? run_tiles(runs[i]) : 0;
+      const int incl = wave_incl_scan(c);
+      const uint64_t hit = __ballot(i < nr && base + incl > t);
+      if (hit) {
+        const int j = __builtin_amdgcn_readfirstlane(__builtin_ffsll((long long)hit) - 1);
+        const int before = __builtin_amdgcn_readfirstlane(base + __shfl(incl - c, j, kWave));
+        r = i0 + j;
+        set_run();
+        k0 += (t - before) * KT;
+        return;
+      }
+      base += __builtin_amdgcn_readfirstlane(__shfl(incl, kWave - 1, kWave));
+    }
+  }
 };
 
 // -------------------------------------------------------------------------------------
@@ -150,11 +152,9 @@ __global__ __launch_bounds__(64 * W, W == 4 ? 2 : 1) void k_bsfa_bf16(const bf16
   constexpr int KRB = DD * 2;                // K row bytes (256 or 128)
   constexpr int KW = KRB / 16;               // 16-byte slots per K row (16 or 8)
   constexpr int KR = 64 / KW;                // K rows per wave-wide 1 KB load
-  constexpr int KI = KT * KRB / (1024 * W);  // 1 KB loads per wave per K tile
   constexpr int VRB = KT * 2;                // V^T row bytes (keys of one dim)
   constexpr int VW = VRB / 16;               // 16-byte slots per V^T row
   constexpr int VR = 1024 / VRB;             // V^T rows per wave-wide 1 KB load
-  constexpr int VI = DD * VRB / (1024 * W);  // 1 KB loads per wave per V^T tile
   constexpr int NC = DD / 16;                // k-chunks of the QK^T product
   constexpr int ND = DD / 32;                // 32-wide d blocks of the output
   constexpr int SB = KT / 32;                // 32-key sub-blocks per tile
@@ -163,10 +163,15 @@ __global__ __launch_bounds__(64 * W, W == 4 ? 2 : 1) void k_bsfa_bf16(const bf16
   constexpr int NPAIR = 8 * SB;              // score pairs per lane per step
   constexpr int PF = 4;                      // operand reads ahead of their product
   constexpr int QT = 32 * W;                 // query rows per tile
-  static_assert((DD == 64 || DD == 128) && KI >= 1 && VI >= 1 && (KT == 32 || KT == 64), "tile shape");
+  constexpr int KTB = KT * DD;               // elements of one K or V^T tile
+  // 8-wave block-sparse tiles of at most 128 rows run split: waves w and w + 4 hold the same
+  // 32 rows, each half walks half of the tile's key tiles with its own staging buffers, and
+  // the two partial softmax states are merged through LDS at the end
+  constexpr bool CAN_SPLIT = MODE == 0 && W == 8;
+  constexpr int NS = CAN_SPLIT ? 2 : 1;      // key streams
+  static_assert((DD == 64 || DD == 128) && (KT == 32 || KT == 64), "tile shape");
   static_assert(STG == 1 || STG == 2, "staging depth");
-  __shared__ __attribute__((aligned(1024))) bf16 Kb[2][KT * DD];
-  __shared__ __attribute__((aligned(1024))) bf16 Vb[2][DD * KT];
+  __shared__ __attribute__((aligned(1024))) bf16 smem[NS * 4 * KTB];  // per stream: K[2], V^T[2]
   __shared__ int2 runs_s[kMaxGroups];
 
   const int nb = gridDim.x;
@@ -192,263 +197,284 @@ __global__ __launch_bounds__(64 * W, W == 4 ? 2 : 1) void k_bsfa_bf16(const bf16
   }
   const int tid = threadIdx.x, l = lane_id(), h = l >> 5, l32 = l & 31;
   const int w = __builtin_amdgcn_readfirstlane(tid / kWave);
-
-  // ---- Q^T operand in registers: query (32w + l32), d-slots 16c + 8h .. +7
-  const int qr = 32 * w + l32;
-  const bool qvalid = qr < rows;
-  const bool wave_active = 32 * w < rows;  // a wave past the tile's last row only stages K / V
-  int tok;
-  if (MODE != 1) tok = B.qperm[(size_t)bh * D.N + pos0 + (qvalid ? qr : 0)];
-  else tok = B.probes[(size_t)bh * D.M + pos0 + (qvalid ? qr : 0)];
-  const bf16* qrow = q + ((size_t)bh * D.N + tok) * DD;
-  bf16x8 qreg[NC];
-#pragma unroll
-  for (int c = 0; c < NC; ++c) qreg[c] = *reinterpret_cast<const bf16x8*>(qrow + 16 * c + 8 * h);
-
-  f32x16 o[ND];
-#pragma unroll
-  for (int i = 0; i < ND; ++i)
-#pragma unroll
-    for (int v = 0; v < 16; ++v) o[i][v] = 0.f;
-  float m_run = -INFINITY, l_half = 0.f;
   const float c2 = D.log2_scale;
-
   const bf16* kpb = (const bf16*)B.kp + (size_t)bh * D.Npad * DD;
   const bf16* vtb = (const bf16*)B.vpt + (size_t)bh * DD * D.Npad;
-
-  // Tile layout in LDS, no padding: 16-byte slot s of row r holds chunk s ^ swz(r), with
-  // swz(r) = r & 15 for 16-slot rows and (r >> 1) & 7 for 8-slot rows (K rows of d = 64,
-  // V^T rows of 64 keys), (r >> 2) & 3 for the 4-slot V^T rows of 32 keys, so the 16 rows one
-  // 16-lane group of an operand read touches fall on distinct banks. Each wave stages whole
-  // 1 KB row blocks; the chunk a lane fetches depends on its lane and wave only, so its
-  // source is one lane offset plus a per-load scalar.
-  auto kswz = [](int r) { return KW == 16 ? (r & 15) : ((r >> 1) & 7); };
-  auto vswz = [](int r) { return VW == 4 ? ((r >> 2) & 3) : (VW == 8 ? ((r >> 1) & 7) : (r & 15)); };
-  unsigned klane, vlane;
-  {
-    const int r = KR * w + l / KW;  // row of this lane in the wave's first load (load g = W i + w)
-    klane = (unsigned)(r * KRB + 16 * ((l % KW) ^ kswz(r)));
-    const int rv = VR * w + l / VW;
-    vlane = (unsigned)(rv * 2 * D.Npad + 16 * ((l % VW) ^ vswz(rv)));
+  int nr = 0;
+  if (MODE != 1) {
+    const int2* rg = B.runs + (size_t)bh * D.Cq * D.Ck + B.row_ptr[(size_t)bh * (D.Cq + 1) + a];
+    nr = __builtin_amdgcn_readfirstlane(B.nruns[(size_t)bh * D.Cq + a]);  // <= C_k <= kMaxGroups
+    for (int i = tid; i < nr; i += 64 * W) runs_s[i] = rg[i];
+    __syncthreads();
   }
-  // Every step issues the same loads (past the last tile they re-read the current one,
-  // unused), so the count of loads in flight is the same on every path and the wait before
-  // a store covers only the loads issued STG - 1 steps before.
-  struct Stage {
-    bf16x8 k[KI], v[VI];
-  };
-  auto load_k = [&](Stage& st, int k0) {
-    const char* src = (const char*)(kpb + (size_t)k0 * DD);
-#pragma unroll
-    for (int i = 0; i < KI; ++i) st.k[i] = *reinterpret_cast<const bf16x8*>(src + i * W * KR * KRB + klane);
-  };
-  auto load_v = [&](Stage& st, int k0) {
-    const char* src = (const char*)(vtb + k0);
-#pragma unroll
-    for (int i = 0; i < VI; ++i)
-      st.v[i] = *reinterpret_cast<const bf16x8*>(src + (size_t)i * W * VR * 2 * D.Npad + vlane);
-  };
-  auto store_k = [&](const Stage& st, bf16* dst) {
-#pragma unroll
-    for (int i = 0; i < KI; ++i) *reinterpret_cast<bf16x8*>(dst + (W * i + w) * 512 + 8 * l) = st.k[i];
-  };
-  auto store_v = [&](const Stage& st, bf16* dst) {
-#pragma unroll
-    for (int i = 0; i < VI; ++i) *reinterpret_cast<bf16x8*>(dst + (W * i + w) * 512 + 8 * l) = st.v[i];
-  };
 
-  // operand reads. K: row 32 sb + pi(l32), chunk 2c + h -> byte sb * 32 rows + (kaddr ^ 32c);
-  // V^T: row 32 db + l32, chunk 2cc + h -> byte (vaddr ^ 32cc) + db * 32 rows.
-  const int prow = swap_bits23(l32);
-  const unsigned kaddr = (unsigned)(prow * KRB + 16 * (h ^ kswz(prow)));
-  const unsigned vaddr = (unsigned)(l32 * VRB + 16 * (h ^ vswz(l32)));
-  auto kread = [&](const bf16* Kc, unsigned kb, int i) {  // i = sb * NC + c
-    const int sb = i / NC, c = i % NC;
-    return *reinterpret_cast<const bf16x8*>((const char*)Kc + sb * 32 * KRB + (kb ^ (32u * c)));
-  };
-  auto vread = [&](const bf16* Vc, unsigned vb, int i) {  // i = cc * ND + db
-    const int cc = i / ND, db = i % ND;
-    return *reinterpret_cast<const bf16x8*>((const char*)Vc + db * 32 * VRB + (vb ^ (32u * cc)));
-  };
-  // S^T = K Q^T of one tile: product j is chunk j / SB of sub-block j % SB, so consecutive
-  // products feed different accumulators. The per-chunk addresses are formed where they are
-  // used (one v_xor each): an empty asm makes the base opaque so that the compiler does not
-  // keep all of them live across the loop.
-  auto qk = [&](const bf16* Kc, f32x16 (&s)[SB]) {
-    unsigned kb = kaddr;
-    asm volatile("" : "+v"(kb));
-    constexpr int NI = NC * SB;
-    auto idx = [](int j) { return (j % SB) * NC + j / SB; };
-    bf16x8 ka[NI];
+  auto body = [&](auto split_tag) {
+    constexpr bool SPLIT = decltype(split_tag)::value;
+    constexpr int WL = SPLIT ? W / 2 : W;      // waves per key stream: loaders and row slices
+    constexpr int STGX = SPLIT ? 1 : STG;      // a split stream stages one step ahead
+    constexpr int KI = KT * KRB / (1024 * WL); // 1 KB loads per wave per K tile
+    constexpr int VI = DD * VRB / (1024 * WL); // 1 KB loads per wave per V^T tile
+    static_assert(KI >= 1 && VI >= 1, "loads per wave");
+    const int stream = SPLIT ? w / WL : 0;
+    const int sw = SPLIT ? w % WL : w;         // row slice and loader index in the stream
+    bf16* const sbase = smem + stream * 4 * KTB;
+    auto Kb = [&](int p) { return sbase + p * KTB; };
+    auto Vb = [&](int p) { return sbase + (2 + p) * KTB; };
+
+    // ---- Q^T operand in registers: query (32 sw + l32), d-slots 16c + 8h .. +7
+    const int qr = 32 * sw + l32;
+    const bool qvalid = qr < rows;
+    const bool wave_active = 32 * sw < rows;  // a wave past the tile's last row only stages K / V
+    int tok;
+    if (MODE != 1) tok = B.qperm[(size_t)bh * D.N + pos0 + (qvalid ? qr : 0)];
+    else tok = B.probes[(size_t)bh * D.M + pos0 + (qvalid ? qr : 0)];
+    const bf16* qrow = q + ((size_t)bh * D.N + tok) * DD;
+    bf16x8 qreg[NC];
 #pragma unroll
-    for (int j = 0; j < PF; ++j) ka[j] = kread(Kc, kb, idx(j));
+    for (int c = 0; c < NC; ++c) qreg[c] = *reinterpret_cast<const bf16x8*>(qrow + 16 * c + 8 * h);
+
+    f32x16 o[ND];
 #pragma unroll
-    for (int j = 0; j < NI; ++j) {
-      const int sb = j % SB, c = j / SB;
-      if (c == 0) {
-        const f32x16 z = {};
-        s[sb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[j], qreg[0], z, 0, 0, 0);
-      } else {
-        s[sb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[j], qreg[c], s[sb], 0, 0, 0);
+    for (int i = 0; i < ND; ++i)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) o[i][v] = 0.f;
+    float m_run = -INFINITY, l_half = 0.f;
+
+    // Tile layout in LDS, no padding: 16-byte slot s of row r holds chunk s ^ swz(r), with
+    // swz(r) = r & 15 for 16-slot rows and (r >> 1) & 7 for 8-slot rows (K rows of d = 64,
+    // V^T rows of 64 keys), (r >> 2) & 3 for the 4-slot V^T rows of 32 keys, so the 16 rows
+    // one 16-lane group of an operand read touches fall on distinct banks. Each wave stages
+    // whole 1 KB row blocks; the chunk a lane fetches depends on its lane and loader index
+    // only, so its source is one lane offset plus a per-load scalar.
+    auto kswz = [](int r) { return KW == 16 ? (r & 15) : ((r >> 1) & 7); };
+    auto vswz = [](int r) { return VW == 4 ? ((r >> 2) & 3) : (VW == 8 ? ((r >> 1) & 7) : (r & 15)); };
+    unsigned klane, vlane;
+    {
+      const int r = KR * sw + l / KW;  // row of this lane in the wave's first load (load g = WL i + sw)
+      klane = (unsigned)(r * KRB + 16 * ((l % KW) ^ kswz(r)));
+      const int rv = VR * sw + l / VW;
+      vlane = (unsigned)(rv * 2 * D.Npad + 16 * ((l % VW) ^ vswz(rv)));
+    }
+    // Every step issues the same loads (past the last tile they re-read the current one,
+    // unused), so the count of loads in flight is the same on every path and the wait before
+    // a store covers only the loads issued STGX - 1 steps before.
+    struct Stage {
+      bf16x8 k[KI], v[VI];
+    };
+    auto load_k = [&](Stage& st, int k0) {
+      const char* src = (const char*)(kpb + (size_t)k0 * DD);
+#pragma unroll
+      for (int i = 0; i < KI; ++i) st.k[i] = *reinterpret_cast<const bf16x8*>(src + i * WL * KR * KRB + klane);
+    };
+    auto load_v = [&](Stage& st, int k0) {
+      const char* src = (const char*)(vtb + k0);
+#pragma unroll
+      for (int i = 0; i < VI; ++i)
+        st.v[i] = *reinterpret_cast<const bf16x8*>(src + (size_t)i * WL * VR * 2 * D.Npad + vlane);
+    };
+    auto store_k = [&](const Stage& st, bf16* dst) {
+#pragma unroll
+      for (int i = 0; i < KI; ++i) *reinterpret_cast<bf16x8*>(dst + (WL * i + sw) * 512 + 8 * l) = st.k[i];
+    };
+    auto store_v = [&](const Stage& st, bf16* dst) {
+#pragma unroll
+      for (int i = 0; i < VI; ++i) *reinterpret_cast<bf16x8*>(dst + (WL * i + sw) * 512 + 8 * l) = st.v[i];
+    };
+
+    // operand reads. K: row 32 sb + pi(l32), chunk 2c + h -> byte sb * 32 rows + (kaddr ^ 32c);
+    // V^T: row 32 db + l32, chunk 2cc + h -> byte (vaddr ^ 32cc) + db * 32 rows.
+    const int prow = swap_bits23(l32);
+    const unsigned kaddr = (unsigned)(prow * KRB + 16 * (h ^ kswz(prow)));
+    const unsigned vaddr = (unsigned)(l32 * VRB + 16 * (h ^ vswz(l32)));
+    auto kread = [&](const bf16* Kc, unsigned kb, int i) {  // i = sb * NC + c
+      const int sb = i / NC, c = i % NC;
+      return *reinterpret_cast<const bf16x8*>((const char*)Kc + sb * 32 * KRB + (kb ^ (32u * c)));
+    };
+    auto vread = [&](const bf16* Vc, unsigned vb, int i) {  // i = cc * ND + db
+      const int cc = i / ND, db = i % ND;
+      return *reinterpret_cast<const bf16x8*>((const char*)Vc + db * 32 * VRB + (vb ^ (32u * cc)));
+    };
+    // S^T = K Q^T of one tile: product j is chunk j / SB of sub-block j % SB, so consecutive
+    // products feed different accumulators. The per-chunk addresses are formed where they
+    // are used (one v_xor each): an empty asm makes the base opaque so that the compiler does
+    // not keep all of them live across the loop.
+    auto qk = [&](const bf16* Kc, f32x16 (&s)[SB]) {
+      unsigned kb = kaddr;
+      asm volatile("" : "+v"(kb));
+      constexpr int NI = NC * SB;
+      auto idx = [](int j) { return (j % SB) * NC + j / SB; };
+      bf16x8 ka[NI];
+#pragma unroll
+      for (int j = 0; j < PF; ++j) ka[j] = kread(Kc, kb, idx(j));
+#pragma unroll
+      for (int j = 0; j < NI; ++j) {
+        const int sb = j % SB, c = j / SB;
+        if (c == 0) {
+          const f32x16 z = {};
+          s[sb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[j], qreg[0], z, 0, 0, 0);
+        } else {
+          s[sb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[j], qreg[c], s[sb], 0, 0, 0);
+        }
+        if (j + PF < NI) ka[j + PF] = kread(Kc, kb, idx(j + PF));
+        __builtin_amdgcn_sched_barrier(0);
       }
-      if (j + PF < NI) ka[j + PF] = kread(Kc, kb, idx(j + PF));
-      __builtin_amdgcn_sched_barrier(0);
-    }
-  };
-  // keys outside [lo, hi) of an edge tile get score -inf; score v of sub-block sb is key
-  // 32 sb + 16 (v >> 3) + 8 h + (v & 7) of the tile (pi order)
-  auto mask = [&](f32x16 (&s)[SB], int k0, int lo, int hi) {
+    };
+    // keys outside [lo, hi) of an edge tile get score -inf; score v of sub-block sb is key
+    // 32 sb + 16 (v >> 3) + 8 h + (v & 7) of the tile (pi order)
+    auto mask = [&](f32x16 (&s)[SB], int k0, int lo, int hi) {
 #pragma unroll
-    for (int sb = 0; sb < SB; ++sb) {
-      const int vlo = lo - k0 - 32 * sb - 8 * h, vhi = hi - k0 - 32 * sb - 8 * h;
-      if (lo > k0 + 32 * sb) {
+      for (int sb = 0; sb < SB; ++sb) {
+        const int vlo = lo - k0 - 32 * sb - 8 * h, vhi = hi - k0 - 32 * sb - 8 * h;
+        if (lo > k0 + 32 * sb) {
 #pragma unroll
-        for (int v = 0; v < 16; ++v)
-          if (16 * (v >> 3) + (v & 7) < vlo) s[sb][v] = -INFINITY;
+          for (int v = 0; v < 16; ++v)
+            if (16 * (v >> 3) + (v & 7) < vlo) s[sb][v] = -INFINITY;
+        }
+        if (hi < k0 + 32 * sb + 32) {
+#pragma unroll
+          for (int v = 0; v < 16; ++v)
+            if (16 * (v >> 3) + (v & 7) >= vhi) s[sb][v] = -INFINITY;
+        }
       }
-      if (hi < k0 + 32 * sb + 32) {
+    };
+    auto max16 = [&](const f32x16& s) {  // max of the 16 scores (v_max3 tree)
+      const float a = fmaxf(fmaxf(s[0], s[1]), s[2]), b = fmaxf(fmaxf(s[3], s[4]), s[5]);
+      const float c = fmaxf(fmaxf(s[6], s[7]), s[8]), e = fmaxf(fmaxf(s[9], s[10]), s[11]);
+      const float f = fmaxf(fmaxf(s[12], s[13]), s[14]);
+      return fmaxf(fmaxf(fmaxf(a, b), s[15]), fmaxf(fmaxf(c, e), f));
+    };
+    // moves the accumulator and row sum to max mu when any lane of the wave raised its max
+    auto rescale = [&](float mu) {
+      if (__builtin_amdgcn_ballot_w64(mu != m_run)) {
+        const float alpha = __builtin_amdgcn_exp2f(m_run - mu);
+        m_run = mu;
+        l_half *= alpha;
 #pragma unroll
-        for (int v = 0; v < 16; ++v)
-          if (16 * (v >> 3) + (v & 7) >= vhi) s[sb][v] = -INFINITY;
+        for (int i = 0; i < ND; ++i)
+#pragma unroll
+          for (int v = 0; v < 16; ++v) o[i][v] *= alpha;
       }
-    }
-  };
-  auto max16 = [&](const f32x16& s) {  // max of the 16 scores (v_max3 tree)
-    const float a = fmaxf(fmaxf(s[0], s[1]), s[2]), b = fmaxf(fmaxf(s[3], s[4]), s[5]);
-    const float c = fmaxf(fmaxf(s[6], s[7]), s[8]), e = fmaxf(fmaxf(s[9], s[10]), s[11]);
-    const float f = fmaxf(fmaxf(s[12], s[13]), s[14]);
-    return fmaxf(fmaxf(fmaxf(a, b), s[15]), fmaxf(fmaxf(c, e), f));
-  };
-  // moves the accumulator and row sum to max mu when any lane of the wave raised its max
-  auto rescale = [&](float mu) {
-    if (__builtin_amdgcn_ballot_w64(mu != m_run)) {
-      const float alpha = __builtin_amdgcn_exp2f(m_run - mu);
-      m_run = mu;
-      l_half *= alpha;
+    };
+    // Softmax numerators of one tile against the reference max mu, in pairs of scores:
+    // scale and shift, exponentiate, pack to bf16 and add the packed pair to the row sum (one
+    // v_dot2 with (1, 1), so the sum is of the same rounded values that enter PV). Pair g
+    // (scores 2g, 2g + 1 of sub-block g / 8) goes through a three-slice pipeline (shift in
+    // slice g, exp in g+1, pack in g+2) and lands in P chunk g / 4; the slices follow the
+    // MFMAs of the previous tile's PV product, the last two close the pipeline.
+    const bf16x2 ones = {(bf16)1.f, (bf16)1.f};
+    auto soft_slice = [&](const f32x16 (&s)[SB], int i, float mu, float& ps, float (&xe)[2 * NPAIR],
+                          bf16x8 (&pn)[NCC]) {
+      const int gp = i - 2, ge = i - 1, gf = i;
+      if (gp >= 0 && gp < NPAIR) {
+        bf16x2 pr;
+        pr[0] = (bf16)xe[2 * gp];
+        pr[1] = (bf16)xe[2 * gp + 1];
+        pn[gp >> 2][2 * (gp & 3)] = pr[0];
+        pn[gp >> 2][2 * (gp & 3) + 1] = pr[1];
+        ps = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, ps, false);
+      }
+      if (ge >= 0 && ge < NPAIR) {
+        xe[2 * ge] = __builtin_amdgcn_exp2f(xe[2 * ge]);
+        xe[2 * ge + 1] = __builtin_amdgcn_exp2f(xe[2 * ge + 1]);
+      }
+      if (gf < NPAIR) {
+        const int sb = gf / 8, v = 2 * (gf % 8);
+        xe[2 * gf] = fmaf(s[sb][v], c2, -mu);
+        xe[2 * gf + 1] = fmaf(s[sb][v + 1], c2, -mu);
+      }
+    };
+    // The reference max is kept lazily: numerators are formed against the running max, and
+    // only when a lane's partial row sum of the tile exceeds 2^16 (so some numerator may be
+    // large, or infinite) is the tile redone against its exact max; the first tile of a work
+    // item, with no max yet, always is. Every numerator kept is therefore <= 2^16: far from
+    // overflow in fp32, and bf16 keeps its relative precision at any magnitude.
+    auto soft_exact = [&](const f32x16 (&s)[SB], float& mu, float& ps, bf16x8 (&pn)[NCC]) {
+      float mt = max16(s[0]);
 #pragma unroll
-      for (int i = 0; i < ND; ++i)
+      for (int sb = 1; sb < SB; ++sb) mt = fmaxf(mt, max16(s[sb]));
+      mu = fmaxf(mu, fmaxf(mt, xor32(mt)) * c2);
+      ps = 0.f;
+      float xe[2 * NPAIR];
 #pragma unroll
-        for (int v = 0; v < 16; ++v) o[i][v] *= alpha;
-    }
-  };
-  // Softmax numerators of one tile against the reference max mu, in pairs of scores: scale
-  // and shift, exponentiate, pack to bf16 and add the packed pair to the row sum (one
-  // v_dot2 with (1, 1), so the sum is of the same rounded values that enter PV). Pair g
-  // (scores 2g, 2g + 1 of sub-block g / 8) goes through a three-slice pipeline (shift in
-  // slice g, exp in g+1, pack in g+2) and lands in P chunk g / 4; the slices follow the
-  // MFMAs of the previous tile's PV product, the last two close the pipeline.
-  const bf16x2 ones = {(bf16)1.f, (bf16)1.f};
-  auto soft_slice = [&](const f32x16 (&s)[SB], int i, float mu, float& ps, float (&xe)[2 * NPAIR],
-                        bf16x8 (&pn)[NCC]) {
-    const int gp = i - 2, ge = i - 1, gf = i;
-    if (gp >= 0 && gp < NPAIR) {
-      bf16x2 pr;
-      pr[0] = (bf16)xe[2 * gp];
-      pr[1] = (bf16)xe[2 * gp + 1];
-      pn[gp >> 2][2 * (gp & 3)] = pr[0];
-      pn[gp >> 2][2 * (gp & 3) + 1] = pr[1];
-      ps = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, ps, false);
-    }
-    if (ge >= 0 && ge < NPAIR) {
-      xe[2 * ge] = __builtin_amdgcn_exp2f(xe[2 * ge]);
-      xe[2 * ge + 1] = __builtin_amdgcn_exp2f(xe[2 * ge + 1]);
-    }
-    if (gf < NPAIR) {
-      const int sb = gf / 8, v = 2 * (gf % 8);
-      xe[2 * gf] = fmaf(s[sb][v], c2, -mu);
-      xe[2 * gf + 1] = fmaf(s[sb][v + 1], c2, -mu);
-    }
-  };
-  // The reference max is kept lazily: numerators are formed against the running max, and
-  // only when a lane's partial row sum of the tile exceeds 2^16 (so some numerator may be
-  // large, or infinite) is the tile redone against its exact max; the first tile of a work
-  // item, with no max yet, always is. Every numerator kept is therefore <= 2^16: far from
-  // overflow in fp32, and bf16 keeps its relative precision at any magnitude.
-  auto soft_exact = [&](const f32x16 (&s)[SB], float& mu, float& ps, bf16x8 (&pn)[NCC]) {
-    float mt = max16(s[0]);
+      for (int i = 0; i < NPAIR + 2; ++i) soft_slice(s, i, mu, ps, xe, pn);
+    };
+    auto check = [&](const f32x16 (&s)[SB], float& mu, float& ps, bf16x8 (&pn)[NCC]) {
+      if (__builtin_amdgcn_ballot_w64(!(ps <= 65536.f))) soft_exact(s, mu, ps, pn);
+    };
+    // O^T += V^T P^T of the previous tile interleaved with the softmax numerators of the
+    // current tile
+    auto pv_soft = [&](const bf16* Vp, const bf16x8 (&pp)[NCC], const f32x16 (&s)[SB], float& mu, float& ps,
+                       bf16x8 (&pn)[NCC]) {
+      unsigned vb = vaddr;
+      asm volatile("" : "+v"(vb));
+      bf16x8 va[NPV];
 #pragma unroll
-    for (int sb = 1; sb < SB; ++sb) mt = fmaxf(mt, max16(s[sb]));
-    mu = fmaxf(mu, fmaxf(mt, xor32(mt)) * c2);
-    ps = 0.f;
-    float xe[2 * NPAIR];
+      for (int j = 0; j < PF; ++j) va[j] = vread(Vp, vb, j);
+      float xe[2 * NPAIR];
+      ps = 0.f;
+      constexpr int NSL = NPV > NPAIR + 2 ? NPV : NPAIR + 2;
 #pragma unroll
-    for (int i = 0; i < NPAIR + 2; ++i) soft_slice(s, i, mu, ps, xe, pn);
-  };
-  auto check = [&](const f32x16 (&s)[SB], float& mu, float& ps, bf16x8 (&pn)[NCC]) {
-    if (__builtin_amdgcn_ballot_w64(!(ps <= 65536.f))) soft_exact(s, mu, ps, pn);
-  };
-  // O^T += V^T P^T of the previous tile interleaved with the softmax numerators of the
-  // current tile
-  auto pv_soft = [&](const bf16* Vp, const bf16x8 (&pp)[NCC], const f32x16 (&s)[SB], float& mu, float& ps,
-                     bf16x8 (&pn)[NCC]) {
-    unsigned vb = vaddr;
-    asm volatile("" : "+v"(vb));
-    bf16x8 va[NPV];
+      for (int i = 0; i < NSL; ++i) {
+        if (i < NPV) {
+          const int cc = i / ND, db = i % ND;
+          o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[i], pp[cc], o[db], 0, 0, 0);
+          if (i + PF < NPV) va[i + PF] = vread(Vp, vb, i + PF);
+        }
+        if (i < NPAIR + 2) soft_slice(s, i, mu, ps, xe, pn);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      check(s, mu, ps, pn);
+    };
+    auto pv = [&](const bf16* Vp, const bf16x8 (&pp)[NCC]) {
+      unsigned vb = vaddr;
+      asm volatile("" : "+v"(vb));
+      bf16x8 va[NPV];
 #pragma unroll
-    for (int j = 0; j < PF; ++j) va[j] = vread(Vp, vb, j);
-    float xe[2 * NPAIR];
-    ps = 0.f;
-    constexpr int NS = NPV > NPAIR + 2 ? NPV : NPAIR + 2;
+      for (int j = 0; j < PF; ++j) va[j] = vread(Vp, vb, j);
 #pragma unroll
-    for (int i = 0; i < NS; ++i) {
-      if (i < NPV) {
+      for (int i = 0; i < NPV; ++i) {
         const int cc = i / ND, db = i % ND;
         o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[i], pp[cc], o[db], 0, 0, 0);
         if (i + PF < NPV) va[i + PF] = vread(Vp, vb, i + PF);
+        __builtin_amdgcn_sched_barrier(0);
       }
-      if (i < NPAIR + 2) soft_slice(s, i, mu, ps, xe, pn);
-      __builtin_amdgcn_sched_barrier(0);
+    };
+
+    // ---- the key tiles of this stream
+    TileWalk<KT> ts;
+    int Ts = 0, nsteps = 0;  // split: this stream's tiles, and the steps every stream runs
+    bool has;                // the stream's first tile exists
+    if (MODE != 1) {
+      ts.runs = runs_s;
+      ts.nr = nr;
+      has = ts.first();
+      if (SPLIT) {
+        const int T = ts.count();  // >= 1: every query group keeps a key group
+        nsteps = (T + 1) / 2;      // stream 0 takes the first half (rounded up)
+        Ts = stream ? T - nsteps : nsteps;
+        has = Ts > 0;
+        if (stream && has) ts.seek(nsteps);
+      }
+    } else {
+      const int clo = a * D.pkc;
+      has = ts.first_single(clo, min(D.N, clo + D.pkc));
     }
-    check(s, mu, ps, pn);
-  };
-  auto pv = [&](const bf16* Vp, const bf16x8 (&pp)[NCC]) {
-    unsigned vb = vaddr;
-    asm volatile("" : "+v"(vb));
-    bf16x8 va[NPV];
-#pragma unroll
-    for (int j = 0; j < PF; ++j) va[j] = vread(Vp, vb, j);
-#pragma unroll
-    for (int i = 0; i < NPV; ++i) {
-      const int cc = i / ND, db = i % ND;
-      o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[i], pp[cc], o[db], 0, 0, 0);
-      if (i + PF < NPV) va[i + PF] = vread(Vp, vb, i + PF);
-      __builtin_amdgcn_sched_barrier(0);
-    }
-  };
-  TileWalk<KT> ts;
-  bool has;  // the first tile exists
-  if (MODE != 1) {
-    const int2* rg = B.runs + (size_t)bh * D.Cq * D.Ck + B.row_ptr[(size_t)bh * (D.Cq + 1) + a];
-    const int nr = __builtin_amdgcn_readfirstlane(B.nruns[(size_t)bh * D.Cq + a]);  // <= C_k <= kMaxGroups
-    for (int i = tid; i < nr; i += 64 * W) runs_s[i] = rg[i];
-    __syncthreads();
-    ts.runs = runs_s;
-    ts.nr = nr;
-    has = ts.first();
-  } else {
-    const int clo = a * D.pkc;
-    has = ts.first_single(clo, min(D.N, clo + D.pkc));
-  }
-  // Tile j: K(j) sits in K buffer j%2 and V(j) in V buffer j%2. Step j (j >= 1) loads K(j+STG)
-  // and V(j+STG-1) into registers, forms S(j), runs O += V(j-1) P(j-1) while it turns S(j)
-  // into P(j), and stores at its end K(j+1) and V(j), loaded STG-1 steps earlier. P is
-  // double-buffered in registers; the max and row sum of P(j) are applied (rescale, sum) at
-  // the start of step j+1, after P(j-1) has entered O. Tile 0 is handled before the loop and
-  // the last PV after it, so every step runs the same code and O never changes registers.
-  // Tile descriptors (k0, lo, hi) run STG steps ahead of the compute.
-  bf16x8 pp[NCC];  // P^T operands of the pending tile
-  float mu = -INFINITY, ps = 0.f;
-  if (has) {
+    // Tile j: K(j) sits in K buffer j%2 and V(j) in V buffer j%2. Step j (j >= 1) loads
+    // K(j+STGX) and V(j+STGX-1) into registers, forms S(j), runs O += V(j-1) P(j-1) while it
+    // turns S(j) into P(j), and stores at its end K(j+1) and V(j), loaded STGX-1 steps earlier.
+    // P is double-buffered in registers; the max and row sum of P(j) are applied (rescale,
+    // sum) at the start of step j+1, after P(j-1) has entered O. Tile 0 is handled before the
+    // loop and the last PV after it, so every step runs the same code and O never changes
+    // registers. Tile descriptors (k0, lo, hi) run STGX steps ahead of the compute.
+    bf16x8 pp[NCC];  // P^T operands of the pending tile
+    float mu = -INFINITY, ps = 0.f;
+    int par = 0;     // parity of the current tile
     int k0c = ts.k0, loc = ts.lo, hic = ts.hi;
-    bool has1 = ts.next();
-    int k01 = ts.k0, lo1 = ts.lo, hi1 = ts.hi;
-    bool has2 = STG == 2 && has1 && ts.next();  // STG 2 only: the tile after next
-    int k02 = STG == 2 ? ts.k0 : 0;
-    int par = 0;  // parity of the current tile
+    if (!has) k0c = loc = hic = 0;  // a split stream with no tile stages (unused) key 0
     auto compute_first = [&]() {
       if (wave_active) {
         f32x16 s[SB];
-        qk(Kb[0], s);
+        qk(Kb(0), s);
         if (loc > k0c || hic < k0c + KT) mask(s, k0c, loc, hic);
         soft_exact(s, mu, ps, pp);
       }
@@ -458,127 +484,201 @@ __global__ __launch_bounds__(64 * W, W == 4 ? 2 : 1) void k_bsfa_bf16(const bf16
         rescale(mu);
         l_half += ps;
         f32x16 s[SB];
-        qk(Kb[par], s);
+        qk(Kb(par), s);
         if (loc > k0c || hic < k0c + KT) mask(s, k0c, loc, hic);
         bf16x8 pn[NCC];
-        pv_soft(Vb[par ^ 1], pp, s, mu, ps, pn);
+        pv_soft(Vb(par ^ 1), pp, s, mu, ps, pn);
 #pragma unroll
         for (int c = 0; c < NCC; ++c) pp[c] = pn[c];
       }
     };
-    if (STG == 2) {
-      Stage sa, sb;  // sa: K(j+1), V(j) (stored at the end of step j); sb: K(j+2), V(j+1)
-      load_k(sa, k0c);
-      store_k(sa, Kb[0]);
-      load_k(sa, has1 ? k01 : k0c);
-      load_v(sa, k0c);
-      __syncthreads();
-      load_k(sb, has2 ? k02 : k0c);
-      load_v(sb, has1 ? k01 : k0c);
-      compute_first();
-      if (has1) store_k(sa, Kb[1]);
-      store_v(sa, Vb[0]);
-      // step of tile j; `cur` holds K(j+1), V(j) (loaded a step ago), `nxt` receives K(j+2), V(j+1)
-      auto step = [&](Stage& cur, Stage& nxt) {
-        k0c = k01; loc = lo1; hic = hi1;
-        has1 = has2;
-        k01 = k02; lo1 = ts.lo; hi1 = ts.hi;
-        has2 = has2 && ts.next();
-        k02 = ts.k0;
-        par ^= 1;
-        __syncthreads();
-        load_k(nxt, has2 ? k02 : k0c);
-        load_v(nxt, has1 ? k01 : k0c);
-        compute_step();
-        if (has1) store_k(cur, Kb[par ^ 1]);
-        store_v(cur, Vb[par]);
-      };
-      // whole pairs of steps (stages swap roles twice), then at most one more step
-      while (has1 && has2) {
-        step(sb, sa);
-        step(sa, sb);
-      }
-      if (has1) step(sb, sa);
-    } else {
+    if (SPLIT) {
+      // a fixed number of steps for both streams (barriers are shared); a stream past its
+      // last tile only re-reads that tile's keys, unused
+      bool has1 = Ts > 1 && ts.next();
+      int k01 = ts.k0, lo1 = ts.lo, hi1 = ts.hi;
       Stage sa;  // K(j+1), V(j): loaded at the start of step j, stored at its end
       load_k(sa, k0c);
-      store_k(sa, Kb[0]);
+      store_k(sa, Kb(0));
       __syncthreads();
       load_k(sa, has1 ? k01 : k0c);
       load_v(sa, k0c);
-      compute_first();
-      if (has1) store_k(sa, Kb[1]);
-      store_v(sa, Vb[0]);
-      while (has1) {
-        const int k0v = k01;  // V(j) of the step below
-        k0c = k01; loc = lo1; hic = hi1;
-        has1 = ts.next();
-        k01 = ts.k0; lo1 = ts.lo; hi1 = ts.hi;
-        par ^= 1;
+      if (has) compute_first();
+      if (has1) store_k(sa, Kb(1));
+      store_v(sa, Vb(0));
+      for (int j = 1; j < nsteps; ++j) {
+        const bool live = j < Ts;
+        if (live) {
+          k0c = k01; loc = lo1; hic = hi1;
+          has1 = j + 1 < Ts && ts.next();
+          k01 = ts.k0; lo1 = ts.lo; hi1 = ts.hi;
+          par ^= 1;
+        }
         __syncthreads();
         load_k(sa, has1 ? k01 : k0c);
-        load_v(sa, k0v);
-        compute_step();
-        if (has1) store_k(sa, Kb[par ^ 1]);
-        store_v(sa, Vb[par]);
+        load_v(sa, k0c);
+        if (live) compute_step();
+        if (has1) store_k(sa, Kb(par ^ 1));
+        if (live) store_v(sa, Vb(par));
+      }
+      __syncthreads();
+      if (has && wave_active) {
+        rescale(mu);
+        l_half += ps;
+        pv(Vb(par), pp);
+      }
+    } else if (has) {
+      int k01 = 0, lo1 = 0, hi1 = 0, k02 = 0;
+      bool has1 = ts.next();
+      k01 = ts.k0; lo1 = ts.lo; hi1 = ts.hi;
+      bool has2 = STGX == 2 && has1 && ts.next();  // STGX 2 only: the tile after next
+      k02 = STGX == 2 ? ts.k0 : 0;
+      if (STGX == 2) {
+        Stage sa, sb;  // sa: K(j+1), V(j) (stored at the end of step j); sb: K(j+2), V(j+1)
+        load_k(sa, k0c);
+        store_k(sa, Kb(0));
+        load_k(sa, has1 ? k01 : k0c);
+        load_v(sa, k0c);
+        __syncthreads();
+        load_k(sb, has2 ? k02 : k0c);
+        load_v(sb, has1 ? k01 : k0c);
+        compute_first();
+        if (has1) store_k(sa, Kb(1));
+        store_v(sa, Vb(0));
+        // step of tile j; `cur` holds K(j+1), V(j) (loaded a step ago), `nxt` receives K(j+2), V(j+1)
+        auto step = [&](Stage& cur, Stage& nxt) {
+          k0c = k01; loc = lo1; hic = hi1;
+          has1 = has2;
+          k01 = k02; lo1 = ts.lo; hi1 = ts.hi;
+          has2 = has2 && ts.next();
+          k02 = ts.k0;
+          par ^= 1;
+          __syncthreads();
+          load_k(nxt, has2 ? k02 : k0c);
+          load_v(nxt, has1 ? k01 : k0c);
+          compute_step();
+          if (has1) store_k(cur, Kb(par ^ 1));
+          store_v(cur, Vb(par));
+        };
+        // whole pairs of steps (stages swap roles twice), then at most one more step
+        while (has1 && has2) {
+          step(sb, sa);
+          step(sa, sb);
+        }
+        if (has1) step(sb, sa);
+      } else {
+        Stage sa;  // K(j+1), V(j): loaded at the start of step j, stored at its end
+        load_k(sa, k0c);
+        store_k(sa, Kb(0));
+        __syncthreads();
+        load_k(sa, has1 ? k01 : k0c);
+        load_v(sa, k0c);
+        compute_first();
+        if (has1) store_k(sa, Kb(1));
+        store_v(sa, Vb(0));
+        while (has1) {
+          k0c = k01; loc = lo1; hic = hi1;
+          has1 = ts.next();
+          k01 = ts.k0; lo1 = ts.lo; hi1 = ts.hi;
+          par ^= 1;
+          __syncthreads();
+          load_k(sa, has1 ? k01 : k0c);
+          load_v(sa, k0c);
+          compute_step();
+          if (has1) store_k(sa, Kb(par ^ 1));
+          store_v(sa, Vb(par));
+        }
+      }
+      // O += V(T-1) P(T-1), V(T-1) in V buffer par
+      __syncthreads();
+      if (wave_active) {
+        rescale(mu);
+        l_half += ps;
+        pv(Vb(par), pp);
       }
     }
-    // O += V(T-1) P(T-1), V(T-1) in V buffer par
-    __syncthreads();
-    if (wave_active) {
-      rescale(mu);
-      l_half += ps;
-      pv(Vb[par], pp);
-    }
-  }
 
-  // ---- normalise and store query l32's row: d = 32db + 8g + 4h + r
-  const float lsum = l_half + xor32(l_half);
-  const float inv = 1.f / lsum;
-  if (!qvalid) return;
-  if (MODE != 1) {
-    bf16* orow = (bf16*)out + ((size_t)bh * D.N + tok) * DD;
+    if (SPLIT) {
+      // stream 1 hands its softmax state (running max, half row sum, unnormalised output)
+      // to stream 0 through LDS (the staging buffers are free), lane for lane
+      constexpr int NV = 16 * ND + 2;
+      float* xs = reinterpret_cast<float*>(smem) + (size_t)sw * NV * kWave + l;
+      __syncthreads();  // every wave is past its last operand read
+      if (stream == 1) {
 #pragma unroll
-    for (int db = 0; db < ND; ++db)
+        for (int i = 0; i < ND; ++i)
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        bf16x4 ov;
-#pragma unroll
-        for (int r = 0; r < 4; ++r) ov[r] = (bf16)(o[db][4 * g + r] * inv);
-        *reinterpret_cast<bf16x4*>(orow + 32 * db + 8 * g + 4 * h) = ov;
+          for (int v = 0; v < 16; ++v) xs[(16 * i + v) * kWave] = o[i][v];
+        xs[(16 * ND) * kWave] = m_run;
+        xs[(16 * ND + 1) * kWave] = l_half;
       }
-    // probe rows also keep their sparse output in float for the ridge fit
-    const int slot = (psp && D.M > 0) ? B.pslot[(size_t)bh * D.N + tok] : -1;
-    if (slot >= 0) {
-      float* prow = psp + ((size_t)bh * D.M + slot) * DD;
+      __syncthreads();
+      if (stream == 1) return;
+      const float m1 = xs[(16 * ND) * kWave], l1 = xs[(16 * ND + 1) * kWave];
+      const float mm = fmaxf(m_run, m1);  // finite: stream 0 has at least one tile
+      const float a0 = __builtin_amdgcn_exp2f(m_run - mm), a1 = __builtin_amdgcn_exp2f(m1 - mm);
+#pragma unroll
+      for (int i = 0; i < ND; ++i)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) o[i][v] = o[i][v] * a0 + xs[(16 * i + v) * kWave] * a1;
+      l_half = l_half * a0 + l1 * a1;
+      m_run = mm;
+    }
+
+    // ---- normalise and store query l32's row: d = 32db + 8g + 4h + r
+    const float lsum = l_half + xor32(l_half);
+    const float inv = 1.f / lsum;
+    if (!qvalid) return;
+    if (MODE != 1) {
+      bf16* orow = (bf16*)out + ((size_t)bh * D.N + tok) * DD;
+#pragma unroll
+      for (int db = 0; db < ND; ++db)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          bf16x4 ov;
+#pragma unroll
+          for (int r = 0; r < 4; ++r) ov[r] = (bf16)(o[db][4 * g + r] * inv);
+          *reinterpret_cast<bf16x4*>(orow + 32 * db + 8 * g + 4 * h) = ov;
+        }
+      // probe rows also keep their sparse output in float for the ridge fit
+      const int slot = (psp && D.M > 0) ? B.pslot[(size_t)bh * D.N + tok] : -1;
+      if (slot >= 0) {
+        float* prow = psp + ((size_t)bh * D.M + slot) * DD;
+#pragma unroll
+        for (int db = 0; db < ND; ++db)
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            float4 ov;
+            ov.x = o[db][4 * g + 0] * inv;
+            ov.y = o[db][4 * g + 1] * inv;
+            ov.z = o[db][4 * g + 2] * inv;
+            ov.w = o[db][4 * g + 3] * inv;
+            *reinterpret_cast<float4*>(prow + 32 * db + 8 * g + 4 * h) = ov;
+          }
+      }
+    } else {
+      // partial of key chunk `a`: unnormalised output and (max, sum) in the log2 domain
+      const size_t pr = ((size_t)bh * D.M + pos0 + qr) * D.pch + a;
+      float* orow = B.pp_o + pr * DD;
 #pragma unroll
       for (int db = 0; db < ND; ++db)
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
           float4 ov;
-          ov.x = o[db][4 * g + 0] * inv;
-          ov.y = o[db][4 * g + 1] * inv;
-          ov.z = o[db][4 * g + 2] * inv;
-          ov.w = o[db][4 * g + 3] * inv;
-          *reinterpret_cast<float4*>(prow + 32 * db + 8 * g + 4 * h) = ov;
+          ov.x = o[db][4 * g + 0];
+          ov.y = o[db][4 * g + 1];
+          ov.z = o[db][4 * g + 2];
+          ov.w = o[db][4 * g + 3];
+          *reinterpret_cast<float4*>(orow + 32 * db + 8 * g + 4 * h) = ov;
         }
+      if (h == 0) B.pp_ml[pr] = make_float2(m_run, lsum);
     }
+  };
+  if constexpr (CAN_SPLIT) {
+    if (rows <= QT / 2) body(std::true_type{});
+    else body(std::false_type{});
   } else {
-    // partial of key chunk `a`: unnormalised output and (max, sum) in the log2 domain
-    const size_t pr = ((size_t)bh * D.M + pos0 + qr) * D.pch + a;
-    float* orow = B.pp_o + pr * DD;
-#pragma unroll
-    for (int db = 0; db < ND; ++db)
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        float4 ov;
-        ov.x = o[db][4 * g + 0];
-        ov.y = o[db][4 * g + 1];
-        ov.z = o[db][4 * g + 2];
-        ov.w = o[db][4 * g + 3];
-        *reinterpret_cast<float4*>(orow + 32 * db + 8 * g + 4 * h) = ov;
-      }
-    if (h == 0) B.pp_ml[pr] = make_float2(m_run, lsum);
+    body(std::false_type{});
   }
 }
 
