@@ -5,9 +5,9 @@
 //
 // Normal equations per head, in float64:
 //   (Z^T W Z + Lambda) Theta = Z^T W R,  Z = [O_sp(probes), 1],  Lambda = diag(lambda 1_d, 0),
-// built as one bordered matrix [A | B] (A (d+1)x(d+1), B (d+1)xd), then solved by a
-// Cholesky factorisation held packed in LDS. A pivot at or below 1e-12 x max diag(A)
-// marks the head numerically singular.
+// built as one bordered matrix [A | B] (A (d+1)x(d+1), B (d+1)xd), then solved by a blocked
+// LDL^T factorisation (the Cholesky factorisation up to the scaling of its columns) held in
+// LDS. A pivot at or below 1e-12 x max diag(A) marks the head numerically singular.
 #include <type_traits>
 
 #include "common.h"
@@ -18,313 +18,420 @@ namespace spr {
 
 constexpr double kPivotRtol = 1e-12;
 
-// [A | B] in 32x32 tiles; column j < d+1 of the left factor is Z, column j >= d+1 is R.
+// Offset of element (r, c) of a row-major tile of 16 double columns whose 16-byte chunks are
+// XOR-swizzled by the row's group of four rows: rows 4 apart (the rows of neighbouring 4 x 4
+// blocks) fall on different LDS banks.
+__device__ constexpr int swz(int r, int c) { return 16 * r + ((((c >> 1) ^ ((r >> 2) & 7)) << 1) | (c & 1)); }
+
+// Makes the LDS writes of a wave visible to the same wave's later reads (no block barrier).
+__device__ inline void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// [A | B] of one head. The products of the probe sparse outputs' columns with the columns of
+// [O_sp | R] (R = O_dense - O_sp, the residual) form a d x 2d matrix, computed in 64 x 64
+// tiles (thread (ty, tx) of a 16 x 16 grid owns the 4 x 4 block at rows 4 ty, columns 4 tx):
+// the lower tiles of A (mirrored into the upper) and every tile of B. The weighted column
+// sums, which are the bias row of [A | B] and the bias column of A, come with them: wave 0
+// of each diagonal tile of A and of each first-row tile of B sums its 64 columns, and the
+// first tile adds the weight total (the bias pivot). Probes go 32 at a time through LDS (the
+// column operand pre-multiplied by the weight); the next 32 are loaded into registers while
+// the current ones are multiplied. Probes are summed in order, so the result does not depend
+// on scheduling.
 template <int DD>
 __global__ __launch_bounds__(256) void k_ridge_gram(Dims D, Bufs B, const float* o_psp, const float* o_dn,
                                                     const float* weights) {
   constexpr int n = DD + 1;
   constexpr int W = n + DD;
-  constexpr int PC = 32;  // probes per chunk
-  __shared__ double Zi[PC][33];
-  __shared__ double Zj[PC][33];
-  __shared__ double wv[PC];
-  const int bi = blockIdx.x, bj = blockIdx.y, bh = blockIdx.z;
-  const int i0 = bi * 32, j0 = bj * 32;
-  if (i0 >= n || j0 >= W) return;
-  const int tx = threadIdx.x % 32, ty = threadIdx.x / 32;  // 8 row groups of 4
-  double acc[4] = {0, 0, 0, 0};
-  const float* wp = weights ? weights + (size_t)bh * D.M : B.pweights + (size_t)bh * D.M;
+  constexpr int TI = DD / 64;               // row tiles (rows of A's z part)
+  constexpr int NA = TI * (TI + 1) / 2;     // lower tiles of A
+  constexpr int PC = 32;                    // probes per chunk
+  constexpr int NJ = 2;                     // 16-byte loads per thread and operand per chunk
+  __shared__ __attribute__((aligned(16))) double Zi[PC][64];
+  __shared__ __attribute__((aligned(16))) double Zj[PC][64];
+  const int bh = blockIdx.y, tix = blockIdx.x, tid = threadIdx.x;
+  // tile -> (ti, tj): the lower tiles of A first, then B's
+  int ti, tj;
+  if (tix < NA) {
+    ti = 0;
+    while ((ti + 1) * (ti + 2) / 2 <= tix) ++ti;
+    tj = tix - ti * (ti + 1) / 2;
+  } else {
+    ti = (tix - NA) / TI;
+    tj = TI + (tix - NA) % TI;
+  }
+  const bool bpart = tj >= TI;
+  const bool sums = bpart ? ti == 0 : ti == tj;  // this tile's wave 0 sums its columns
+  const int ty = tid / 16, tx = tid % 16;
+  const float* wp = (weights ? weights : B.pweights) + (size_t)bh * D.M;
   const float* zs = o_psp + (size_t)bh * D.M * DD;
   const float* zd = o_dn + (size_t)bh * D.M * DD;
-  auto zval = [&](int p, int col) -> double {
-    if (col < DD) return (double)zs[(size_t)p * DD + col];
-    if (col == DD) return 1.0;
-    const int c = col - n;
-    return (double)zd[(size_t)p * DD + c] - (double)zs[(size_t)p * DD + c];
-  };
-  for (int p0 = 0; p0 < D.M; p0 += PC) {
-    __syncthreads();
-    for (int e = threadIdx.x; e < PC * 32; e += 256) {
-      const int p = e / 32, c = e % 32;
-      const bool pv = p0 + p < D.M;
-      Zi[p][c] = (pv && i0 + c < n) ? zval(p0 + p, i0 + c) : 0.0;
-      Zj[p][c] = (pv && j0 + c < W) ? zval(p0 + p, j0 + c) : 0.0;
-    }
-    if (threadIdx.x < PC) wv[threadIdx.x] = p0 + threadIdx.x < D.M ? (double)wp[p0 + threadIdx.x] : 0.0;
-    __syncthreads();
-    for (int p = 0; p < PC; ++p) {
-      const double zj = wv[p] * Zj[p][tx];
+  const int ci = 64 * ti, cj = 64 * (bpart ? tj - TI : tj);
+  // staging: thread e covers probe p = e / 16 of the chunk, columns 4 (e % 16) .. + 3, for
+  // e = tid and tid + 256
+  float4 ri[NJ], rs[NJ], rd[NJ];
+  float rw[NJ];
+  auto load = [&](int p0) {
 #pragma unroll
-      for (int r = 0; r < 4; ++r) acc[r] = fma(Zi[p][ty * 4 + r], zj, acc[r]);
+    for (int u = 0; u < NJ; ++u) {
+      const int e = tid + 256 * u, p = p0 + e / 16, c = 4 * (e % 16);
+      const bool pv = p < D.M;
+      const size_t o = (size_t)(pv ? p : 0) * DD;
+      ri[u] = pv ? *reinterpret_cast<const float4*>(zs + o + ci + c) : make_float4(0.f, 0.f, 0.f, 0.f);
+      rs[u] = pv ? *reinterpret_cast<const float4*>(zs + o + cj + c) : make_float4(0.f, 0.f, 0.f, 0.f);
+      if (bpart) rd[u] = pv ? *reinterpret_cast<const float4*>(zd + o + cj + c) : make_float4(0.f, 0.f, 0.f, 0.f);
+      rw[u] = pv ? wp[p] : 0.f;
+    }
+  };
+  auto store = [&]() {
+#pragma unroll
+    for (int u = 0; u < NJ; ++u) {
+      const int e = tid + 256 * u, p = e / 16, c = 4 * (e % 16);
+      const double wv = (double)rw[u];
+      double2* di = reinterpret_cast<double2*>(&Zi[p][c]);
+      di[0] = make_double2((double)ri[u].x, (double)ri[u].y);
+      di[1] = make_double2((double)ri[u].z, (double)ri[u].w);
+      double v[4] = {(double)rs[u].x, (double)rs[u].y, (double)rs[u].z, (double)rs[u].w};
+      if (bpart) {
+        v[0] = (double)rd[u].x - v[0];
+        v[1] = (double)rd[u].y - v[1];
+        v[2] = (double)rd[u].z - v[2];
+        v[3] = (double)rd[u].w - v[3];
+      }
+      double2* dj = reinterpret_cast<double2*>(&Zj[p][c]);
+      dj[0] = make_double2(wv * v[0], wv * v[1]);
+      dj[1] = make_double2(wv * v[2], wv * v[3]);
+    }
+  };
+  double acc[4][4];
+#pragma unroll
+  for (int u = 0; u < 4; ++u)
+#pragma unroll
+    for (int v = 0; v < 4; ++v) acc[u][v] = 0.0;
+  double csum = 0.0, wsum = 0.0;  // wave 0: column tid's weighted sum; thread 0: weight total
+  if (D.M > 0) load(0);
+  for (int p0 = 0; p0 < D.M; p0 += PC) {
+    __syncthreads();  // (the previous chunk's reads are done)
+    store();
+    __syncthreads();
+    if (p0 + PC < D.M) load(p0 + PC);
+#pragma unroll 4
+    for (int p = 0; p < PC; ++p) {
+      const double2 a0 = *reinterpret_cast<const double2*>(&Zi[p][4 * ty]);
+      const double2 a1 = *reinterpret_cast<const double2*>(&Zi[p][4 * ty + 2]);
+      const double2 b0 = *reinterpret_cast<const double2*>(&Zj[p][4 * tx]);
+      const double2 b1 = *reinterpret_cast<const double2*>(&Zj[p][4 * tx + 2]);
+      const double av[4] = {a0.x, a0.y, a1.x, a1.y}, bv[4] = {b0.x, b0.y, b1.x, b1.y};
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) acc[u][v] = fma(av[u], bv[v], acc[u][v]);
+    }
+    if (sums && tid < 64) {
+      for (int p = 0; p < PC; ++p) csum += Zj[p][tid];
+      if (tix == 0 && tid == 0)
+        for (int p = 0; p < PC && p0 + p < D.M; ++p) wsum += (double)wp[p0 + p];
     }
   }
   double* G = B.gram + (size_t)bh * n * W;
 #pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    const int i = i0 + ty * 4 + r, j = j0 + tx;
-    if (i < n && j < W) {
-      double v = acc[r];
-      if (i == j && (i < DD || D.pen_bias)) v += (double)D.lambda;
-      G[(size_t)i * W + j] = v;
+  for (int u = 0; u < 4; ++u)
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const int i = ci + 4 * ty + u, c = cj + 4 * tx + v;
+      if (bpart) {
+        G[(size_t)i * W + n + c] = acc[u][v];
+      } else {
+        const double x = acc[u][v] + (i == c ? (double)D.lambda : 0.0);
+        G[(size_t)i * W + c] = x;
+        if (ti != tj) G[(size_t)c * W + i] = x;
+      }
+    }
+  if (sums && tid < 64) {
+    const int c = cj + tid;
+    if (bpart) {
+      G[(size_t)DD * W + n + c] = csum;
+    } else {
+      G[(size_t)DD * W + c] = csum;
+      G[(size_t)c * W + DD] = csum;
     }
   }
+  if (tix == 0 && tid == 0) G[(size_t)DD * W + DD] = wsum + (D.pen_bias ? (double)D.lambda : 0.0);
 }
 
-// One block of 512 threads per (head, 32 right-hand-side columns); each block redoes the
-// elimination of A. A = L1 Dg L1^T (unit lower L1, pivots Dg) by Gaussian elimination
-// without pivoting -- the Cholesky factorisation up to the scaling sqrt(Dg), stable for
-// symmetric positive definite A -- with the same row operations on the right-hand side,
-// Z = L1^-1 B, then L1^T X = Dg^-1 Z.
-//
-// The system lives in registers: thread (ty, tx) of a 16 x 32 grid holds A(i, k) for
-// i = ty + 16 r, k = tx + 32 q and B(i, c0 + tx). Elimination goes by panels of 3 columns:
-// the panel's owners publish its columns and right-hand-side rows in LDS (double-buffered,
-// so one barrier per panel), every thread factors the 3 x 3 diagonal block itself
-// (identical arithmetic everywhere, so a failed pivot stops all threads together), forms
-// the multipliers of its own rows and applies the rank-3 update to its elements. The back
-// substitution runs panel by panel from the last, publishing panel rows of L1 and of the
-// right-hand side the same way. A pivot at or below 1e-12 x max diag(A) (the squared
-// Cholesky diagonal) fails the head.
+// The ridge solve of one head for 32 of its right-hand-side columns (one block of 256 threads
+// per head and 32 columns; the blocks of a head factor A alike). The system is padded to
+// NP = 16 NB rows with unit pivots (zero right-hand side), A's lower 16 x 16 blocks and the
+// right-hand side sit in LDS, and A = L D L^T (L unit lower) by blocks of 16 columns:
+//   * panel k: each of waves 0 .. 2 takes the diagonal block's 16 rows (lanes 0 .. 15, the
+//     same in every wave) and 48 of the rows below (lanes 16 .. 63); wave 3 takes the
+//     diagonal rows and the 32 right-hand-side columns (lanes 16 .. 47). Row lanes hold 16
+//     panel entries, column lanes 16 right-hand-side entries. Column by column, the diagonal
+//     lanes publish their current entry of the pivot column in the wave's own LDS slots;
+//     every lane reads the pivot and the column, the rows below the pivot turn their entry
+//     into the multiplier and update the rest of their panel entries, and the right-hand
+//     side takes the forward substitution step. No block barrier inside a panel.
+//   * the trailing update, by all threads in 4 x 4 blocks: A_ij -= L_ik (D_k L_jk^T) on the
+//     lower blocks, B_i -= L_ik Z_k on the right-hand side.
+// Then X = L^-T D^-1 Z by blocks from the last: a 16-step substitution with the diagonal
+// block (one lane per column), and the rows above updated by all threads.
 template <int DD>
-__global__ __launch_bounds__(512) void k_ridge_solve(Dims D, Bufs B, float* coeffs) {
+__global__ __launch_bounds__(256) void k_ridge_solve(Dims D, Bufs B, float* coeffs) {
   constexpr int n = DD + 1;
   constexpr int W = n + DD;
-  constexpr int CB = 32;  // right-hand-side columns per block
-  constexpr int TY = 16, TX = 32;
-  constexpr int RT = (n + TY - 1) / TY;  // rows per thread
-  constexpr int QT = (n + TX - 1) / TX;  // matrix columns per thread
-  constexpr int NP = RT * TY > QT * TX ? RT * TY : QT * TX;  // padded index range
-  constexpr int P = 3;                   // panel width (n = 129 = 43 panels)
-  __shared__ double cb[2][P][NP];        // panel columns / panel rows of L1
-  __shared__ double rb[2][P][CB];        // panel rows of the right-hand side
-  __shared__ double piv[NP];
+  constexpr int NB = (n + 15) / 16;          // 16-row blocks of the padded system
+  constexpr int NP = 16 * NB;
+  constexpr int NLB = NB * (NB + 1) / 2;     // lower blocks
+  constexpr int CB = 32;                     // right-hand-side columns per block
+  constexpr int NBR = NP - 16;               // rows below the first diagonal block
+  static_assert(NBR <= 144, "three waves of 48 rows below the diagonal block");
+  __shared__ __attribute__((aligned(16))) double Ab[NLB * 256];  // block (bi, bj): swz(r, c)
+  __shared__ __attribute__((aligned(16))) double Bs[NP * CB];
+  __shared__ __attribute__((aligned(16))) double Wp[NBR * 16];   // D_k L_ik^T rows of the panel, swz
+  __shared__ double xc[4][16];                                    // per-wave pivot column
+  __shared__ double rdv[NP];                                      // reciprocal pivots
   __shared__ double s_floor;
+  auto blk = [](int bi, int bj) { return (bi * (bi + 1) / 2 + bj) * 256; };
   const int bh = blockIdx.y, c0 = blockIdx.x * CB;
-  const int tid = threadIdx.x, ty = tid / TX, tx = tid % TX;
+  const int tid = threadIdx.x, l = lane_id();
+  const int w = __builtin_amdgcn_readfirstlane(tid / kWave);
   float* Th = coeffs + (size_t)bh * n * DD;
-  const bool col_ok = c0 + tx < DD;
   if (D.M == 0) {
-#pragma unroll
-    for (int r = 0; r < RT; ++r) {
-      const int i = ty + TY * r;
-      if (i < n && col_ok) Th[(size_t)i * DD + c0 + tx] = 0.f;
+    for (int e = tid; e < n * CB; e += 256) {
+      const int i = e / CB, c = e % CB;
+      if (c0 + c < DD) Th[(size_t)i * DD + c0 + c] = 0.f;
     }
     return;
   }
   const double* G = B.gram + (size_t)bh * n * W;
-  double a[RT][QT], b[RT];
+  // thread t loads element (t / 16, t % 16) of every lower block and rows t / 32 + 8 j of the
+  // right-hand side, all loads issued before the first store (fully unrolled: block b's
+  // coordinates are compile-time constants)
+  {
+    const int r = tid / 16, c = tid % 16;
+    double va[NLB];
 #pragma unroll
-  for (int r = 0; r < RT; ++r) {
-    const int i = ty + TY * r;
+    for (int bi = 0, b = 0; bi < NB; ++bi)
 #pragma unroll
-    for (int q = 0; q < QT; ++q) {
-      const int k = tx + TX * q;
-      a[r][q] = (i < n && k < n) ? G[(size_t)i * W + k] : 0.0;
+      for (int bj = 0; bj <= bi; ++bj, ++b) {
+        const int i = 16 * bi + r, k = 16 * bj + c;
+        const double g = G[(size_t)min(i, n - 1) * W + min(k, n - 1)];  // (clamped: no branch)
+        va[b] = (i < n && k < n) ? g : (i == k ? 1.0 : 0.0);
+      }
+    constexpr int NBL = NP * CB / 256;
+    double vb[NBL];
+    const int rb = tid / CB, cb = tid % CB;
+#pragma unroll
+    for (int j = 0; j < NBL; ++j) {
+      const int i = rb + (256 / CB) * j;
+      const double g = G[(size_t)min(i, n - 1) * W + n + min(c0 + cb, DD - 1)];
+      vb[j] = (i < n && c0 + cb < DD) ? g : 0.0;
     }
-    b[r] = (i < n && col_ok) ? G[(size_t)i * W + n + c0 + tx] : 0.0;
+#pragma unroll
+    for (int b = 0; b < NLB; ++b) Ab[256 * b + swz(r, c)] = va[b];
+#pragma unroll
+    for (int j = 0; j < NBL; ++j) Bs[256 * j + tid] = vb[j];
   }
-  // entries never published stay zero (indices beyond n)
-  for (int e = tid; e < 2 * P * NP; e += 512) (&cb[0][0][0])[e] = 0.0;
-  for (int e = tid; e < 2 * P * CB; e += 512) (&rb[0][0][0])[e] = 0.0;
-  if (tid < 64) {
+  if (tid < kWave) {
     double mx = 0.0;
-    for (int i = tid; i < n; i += 64) mx = fmax(mx, G[(size_t)i * W + i]);
-    for (int o = 32; o > 0; o >>= 1) mx = fmax(mx, __shfl_xor(mx, o, 64));
+    for (int i = tid; i < n; i += kWave) mx = fmax(mx, G[(size_t)i * W + i]);
+    for (int o = 32; o > 0; o >>= 1) mx = fmax(mx, __shfl_xor(mx, o, kWave));
     if (tid == 0) s_floor = kPivotRtol * mx;
   }
   __syncthreads();
   const double floor_ = s_floor;
   bool fail = false;
-  int buf = 0;
-  for (int j0 = 0; j0 < n; j0 += P, buf ^= 1) {
-    const int pw = min(P, n - j0);
-    // owners publish the panel columns (rows >= j0) and the panel rows of the right-hand side.
-    // Here and below, a block of TY rows or TX columns that lies wholly before j0 is skipped:
-    // its entries are final (block-uniform branches).
+  for (int k = 0; k < NB; ++k) {
+    const int j0 = 16 * k, nbr = NP - j0 - 16;
+    const int b = 48 * w + l - 16;  // row below the diagonal block (waves 0 .. 2)
+    const bool diag = l < 16;
+    const bool below = w < 3 && l >= 16 && b < nbr;
+    const bool rhs = w == 3 && l >= 16 && l < 16 + CB;
+    const int ib = j0 + 16 + b;
+    const int rrow = diag ? l : ib % 16, rsw = (rrow >> 2) & 7;  // row in its block, its swizzle
+    double* rowp = diag ? &Ab[blk(k, k) + 16 * l] : (below ? &Ab[blk(ib / 16, k) + 16 * rrow] : nullptr);
+    double a[16];
+    if (diag || below) {
 #pragma unroll
-    for (int q = 0; q < QT; ++q) {
-      if (TX * q + TX <= j0) continue;
-      const int pc = tx + TX * q - j0;
-      if (pc >= 0 && pc < pw) {
-#pragma unroll
-        for (int r = 0; r < RT; ++r) {
-          if (TY * r + TY <= j0) continue;
-          const int i = ty + TY * r;
-          if (i >= j0 && i < n) cb[buf][pc][i] = a[r][q];
-        }
+      for (int c = 0; c < 16; c += 2) {
+        const double2 v = *reinterpret_cast<const double2*>(rowp + 2 * ((c >> 1) ^ rsw));
+        a[c] = v.x;
+        a[c + 1] = v.y;
       }
-    }
+    } else {
 #pragma unroll
-    for (int r = 0; r < RT; ++r) {
-      if (TY * r + TY <= j0) continue;
-      const int pr = ty + TY * r - j0;
-      if (pr >= 0 && pr < pw) rb[buf][pr][tx] = b[r];
+      for (int r = 0; r < 16; ++r) a[r] = rhs ? Bs[(j0 + r) * CB + l - 16] : 0.0;
+    }
+    double dk[16];
+#pragma unroll
+    for (int p = 0; p < 16; ++p) {
+      wave_lds_sync();  // (the previous column's reads are done)
+      if (diag) xc[w][l] = a[p];
+      wave_lds_sync();
+      const double d = xc[w][p];
+      double wc[16];
+#pragma unroll
+      for (int c = p + 1; c < 16; ++c) wc[c] = xc[w][c];
+      fail |= j0 + p < n && !(d > floor_);
+      // 1 / d: the hardware reciprocal and two Newton steps (the pivot is > 0 here or the
+      // head fails)
+      double rd = __builtin_amdgcn_rcp(d);
+      rd = fma(rd, fma(-d, rd, 1.0), rd);
+      rd = fma(rd, fma(-d, rd, 1.0), rd);
+      dk[p] = d;
+      if (tid == 0) rdv[j0 + p] = rd;
+      // one update for every lane: a row lane subtracts its multiplier times the pivot
+      // column's entries W[x] (x > p), a column lane subtracts L[x][p] z_p (the same product);
+      // other entries it touches are never read. A row lane then keeps its multiplier in
+      // place of its pivot-column entry; the pivot row keeps the pivot, a column lane z_p.
+      const double lv = a[p] * rd;
+#pragma unroll
+      for (int x = p + 1; x < 16; ++x) a[x] = fma(-lv, wc[x], a[x]);
+      a[p] = (rhs || l == p) ? a[p] : lv;
+    }
+    if (fail) break;  // (every thread of the block takes the same pivots)
+    if ((diag && w == 0) || below) {
+#pragma unroll
+      for (int c = 0; c < 16; c += 2)
+        *reinterpret_cast<double2*>(rowp + 2 * ((c >> 1) ^ rsw)) = make_double2(a[c], a[c + 1]);
+    }
+    if (below) {
+#pragma unroll
+      for (int c = 0; c < 16; c += 2)
+        *reinterpret_cast<double2*>(&Wp[swz(b, c)]) = make_double2(a[c] * dk[c], a[c + 1] * dk[c + 1]);
+    }
+    if (rhs) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) Bs[(j0 + r) * CB + l - 16] = a[r];
     }
     __syncthreads();
-    // the diagonal block, factored by every thread alike: Lb unit lower, db pivots; entries
-    // beyond the panel width are zero (their reciprocal pivots too)
-    double Lb[P][P], db[P], rd[P];
+    // trailing update: lower blocks of A, then the right-hand side rows below the panel
+    const int m = NB - 1 - k;
+    const int nA = 16 * (m * (m + 1) / 2), nR = 32 * m;
+    for (int it = tid; it < nA + nR; it += 256) {
+      double acc[4][4];
+      const double* Lr;
+      if (it < nA) {
+        const int pr = it / 16, sub = it % 16;
+        int bi = 0;
+        while ((bi + 1) * (bi + 2) / 2 <= pr) ++bi;
+        const int bj = pr - bi * (bi + 1) / 2, rr = sub / 4, cc = sub % 4;
+        const int wb = 16 * bj + 4 * cc, wsw = (wb >> 2) & 7;  // first W row, its swizzle
+        Lr = &Ab[blk(k + 1 + bi, k) + 64 * rr];  // rows 4 rr .. 4 rr + 3 (swizzle rr)
+        const double* Wr = &Wp[16 * wb];
+        double* At = &Ab[blk(k + 1 + bi, k + 1 + bj)];
 #pragma unroll
-    for (int p1 = 0; p1 < P; ++p1) {
-      const bool in1 = p1 < pw;
+        for (int u = 0; u < 4; ++u)
 #pragma unroll
-      for (int p2 = 0; p2 < p1; ++p2) {
-        double v = cb[buf][p2][j0 + p1];
+          for (int v = 0; v < 4; ++v) acc[u][v] = At[swz(4 * rr + u, 4 * cc + v)];
 #pragma unroll
-        for (int m = 0; m < p2; ++m) v -= Lb[p1][m] * Lb[p2][m] * db[m];
-        Lb[p1][p2] = in1 ? v * rd[p2] : 0.0;
-      }
-      double d = cb[buf][p1][j0 + p1];
+        for (int p = 0; p < 16; p += 2) {
+          double2 lv[4], wv[4];
 #pragma unroll
-      for (int m = 0; m < p1; ++m) d -= Lb[p1][m] * Lb[p1][m] * db[m];
-      db[p1] = in1 ? d : 1.0;
-      rd[p1] = in1 ? 1.0 / d : 0.0;
-      fail |= in1 && !(d > floor_);
-    }
-    if (fail) break;
-    if (tid == 0) {
+          for (int u = 0; u < 4; ++u) lv[u] = *reinterpret_cast<const double2*>(Lr + 16 * u + 2 * ((p >> 1) ^ rr));
 #pragma unroll
-      for (int p = 0; p < P; ++p)
-        if (p < pw) piv[j0 + p] = db[p];
-    }
-    // the panel entries of my columns, solved (y Lb^T = c); zero unless a trailing column
-    double yq[QT][P];
+          for (int v = 0; v < 4; ++v) wv[v] = *reinterpret_cast<const double2*>(Wr + 16 * v + 2 * ((p >> 1) ^ wsw));
 #pragma unroll
-    for (int q = 0; q < QT; ++q) {
-      if (TX * q + TX <= j0) continue;  // (yq of such a block is never read)
-      const int k = tx + TX * q;
-      const bool tk = k >= j0 + pw && k < n;
-      double y[P];
+          for (int u = 0; u < 4; ++u)
 #pragma unroll
-      for (int p = 0; p < P; ++p) {
-        double v = cb[buf][p][k];
-#pragma unroll
-        for (int m = 0; m < p; ++m) v -= y[m] * Lb[p][m];
-        y[p] = v;
-        yq[q][p] = (tk && p < pw) ? v : 0.0;
-      }
-    }
-    // right-hand side of the panel: z = Lb^-1 b_J
-    double z[P];
-#pragma unroll
-    for (int p = 0; p < P; ++p) {
-      double v = rb[buf][p][tx];
-#pragma unroll
-      for (int m = 0; m < p; ++m) v -= Lb[p][m] * z[m];
-      z[p] = p < pw ? v : 0.0;
-    }
-    // row by row: the multipliers of my row (below the diagonal of a panel column they are
-    // L1's entries, for the panel's own rows too), the rank-pw update of a trailing row and
-    // its right-hand side; the panel rows of the right-hand side take z
-#pragma unroll
-    for (int r = 0; r < RT; ++r) {
-      if (TY * r + TY <= j0) continue;
-      const int i = ty + TY * r;
-      const bool tr = i >= j0 + pw && i < n;
-      double lf[P], li[P];
-#pragma unroll
-      for (int p = 0; p < P; ++p) {
-        double v = cb[buf][p][i];
-#pragma unroll
-        for (int m = 0; m < p; ++m) v -= lf[m] * db[m] * Lb[p][m];
-        lf[p] = v * rd[p];
-        li[p] = tr ? lf[p] : 0.0;
-      }
-#pragma unroll
-      for (int q = 0; q < QT; ++q) {
-        if (TX * q + TX <= j0) continue;
-        double v = a[r][q];
-#pragma unroll
-        for (int p = 0; p < P; ++p) v -= li[p] * yq[q][p];
-        const int k = tx + TX * q, pc = k - j0;
-        if (pc >= 0 && pc < pw && i > k && i < n) {
-          double m = lf[0];
-#pragma unroll
-          for (int u = 1; u < P; ++u) m = pc == u ? lf[u] : m;
-          v = m;
+            for (int v = 0; v < 4; ++v) {
+              acc[u][v] = fma(-lv[u].x, wv[v].x, acc[u][v]);
+              acc[u][v] = fma(-lv[u].y, wv[v].y, acc[u][v]);
+            }
         }
-        a[r][q] = v;
-      }
-      double v = b[r];
 #pragma unroll
-      for (int p = 0; p < P; ++p) v -= li[p] * z[p];
-      const int pr = i - j0;
-      if (pr >= 0 && pr < pw) {
-        double m = z[0];
+        for (int u = 0; u < 4; ++u)
 #pragma unroll
-        for (int u = 1; u < P; ++u) m = pr == u ? z[u] : m;
-        v = m;
-      }
-      b[r] = v;
-    }
-  }
-  if (fail) {
+          for (int v = 0; v < 4; ++v) At[swz(4 * rr + u, 4 * cc + v)] = acc[u][v];
+      } else {
+        const int t = it - nA, bi = t / 32, sub = t % 32, rr = sub / 8, cc = sub % 8;
+        Lr = &Ab[blk(k + 1 + bi, k) + 64 * rr];
+        double* dst = &Bs[(16 * (k + 1 + bi) + 4 * rr) * CB + 4 * cc];
 #pragma unroll
-    for (int r = 0; r < RT; ++r) {
-      const int i = ty + TY * r;
-      if (i < n && col_ok) Th[(size_t)i * DD + c0 + tx] = 0.f;
-    }
-    if (tid == 0) B.status[bh] = 5;  // SPARSEPR_ERR_NUMERICAL
-    return;
-  }
-  __syncthreads();
+        for (int u = 0; u < 4; ++u)
 #pragma unroll
-  for (int r = 0; r < RT; ++r) {
-    const int i = ty + TY * r;
-    if (i < n) b[r] /= piv[i];
-  }
-  // ---- L1^T X = Dg^-1 Z, panels from the last
-  for (int j0 = ((n - 1) / P) * P; j0 >= 0; j0 -= P, buf ^= 1) {
-    const int pw = min(P, n - j0);
-    // owners publish the panel rows: right-hand side, and L1 left of the diagonal
+          for (int v = 0; v < 4; ++v) acc[u][v] = dst[u * CB + v];
 #pragma unroll
-    for (int r = 0; r < RT; ++r) {
-      if (TY * r + TY <= j0 || TY * r >= j0 + pw) continue;
-      const int i = ty + TY * r;
-      const int pr = i - j0;
-      if (pr >= 0 && pr < pw) {
-        rb[buf][pr][tx] = b[r];
+        for (int p = 0; p < 16; p += 2) {
+          double2 lv[4];
 #pragma unroll
-        for (int q = 0; q < QT; ++q) {
-          const int k = tx + TX * q;
-          if (k < i) cb[buf][pr][k] = a[r][q];
+          for (int u = 0; u < 4; ++u) lv[u] = *reinterpret_cast<const double2*>(Lr + 16 * u + 2 * ((p >> 1) ^ rr));
+#pragma unroll
+          for (int q = 0; q < 2; ++q) {
+            const double* zr = &Bs[(j0 + p + q) * CB + 4 * cc];
+            const double2 z0 = *reinterpret_cast<const double2*>(zr), z1 = *reinterpret_cast<const double2*>(zr + 2);
+            const double zv[4] = {z0.x, z0.y, z1.x, z1.y};
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+              const double lu = q ? lv[u].y : lv[u].x;
+#pragma unroll
+              for (int v = 0; v < 4; ++v) acc[u][v] = fma(-lu, zv[v], acc[u][v]);
+            }
+          }
         }
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+#pragma unroll
+          for (int v = 0; v < 4; ++v) dst[u * CB + v] = acc[u][v];
       }
     }
     __syncthreads();
-    // Lb^T x = z inside the panel, for my column
-    double x[P];
+  }
+  if (!fail) {
+    // y = D^-1 z, then L^T x = y by blocks from the last
+    for (int e = tid; e < NP * CB; e += 256) Bs[e] *= rdv[e / CB];
+    __syncthreads();
+    for (int k = NB - 1; k >= 0; --k) {
+      const int j0 = 16 * k;
+      if (w == 0 && l < CB) {
+        double y[16];
 #pragma unroll
-    for (int p = P - 1; p >= 0; --p) {
-      double v = rb[buf][p][tx];
+        for (int r = 0; r < 16; ++r) y[r] = Bs[(j0 + r) * CB + l];
+        const double* Lk = &Ab[blk(k, k)];
 #pragma unroll
-      for (int m = p + 1; m < P; ++m) v -= cb[buf][m][j0 + p] * x[m];
-      x[p] = p < pw ? v : 0.0;
-    }
+        for (int r = 15; r > 0; --r)
 #pragma unroll
-    for (int r = 0; r < RT; ++r) {
-      if (TY * r >= j0 + pw) continue;  // rows wholly after the panel are final
-      const int i = ty + TY * r;
-      double v = b[r];
-      if (i < j0) {
+          for (int q = 0; q < r; ++q) y[q] = fma(-Lk[swz(r, q)], y[r], y[q]);
 #pragma unroll
-        for (int p = 0; p < P; ++p) v -= cb[buf][p][i] * x[p];
+        for (int r = 0; r < 16; ++r) Bs[(j0 + r) * CB + l] = y[r];
       }
-      const int pr = i - j0;
-      if (pr >= 0 && pr < pw) {
-        double m = x[0];
+      __syncthreads();
+      for (int it = tid; it < 32 * k; it += 256) {
+        const int j = it / 32, sub = it % 32, rr = sub / 8, cc = sub % 8;
+        const double* Lb = &Ab[blk(k, j)];  // columns 4 rr .. 4 rr + 3 of block (k, j), by rows p
+        double* dst = &Bs[(16 * j + 4 * rr) * CB + 4 * cc];
+        double acc[4][4];
 #pragma unroll
-        for (int u = 1; u < P; ++u) m = pr == u ? x[u] : m;
-        v = m;
+        for (int u = 0; u < 4; ++u)
+#pragma unroll
+          for (int v = 0; v < 4; ++v) acc[u][v] = dst[u * CB + v];
+#pragma unroll
+        for (int p = 0; p < 16; ++p) {
+          const double2 l0 = *reinterpret_cast<const double2*>(Lb + swz(p, 4 * rr));
+          const double2 l1 = *reinterpret_cast<const double2*>(Lb + swz(p, 4 * rr + 2));
+          const double* xr = &Bs[(j0 + p) * CB + 4 * cc];
+          const double2 x0 = *reinterpret_cast<const double2*>(xr), x1 = *reinterpret_cast<const double2*>(xr + 2);
+          const double lu[4] = {l0.x, l0.y, l1.x, l1.y}, xv[4] = {x0.x, x0.y, x1.x, x1.y};
+#pragma unroll
+          for (int u = 0; u < 4; ++u)
+#pragma unroll
+            for (int v = 0; v < 4; ++v) acc[u][v] = fma(-lu[u], xv[v], acc[u][v]);
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+#pragma unroll
+          for (int v = 0; v < 4; ++v) dst[u * CB + v] = acc[u][v];
       }
-      b[r] = v;
+      __syncthreads();
     }
   }
-#pragma unroll
-  for (int r = 0; r < RT; ++r) {
-    const int i = ty + TY * r;
-    if (i < n && col_ok) Th[(size_t)i * DD + c0 + tx] = (float)b[r];
+  for (int e = tid; e < n * CB; e += 256) {
+    const int i = e / CB, c = e % CB;
+    if (c0 + c < DD) Th[(size_t)i * DD + c0 + c] = fail ? 0.f : (float)Bs[i * CB + c];
   }
+  if (fail && tid == 0) B.status[bh] = 5;  // SPARSEPR_ERR_NUMERICAL
 }
 
 // out_i = o_i + [o_i, 1] Theta (unprobed rows); probe rows take their exact dense output.
@@ -564,16 +671,16 @@ __global__ __launch_bounds__(DD) void k_fit_mean(Dims D, Bufs B, const float* o_
 template <int DD>
 static void fit_impl(const Dims& D, const Bufs& B, const float* o_psp, const float* o_dn, const float* w, float* coeffs,
                      hipStream_t s) {
-  constexpr int n = DD + 1;
   if (D.correction != 0) {
     hipLaunchKernelGGL((k_fit_mean<DD>), dim3(D.BH), dim3(DD), 0, s, D, B, o_psp, o_dn, w, coeffs);
     return;
   }
   if (D.M > 0) {
-    dim3 g((n + 31) / 32, (n + DD + 31) / 32, D.BH);
-    hipLaunchKernelGGL((k_ridge_gram<DD>), g, dim3(256), 0, s, D, B, o_psp, o_dn, w);
+    constexpr int TI = DD / 64;
+    hipLaunchKernelGGL((k_ridge_gram<DD>), dim3(TI * (TI + 1) / 2 + TI * TI, D.BH), dim3(256), 0, s, D, B, o_psp,
+                       o_dn, w);
   }
-  hipLaunchKernelGGL((k_ridge_solve<DD>), dim3((DD + 31) / 32, D.BH), dim3(512), 0, s, D, B, coeffs);
+  hipLaunchKernelGGL((k_ridge_solve<DD>), dim3((DD + 31) / 32, D.BH), dim3(256), 0, s, D, B, coeffs);
   if (D.output_rank > 0 && D.M > 0) {
     hipLaunchKernelGGL((k_resid_cov<DD>), dim3(DD / 32, DD / 32, D.BH), dim3(256), 0, s, D, B, o_psp, o_dn, w);
     launch_residual_projector(D, B, s);
