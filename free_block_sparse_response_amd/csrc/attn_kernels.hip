@@ -164,28 +164,45 @@ __global__ __launch_bounds__(64 * W, W == 4 ? 2 : 1) void k_bsfa_bf16(const bf16
   constexpr int PF = 4;                      // operand reads ahead of their product
   constexpr int QT = 32 * W;                 // query rows per tile
   constexpr int KTB = KT * DD;               // elements of one K or V^T tile
-  // 8-wave block-sparse tiles of at most 128 rows run split: waves w and w + 4 hold the same
-  // 32 rows, each half walks half of the tile's key tiles with its own staging buffers, and
-  // the two partial softmax states are merged through LDS at the end
+  // 8-wave block-sparse work items (the attention item table) run one chunk of up to 256
+  // rows on all waves, or two key streams, each with its own staging buffers and staged by
+  // one wave half: a chunk of at most 128 rows split (waves w and w + 4 hold the same 32 rows
+  // and walk half of the chunk's key tiles each; the two partial softmax states are merged
+  // through LDS at the end), or a pair of chunks of two query groups (waves 0 .. w_0 - 1 on
+  // the first, the rest on the second, each on its own group's keys)
   constexpr bool CAN_SPLIT = MODE == 0 && W == 8;
   constexpr int NS = CAN_SPLIT ? 2 : 1;      // key streams
   static_assert((DD == 64 || DD == 128) && (KT == 32 || KT == 64), "tile shape");
   static_assert(STG == 1 || STG == 2, "staging depth");
   __shared__ __attribute__((aligned(1024))) bf16 smem[NS * 4 * KTB];  // per stream: K[2], V^T[2]
-  __shared__ int2 runs_s[kMaxGroups];
+  __shared__ int2 runs_s[NS][kMaxGroups];
 
   const int nb = gridDim.x;
   const int bid = xcd_remap(blockIdx.x, nb);
   int bh, rows, a = 0, pos0 = 0;
+  int kind = -1, a1 = 0, pos1 = 0, rows1 = 0;  // the second chunk of a pair (kind >= 0)
   if (MODE != 1) {
     bh = bid / D.max_atiles;
     const int t = bid % D.max_atiles;
-    if (t >= B.antiles[bh]) return;
-    const int2 tl = B.atiles[(size_t)bh * D.max_atiles + t];
-    a = tl.x;
-    pos0 = tl.y;
-    const int end = B.qoff[(size_t)bh * (D.Cq + 1) + a + 1];
-    rows = min(QT, end - pos0);
+    const int* qo = B.qoff + (size_t)bh * (D.Cq + 1);
+    if constexpr (CAN_SPLIT) {
+      if (t >= B.nptiles[bh]) return;
+      const int4 pt = B.ptiles[(size_t)bh * D.max_atiles + t];
+      a = pt.x;
+      pos0 = pt.y;
+      kind = pt.z;
+      if (kind >= 0) {
+        a1 = pt.z;
+        pos1 = pt.w;
+        rows1 = min(QT, qo[a1 + 1] - pos1);
+      }
+    } else {
+      if (t >= B.antiles[bh]) return;
+      const int2 tl = B.atiles[(size_t)bh * D.max_atiles + t];
+      a = tl.x;
+      pos0 = tl.y;
+    }
+    rows = min(QT, qo[a + 1] - pos0);
   } else {
     // probe rows: (head, QT-row tile, key chunk)
     const int per = ((D.M + QT - 1) / QT) * D.pch;
@@ -200,33 +217,46 @@ __global__ __launch_bounds__(64 * W, W == 4 ? 2 : 1) void k_bsfa_bf16(const bf16
   const float c2 = D.log2_scale;
   const bf16* kpb = (const bf16*)B.kp + (size_t)bh * D.Npad * DD;
   const bf16* vtb = (const bf16*)B.vpt + (size_t)bh * DD * D.Npad;
-  int nr = 0;
+  int nr = 0, nr1 = 0;
   if (MODE != 1) {
-    const int2* rg = B.runs + (size_t)bh * D.Cq * D.Ck + B.row_ptr[(size_t)bh * (D.Cq + 1) + a];
+    const int* rp = B.row_ptr + (size_t)bh * (D.Cq + 1);
+    const int2* rg = B.runs + (size_t)bh * D.Cq * D.Ck + rp[a];
     nr = __builtin_amdgcn_readfirstlane(B.nruns[(size_t)bh * D.Cq + a]);  // <= C_k <= kMaxGroups
-    for (int i = tid; i < nr; i += 64 * W) runs_s[i] = rg[i];
+    for (int i = tid; i < nr; i += 64 * W) runs_s[0][i] = rg[i];
+    if (CAN_SPLIT && kind >= 0) {
+      const int2* rg1 = B.runs + (size_t)bh * D.Cq * D.Ck + rp[a1];
+      nr1 = __builtin_amdgcn_readfirstlane(B.nruns[(size_t)bh * D.Cq + a1]);
+      for (int i = tid; i < nr1; i += 64 * W) runs_s[NS - 1][i] = rg1[i];
+    }
     __syncthreads();
   }
 
-  auto body = [&](auto split_tag) {
-    constexpr bool SPLIT = decltype(split_tag)::value;
-    constexpr int WL = SPLIT ? W / 2 : W;      // waves per key stream: loaders and row slices
-    constexpr int STGX = SPLIT ? 1 : STG;      // a split stream stages one step ahead
+  // BM 0: one chunk on all waves; 1: one chunk, its keys split between the wave halves;
+  // 2: a pair of chunks
+  auto body = [&](auto mode_tag) {
+    constexpr int BM = decltype(mode_tag)::value;
+    constexpr bool TWO = BM != 0;              // two key streams
+    constexpr int WL = TWO ? W / 2 : W;        // loader waves per key stream
+    constexpr int STGX = TWO ? 1 : STG;        // two streams stage one step ahead
     constexpr int KI = KT * KRB / (1024 * WL); // 1 KB loads per wave per K tile
     constexpr int VI = DD * VRB / (1024 * WL); // 1 KB loads per wave per V^T tile
     static_assert(KI >= 1 && VI >= 1, "loads per wave");
-    const int stream = SPLIT ? w / WL : 0;
-    const int sw = SPLIT ? w % WL : w;         // row slice and loader index in the stream
-    bf16* const sbase = smem + stream * 4 * KTB;
-    auto Kb = [&](int p) { return sbase + p * KTB; };
-    auto Vb = [&](int p) { return sbase + (2 + p) * KTB; };
+    const int ls = TWO ? w / WL : 0;           // the stream this wave stages
+    const int lw = TWO ? w % WL : w;           // its loader index there
+    const int wa = BM == 2 ? (rows + 31) / 32 : WL;    // waves on the first chunk of a pair
+    const int cs = BM == 2 ? (w < wa ? 0 : 1) : ls;    // the stream this wave computes
+    const int sw = BM == 2 ? (cs ? w - wa : w) : lw;   // its row slice there
+    const int crows = BM == 2 && cs ? rows1 : rows;    // rows and first position of its chunk
+    const int cpos = BM == 2 && cs ? pos1 : pos0;
+    auto Kb = [&](int st, int p) { return smem + (4 * st + p) * KTB; };
+    auto Vb = [&](int st, int p) { return smem + (4 * st + 2 + p) * KTB; };
 
     // ---- Q^T operand in registers: query (32 sw + l32), d-slots 16c + 8h .. +7
     const int qr = 32 * sw + l32;
-    const bool qvalid = qr < rows;
-    const bool wave_active = 32 * sw < rows;  // a wave past the tile's last row only stages K / V
+    const bool qvalid = qr < crows;
+    const bool wave_active = 32 * sw < crows;  // a wave past its chunk's last row only stages K / V
     int tok;
-    if (MODE != 1) tok = B.qperm[(size_t)bh * D.N + pos0 + (qvalid ? qr : 0)];
+    if (MODE != 1) tok = B.qperm[(size_t)bh * D.N + cpos + (qvalid ? qr : 0)];
     else tok = B.probes[(size_t)bh * D.M + pos0 + (qvalid ? qr : 0)];
     const bf16* qrow = q + ((size_t)bh * D.N + tok) * DD;
     bf16x8 qreg[NC];
@@ -250,9 +280,9 @@ __global__ __launch_bounds__(64 * W, W == 4 ? 2 : 1) void k_bsfa_bf16(const bf16
     auto vswz = [](int r) { return VW == 4 ? ((r >> 2) & 3) : (VW == 8 ? ((r >> 1) & 7) : (r & 15)); };
     unsigned klane, vlane;
     {
-      const int r = KR * sw + l / KW;  // row of this lane in the wave's first load (load g = WL i + sw)
+      const int r = KR * lw + l / KW;  // row of this lane in the wave's first load (load g = WL i + lw)
       klane = (unsigned)(r * KRB + 16 * ((l % KW) ^ kswz(r)));
-      const int rv = VR * sw + l / VW;
+      const int rv = VR * lw + l / VW;
       vlane = (unsigned)(rv * 2 * D.Npad + 16 * ((l % VW) ^ vswz(rv)));
     }
     // Every step issues the same loads (past the last tile they re-read the current one,
@@ -274,11 +304,11 @@ __global__ __launch_bounds__(64 * W, W == 4 ? 2 : 1) void k_bsfa_bf16(const bf16
     };
     auto store_k = [&](const Stage& st, bf16* dst) {
 #pragma unroll
-      for (int i = 0; i < KI; ++i) *reinterpret_cast<bf16x8*>(dst + (WL * i + sw) * 512 + 8 * l) = st.k[i];
+      for (int i = 0; i < KI; ++i) *reinterpret_cast<bf16x8*>(dst + (WL * i + lw) * 512 + 8 * l) = st.k[i];
     };
     auto store_v = [&](const Stage& st, bf16* dst) {
 #pragma unroll
-      for (int i = 0; i < VI; ++i) *reinterpret_cast<bf16x8*>(dst + (WL * i + sw) * 512 + 8 * l) = st.v[i];
+      for (int i = 0; i < VI; ++i) *reinterpret_cast<bf16x8*>(dst + (WL * i + lw) * 512 + 8 * l) = st.v[i];
     };
 
     // operand reads. K: row 32 sb + pi(l32), chunk 2c + h -> byte sb * 32 rows + (kaddr ^ 32c);
@@ -440,25 +470,6 @@ __global__ __launch_bounds__(64 * W, W == 4 ? 2 : 1) void k_bsfa_bf16(const bf16
       }
     };
 
-    // ---- the key tiles of this stream
-    TileWalk<KT> ts;
-    int Ts = 0, nsteps = 0;  // split: this stream's tiles, and the steps every stream runs
-    bool has;                // the stream's first tile exists
-    if (MODE != 1) {
-      ts.runs = runs_s;
-      ts.nr = nr;
-      has = ts.first();
-      if (SPLIT) {
-        const int T = ts.count();  // >= 1: every query group keeps a key group
-        nsteps = (T + 1) / 2;      // stream 0 takes the first half (rounded up)
-        Ts = stream ? T - nsteps : nsteps;
-        has = Ts > 0;
-        if (stream && has) ts.seek(nsteps);
-      }
-    } else {
-      const int clo = a * D.pkc;
-      has = ts.first_single(clo, min(D.N, clo + D.pkc));
-    }
     // Tile j: K(j) sits in K buffer j%2 and V(j) in V buffer j%2. Step j (j >= 1) loads
     // K(j+STGX) and V(j+STGX-1) into registers, forms S(j), runs O += V(j-1) P(j-1) while it
     // turns S(j) into P(j), and stores at its end K(j+1) and V(j), loaded STGX-1 steps earlier.
@@ -468,143 +479,210 @@ __global__ __launch_bounds__(64 * W, W == 4 ? 2 : 1) void k_bsfa_bf16(const bf16
     // registers. Tile descriptors (k0, lo, hi) run STGX steps ahead of the compute.
     bf16x8 pp[NCC];  // P^T operands of the pending tile
     float mu = -INFINITY, ps = 0.f;
-    int par = 0;     // parity of the current tile
-    int k0c = ts.k0, loc = ts.lo, hic = ts.hi;
-    if (!has) k0c = loc = hic = 0;  // a split stream with no tile stages (unused) key 0
-    auto compute_first = [&]() {
+    auto compute_first = [&](const bf16* Kc, int k0, int lo, int hi) {
       if (wave_active) {
         f32x16 s[SB];
-        qk(Kb(0), s);
-        if (loc > k0c || hic < k0c + KT) mask(s, k0c, loc, hic);
+        qk(Kc, s);
+        if (lo > k0 || hi < k0 + KT) mask(s, k0, lo, hi);
         soft_exact(s, mu, ps, pp);
       }
     };
-    auto compute_step = [&]() {
+    auto compute_step = [&](const bf16* Kc, const bf16* Vp, int k0, int lo, int hi) {
       if (wave_active) {
         rescale(mu);
         l_half += ps;
         f32x16 s[SB];
-        qk(Kb(par), s);
-        if (loc > k0c || hic < k0c + KT) mask(s, k0c, loc, hic);
+        qk(Kc, s);
+        if (lo > k0 || hi < k0 + KT) mask(s, k0, lo, hi);
         bf16x8 pn[NCC];
-        pv_soft(Vb(par ^ 1), pp, s, mu, ps, pn);
+        pv_soft(Vp, pp, s, mu, ps, pn);
 #pragma unroll
         for (int c = 0; c < NCC; ++c) pp[c] = pn[c];
       }
     };
-    if (SPLIT) {
-      // a fixed number of steps for both streams (barriers are shared); a stream past its
-      // last tile only re-reads that tile's keys, unused
-      bool has1 = Ts > 1 && ts.next();
-      int k01 = ts.k0, lo1 = ts.lo, hi1 = ts.hi;
-      Stage sa;  // K(j+1), V(j): loaded at the start of step j, stored at its end
-      load_k(sa, k0c);
-      store_k(sa, Kb(0));
-      __syncthreads();
-      load_k(sa, has1 ? k01 : k0c);
-      load_v(sa, k0c);
-      if (has) compute_first();
-      if (has1) store_k(sa, Kb(1));
-      store_v(sa, Vb(0));
-      for (int j = 1; j < nsteps; ++j) {
-        const bool live = j < Ts;
-        if (live) {
-          k0c = k01; loc = lo1; hic = hi1;
-          has1 = j + 1 < Ts && ts.next();
-          k01 = ts.k0; lo1 = ts.lo; hi1 = ts.hi;
-          par ^= 1;
-        }
-        __syncthreads();
-        load_k(sa, has1 ? k01 : k0c);
-        load_v(sa, k0c);
-        if (live) compute_step();
-        if (has1) store_k(sa, Kb(par ^ 1));
-        if (live) store_v(sa, Vb(par));
-      }
-      __syncthreads();
-      if (has && wave_active) {
-        rescale(mu);
-        l_half += ps;
-        pv(Vb(par), pp);
-      }
-    } else if (has) {
-      int k01 = 0, lo1 = 0, hi1 = 0, k02 = 0;
-      bool has1 = ts.next();
-      k01 = ts.k0; lo1 = ts.lo; hi1 = ts.hi;
-      bool has2 = STGX == 2 && has1 && ts.next();  // STGX 2 only: the tile after next
-      k02 = STGX == 2 ? ts.k0 : 0;
-      if (STGX == 2) {
-        Stage sa, sb;  // sa: K(j+1), V(j) (stored at the end of step j); sb: K(j+2), V(j+1)
-        load_k(sa, k0c);
-        store_k(sa, Kb(0));
-        load_k(sa, has1 ? k01 : k0c);
-        load_v(sa, k0c);
-        __syncthreads();
-        load_k(sb, has2 ? k02 : k0c);
-        load_v(sb, has1 ? k01 : k0c);
-        compute_first();
-        if (has1) store_k(sa, Kb(1));
-        store_v(sa, Vb(0));
-        // step of tile j; `cur` holds K(j+1), V(j) (loaded a step ago), `nxt` receives K(j+2), V(j+1)
-        auto step = [&](Stage& cur, Stage& nxt) {
-          k0c = k01; loc = lo1; hic = hi1;
-          has1 = has2;
-          k01 = k02; lo1 = ts.lo; hi1 = ts.hi;
-          has2 = has2 && ts.next();
-          k02 = ts.k0;
-          par ^= 1;
-          __syncthreads();
-          load_k(nxt, has2 ? k02 : k0c);
-          load_v(nxt, has1 ? k01 : k0c);
-          compute_step();
-          if (has1) store_k(cur, Kb(par ^ 1));
-          store_v(cur, Vb(par));
-        };
-        // whole pairs of steps (stages swap roles twice), then at most one more step
-        while (has1 && has2) {
-          step(sb, sa);
-          step(sa, sb);
-        }
-        if (has1) step(sb, sa);
-      } else {
-        Stage sa;  // K(j+1), V(j): loaded at the start of step j, stored at its end
-        load_k(sa, k0c);
-        store_k(sa, Kb(0));
-        __syncthreads();
-        load_k(sa, has1 ? k01 : k0c);
-        load_v(sa, k0c);
-        compute_first();
-        if (has1) store_k(sa, Kb(1));
-        store_v(sa, Vb(0));
-        while (has1) {
-          k0c = k01; loc = lo1; hic = hi1;
-          has1 = ts.next();
-          k01 = ts.k0; lo1 = ts.lo; hi1 = ts.hi;
-          par ^= 1;
-          __syncthreads();
-          load_k(sa, has1 ? k01 : k0c);
-          load_v(sa, k0c);
-          compute_step();
-          if (has1) store_k(sa, Kb(par ^ 1));
-          store_v(sa, Vb(par));
-        }
-      }
-      // O += V(T-1) P(T-1), V(T-1) in V buffer par
-      __syncthreads();
+    auto last_pv = [&](const bf16* Vp) {  // O += V(T-1) P(T-1)
       if (wave_active) {
         rescale(mu);
         l_half += ps;
-        pv(Vb(par), pp);
+        pv(Vp, pp);
+      }
+    };
+
+    if constexpr (TWO) {
+      // Both key streams step together (the barriers are shared), each wave tracking both:
+      // it stages the tiles of stream ls and computes on those of stream cs. A stream runs
+      // T_s tiles; after its last it only re-reads that tile's keys, unused. Split: stream 0
+      // takes the first half of the chunk's tiles (rounded up), stream 1 the rest.
+      struct Walk {
+        TileWalk<KT> ts;
+        int T, k0, lo, hi, k1, lo1, hi1, par;
+        bool has1;
+        __device__ void start(int skip) {  // first tile (after skipping `skip`), and the next
+          ts.first();
+          if (skip > 0 && T > 0) ts.seek(skip);
+          k0 = T > 0 ? ts.k0 : 0;  // (a stream with no tile stages key 0, unused)
+          lo = T > 0 ? ts.lo : 0;
+          hi = T > 0 ? ts.hi : 0;
+          has1 = T > 1 && ts.next();
+          k1 = ts.k0;
+          lo1 = ts.lo;
+          hi1 = ts.hi;
+          par = 0;
+        }
+        __device__ void step(int j) {  // tile j becomes current (while j < T)
+          if (j < T) {
+            k0 = k1;
+            lo = lo1;
+            hi = hi1;
+            has1 = j + 1 < T && ts.next();
+            k1 = ts.k0;
+            lo1 = ts.lo;
+            hi1 = ts.hi;
+            par ^= 1;
+          }
+        }
+      };
+      Walk w0, w1;
+      w0.ts.runs = runs_s[0];
+      w0.ts.nr = nr;
+      w1.ts.runs = runs_s[BM == 2 ? NS - 1 : 0];
+      w1.ts.nr = BM == 2 ? nr1 : nr;
+      int nsteps;
+      if (BM == 1) {
+        w0.ts.first();
+        const int T = w0.ts.count();  // >= 1: every query group keeps a key group
+        nsteps = (T + 1) / 2;
+        w0.T = nsteps;
+        w1.T = T - nsteps;
+        w0.start(0);
+        w1.start(nsteps);
+      } else {
+        w0.ts.first();
+        w0.T = w0.ts.count();
+        w1.ts.first();
+        w1.T = w1.ts.count();
+        nsteps = max(w0.T, w1.T);
+        w0.start(0);
+        w1.start(0);
+      }
+      // (per-wave selections between the two streams' scalars)
+      auto L_k0 = [&]() { return ls ? w1.k0 : w0.k0; };
+      auto L_next = [&]() { return ls ? (w1.has1 ? w1.k1 : w1.k0) : (w0.has1 ? w0.k1 : w0.k0); };
+      auto L_has1 = [&]() { return ls ? w1.has1 : w0.has1; };
+      auto L_par = [&]() { return ls ? w1.par : w0.par; };
+      auto C_T = [&]() { return cs ? w1.T : w0.T; };
+      Stage sa;  // K(j+1), V(j): loaded at the start of step j, stored at its end
+      load_k(sa, L_k0());
+      store_k(sa, Kb(ls, 0));
+      __syncthreads();
+      load_k(sa, L_next());
+      load_v(sa, L_k0());
+      if (C_T() > 0) compute_first(Kb(cs, 0), cs ? w1.k0 : w0.k0, cs ? w1.lo : w0.lo, cs ? w1.hi : w0.hi);
+      if (L_has1()) store_k(sa, Kb(ls, 1));
+      store_v(sa, Vb(ls, 0));
+      for (int j = 1; j < nsteps; ++j) {
+        w0.step(j);
+        w1.step(j);
+        __syncthreads();
+        load_k(sa, L_next());
+        load_v(sa, L_k0());
+        if (j < C_T()) {
+          const int cp = cs ? w1.par : w0.par;
+          compute_step(Kb(cs, cp), Vb(cs, cp ^ 1), cs ? w1.k0 : w0.k0, cs ? w1.lo : w0.lo, cs ? w1.hi : w0.hi);
+        }
+        if (L_has1()) store_k(sa, Kb(ls, L_par() ^ 1));
+        if (j < (ls ? w1.T : w0.T)) store_v(sa, Vb(ls, L_par()));
+      }
+      __syncthreads();
+      if (C_T() > 0) last_pv(Vb(cs, cs ? w1.par : w0.par));
+    } else {
+      TileWalk<KT> ts;
+      bool has;  // the first tile exists
+      if (MODE != 1) {
+        ts.runs = runs_s[0];
+        ts.nr = nr;
+        has = ts.first();
+      } else {
+        const int clo = a * D.pkc;
+        has = ts.first_single(clo, min(D.N, clo + D.pkc));
+      }
+      int par = 0;  // parity of the current tile
+      int k0c = ts.k0, loc = ts.lo, hic = ts.hi;
+      if (has) {
+        int k01 = 0, lo1 = 0, hi1 = 0, k02 = 0;
+        bool has1 = ts.next();
+        k01 = ts.k0; lo1 = ts.lo; hi1 = ts.hi;
+        bool has2 = STGX == 2 && has1 && ts.next();  // STGX 2 only: the tile after next
+        k02 = STGX == 2 ? ts.k0 : 0;
+        if (STGX == 2) {
+          Stage sa, sb;  // sa: K(j+1), V(j) (stored at the end of step j); sb: K(j+2), V(j+1)
+          load_k(sa, k0c);
+          store_k(sa, Kb(0, 0));
+          load_k(sa, has1 ? k01 : k0c);
+          load_v(sa, k0c);
+          __syncthreads();
+          load_k(sb, has2 ? k02 : k0c);
+          load_v(sb, has1 ? k01 : k0c);
+          compute_first(Kb(0, 0), k0c, loc, hic);
+          if (has1) store_k(sa, Kb(0, 1));
+          store_v(sa, Vb(0, 0));
+          // step of tile j; `cur` holds K(j+1), V(j) (loaded a step ago), `nxt` receives K(j+2), V(j+1)
+          auto step = [&](Stage& cur, Stage& nxt) {
+            k0c = k01; loc = lo1; hic = hi1;
+            has1 = has2;
+            k01 = k02; lo1 = ts.lo; hi1 = ts.hi;
+            has2 = has2 && ts.next();
+            k02 = ts.k0;
+            par ^= 1;
+            __syncthreads();
+            load_k(nxt, has2 ? k02 : k0c);
+            load_v(nxt, has1 ? k01 : k0c);
+            compute_step(Kb(0, par), Vb(0, par ^ 1), k0c, loc, hic);
+            if (has1) store_k(cur, Kb(0, par ^ 1));
+            store_v(cur, Vb(0, par));
+          };
+          // whole pairs of steps (stages swap roles twice), then at most one more step
+          while (has1 && has2) {
+            step(sb, sa);
+            step(sa, sb);
+          }
+          if (has1) step(sb, sa);
+        } else {
+          Stage sa;  // K(j+1), V(j): loaded at the start of step j, stored at its end
+          load_k(sa, k0c);
+          store_k(sa, Kb(0, 0));
+          __syncthreads();
+          load_k(sa, has1 ? k01 : k0c);
+          load_v(sa, k0c);
+          compute_first(Kb(0, 0), k0c, loc, hic);
+          if (has1) store_k(sa, Kb(0, 1));
+          store_v(sa, Vb(0, 0));
+          while (has1) {
+            k0c = k01; loc = lo1; hic = hi1;
+            has1 = ts.next();
+            k01 = ts.k0; lo1 = ts.lo; hi1 = ts.hi;
+            par ^= 1;
+            __syncthreads();
+            load_k(sa, has1 ? k01 : k0c);
+            load_v(sa, k0c);
+            compute_step(Kb(0, par), Vb(0, par ^ 1), k0c, loc, hic);
+            if (has1) store_k(sa, Kb(0, par ^ 1));
+            store_v(sa, Vb(0, par));
+          }
+        }
+        // O += V(T-1) P(T-1), V(T-1) in V buffer par
+        __syncthreads();
+        last_pv(Vb(0, par));
       }
     }
 
-    if (SPLIT) {
+    if constexpr (BM == 1) {
       // stream 1 hands its softmax state (running max, half row sum, unnormalised output)
       // to stream 0 through LDS (the staging buffers are free), lane for lane
       constexpr int NV = 16 * ND + 2;
       float* xs = reinterpret_cast<float*>(smem) + (size_t)sw * NV * kWave + l;
       __syncthreads();  // every wave is past its last operand read
-      if (stream == 1) {
+      if (cs == 1) {
 #pragma unroll
         for (int i = 0; i < ND; ++i)
 #pragma unroll
@@ -613,7 +691,7 @@ __global__ __launch_bounds__(64 * W, W == 4 ? 2 : 1) void k_bsfa_bf16(const bf16
         xs[(16 * ND + 1) * kWave] = l_half;
       }
       __syncthreads();
-      if (stream == 1) return;
+      if (cs == 1) return;
       const float m1 = xs[(16 * ND) * kWave], l1 = xs[(16 * ND + 1) * kWave];
       const float mm = fmaxf(m_run, m1);  // finite: stream 0 has at least one tile
       const float a0 = __builtin_amdgcn_exp2f(m_run - mm), a1 = __builtin_amdgcn_exp2f(m1 - mm);
@@ -675,10 +753,11 @@ __global__ __launch_bounds__(64 * W, W == 4 ? 2 : 1) void k_bsfa_bf16(const bf16
     }
   };
   if constexpr (CAN_SPLIT) {
-    if (rows <= QT / 2) body(std::true_type{});
-    else body(std::false_type{});
+    if (kind >= 0) body(std::integral_constant<int, 2>{});
+    else if (kind == -2) body(std::integral_constant<int, 1>{});
+    else body(std::integral_constant<int, 0>{});
   } else {
-    body(std::false_type{});
+    body(std::integral_constant<int, 0>{});
   }
 }
 
@@ -822,6 +901,7 @@ void launch_attend_sparse(const void* q, const Dims& D, const Bufs& B, void* o_s
   if (D.dtype == 1) {
     const int nb = D.BH * D.max_atiles;
     const bf16* qb = (const bf16*)q;
+    if (!dense && D.attn_w == 8) launch_pair_tiles(D, B, s);
     if (D.d == 128) {
       if (dense) launch_bsfa<128, 2>(D, B, qb, o_sparse, o_psp, nb, s);
       else launch_bsfa<128, 0>(D, B, qb, o_sparse, o_psp, nb, s);

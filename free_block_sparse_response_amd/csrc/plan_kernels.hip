@@ -1792,6 +1792,76 @@ __global__ __launch_bounds__(1024) void k_route_emit(Dims D, Bufs B) {
   if (st) runs[rs].x = ko[tid];
   if (en) runs[rs + (st ? 1 : 0) - 1].y = ko[tid + 1];
   if (tid == 0) B.nruns[(size_t)bh * D.Cq + a] = nr;
+  // the attention kernel's key tiles over these runs (each run from its start rounded down to
+  // 8 keys), for the pairing of its work items
+  __syncthreads();
+  int t = 0;
+  if (en) {
+    const int2 rv = runs[rs + (st ? 1 : 0) - 1];
+    t = (rv.y - (rv.x & ~7) + kKeyTile - 1) / kKeyTile;
+  }
+  const int tt = block_sum<1024, int>(t, ws);
+  if (tid == 0) B.gtiles[(size_t)bh * D.Cq + a] = tt;
+}
+
+// Work items of the 8-wave attention kernel, per head (one thread per query group). A group's
+// rows go in chunks of 256; a full chunk is one item on all 8 waves. The last chunk, of
+// w = ceil(r / 32) < 8 waves, runs on its own: all waves on its keys when w >= 5 (T_g steps,
+// 8 - w waves idle), the two wave halves on half the keys each when w <= 4 (T_g / 2 steps).
+// A last chunk of w <= 3 waves and one of 8 - w waves (buckets in group order, rank for rank)
+// instead share one item, each on its own waves and key stream (max(T_g, T_h) steps), unless
+// the small chunk has more than twice the other's key tiles (then apart is no slower).
+__global__ __launch_bounds__(1024) void k_pair_tiles(Dims D, Bufs B) {
+  __shared__ int slot[8][kMaxGroups];  // bucket w: rank -> group
+  __shared__ int taken[kMaxGroups];    // the group's last chunk shares an item it does not own
+  __shared__ int ws[16];
+  const int bh = blockIdx.x, g = threadIdx.x;
+  const int Cq = B.qst[bh].c_final;
+  const int* qo = B.qoff + (size_t)bh * (D.Cq + 1);
+  const int* gt = B.gtiles + (size_t)bh * D.Cq;
+  auto last_chunk = [&](int x, int& pos, int& w) {  // first row and waves of group x's last chunk
+    const int n = qo[x + 1] - qo[x], c = (n + 255) / 256;
+    pos = qo[x] + 256 * (c - 1);
+    w = (n - 256 * (c - 1) + 31) / 32;
+    return c;
+  };
+  int pos = 0, w = 8, c = 0;
+  if (g < Cq) c = last_chunk(g, pos, w);  // (groups are non-empty)
+  const bool rem = c > 0 && w < 8;
+  __shared__ int cnt[8];  // chunks per bucket
+  int rank = 0;
+  for (int b = 1; b < 8; ++b) {
+    int tot;
+    const int rk = block_excl_scan<1024, int>(rem && w == b ? 1 : 0, &tot, ws);
+    if (rem && w == b) rank = rk;
+    if (g == 0) cnt[b] = tot;
+  }
+  taken[g] = 0;
+  if (rem) slot[w][rank] = g;
+  __syncthreads();
+  int partner = -1;
+  if (rem && w <= 3 && rank < cnt[8 - w]) {
+    partner = slot[8 - w][rank];
+    if (gt[g] > 2 * gt[partner]) partner = -1;
+    else taken[partner] = 1;
+  }
+  __syncthreads();
+  const bool own = rem && !taken[g];  // the last chunk's item is written by this group
+  const int items = (c > 0 ? c - 1 : 0) + (c > 0 && w == 8 ? 1 : 0) + (own ? 1 : 0);
+  int tot;
+  int o = block_excl_scan<1024, int>(items, &tot, ws);
+  int4* pt = B.ptiles + (size_t)bh * D.max_atiles;
+  if (g == 0) B.nptiles[bh] = tot;
+  for (int k = 0; k < c - 1 + (w == 8 ? 1 : 0); ++k) pt[o++] = make_int4(g, qo[g] + 256 * k, -1, 0);
+  if (own) {
+    if (partner >= 0) {
+      int ph, wh;
+      last_chunk(partner, ph, wh);
+      pt[o] = make_int4(partner, ph, g, pos);  // stream 0: the larger chunk
+    } else {
+      pt[o] = make_int4(g, pos, w <= 4 ? -2 : -1, 0);
+    }
+  }
 }
 
 // =====================================================================================
@@ -1937,6 +2007,7 @@ __global__ void k_identity_plan(Dims D, Bufs B) {
     B.cols[(size_t)bh * D.Cq * D.Ck] = 0;
     B.runs[(size_t)bh * D.Cq * D.Ck] = make_int2(0, D.N);
     B.nruns[(size_t)bh * D.Cq] = 1;
+    B.gtiles[(size_t)bh * D.Cq] = (D.N + kKeyTile - 1) / kKeyTile;
     B.qst[bh].c_final = 1;
     B.kst[bh].c_final = 1;
   }
@@ -2294,6 +2365,10 @@ void launch_residual_projector(const Dims& D, const Bufs& B, hipStream_t s) {
 
 void launch_fill_i32(int* p, long long n, int v, hipStream_t s) {
   hipLaunchKernelGGL(k_fill_i32, dim3(64), dim3(256), 0, s, p, n, v);
+}
+
+void launch_pair_tiles(const Dims& D, const Bufs& B, hipStream_t s) {
+  hipLaunchKernelGGL(k_pair_tiles, dim3(D.BH), dim3(1024), 0, s, D, B);
 }
 
 void launch_identity_plan(const Dims& D, const Bufs& B, hipStream_t s) {

@@ -114,6 +114,11 @@ struct Bufs {
   int* ntiles;       // [BH]
   int2* atiles;      // [BH][max_atiles] (query group, first position), attention tiles
   int* antiles;      // [BH]
+  int4* ptiles;      // [BH][max_atiles] 8-wave attention items: (group, first position) of stream 0,
+                     // then (group, first position) of stream 1, or (-1, 0): one chunk on all
+                     // waves, or (-2, 0): one chunk whose keys the two wave halves split
+  int* nptiles;      // [BH]
+  int* gtiles;       // [BH][Cq] key tiles (kKeyTile keys each) over a query group's key runs
   int* tstart;       // [BH][Cq+1] first tile of each query group
   float* mass_part;  // [BH][max_tiles][Ck] per-tile column sums of the group masses
   float* pp_o;       // [BH][M][pch][d] probe attention partial outputs (unnormalised)

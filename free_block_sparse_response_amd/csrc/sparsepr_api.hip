@@ -128,6 +128,9 @@ Bufs carve(const Dims& D, void* base, size_t* total) {
   B.ntiles = c.take<int>(BH);
   B.atiles = c.take<int2>(BH * D.max_tiles);  // max_atiles <= max_tiles for either tile height
   B.antiles = c.take<int>(BH);
+  B.ptiles = c.take<int4>(BH * D.max_tiles);
+  B.nptiles = c.take<int>(BH);
+  B.gtiles = c.take<int>(BH * D.Cq);
   B.tstart = c.take<int>(BH * (D.Cq + 1));
   B.mass_part = c.take<float>(BH * D.max_tiles * D.Ck);
   B.pp_o = c.take<float>(BH * D.M * D.pch * d);
