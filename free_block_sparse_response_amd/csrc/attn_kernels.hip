@@ -922,10 +922,9 @@ void launch_attend_probes(const void* q, const Dims& D, const Bufs& B, float* o_
   if (D.M == 0 || !o_pdn) return;
   float* none = nullptr;
   if (D.dtype == 1) {
-    // probe rows in 128-row tiles (4 waves), each over one key chunk
-    Dims Dp = D;
-    Dp.attn_w = 4;
-    const int nbk = D.BH * ((D.M + kAttnQT - 1) / kAttnQT) * D.pch;
+    // probe rows in tiles of the attention tiles' height, each over one key chunk
+    const int nbk = D.BH * ((D.M + 32 * D.attn_w - 1) / (32 * D.attn_w)) * D.pch;
+    const Dims& Dp = D;
     if (D.d == 128) {
       launch_bsfa<128, 1>(Dp, B, (const bf16*)q, (void*)o_pdn, none, nbk, s);
       hipLaunchKernelGGL((k_probe_combine<128>), dim3(D.M, D.BH), dim3(128), 0, s, D, B, o_pdn);

@@ -230,7 +230,8 @@ sparsepr_status sparsepr_plan_create(const sparsepr_config* cfg, sparsepr_plan_t
   D.max_atiles = (N + 32 * D.attn_w - 1) / (32 * D.attn_w) + D.Cq;
   {
     // split the probe rows' keys so that about 1024 workgroups share the probe attention
-    const int ptiles = (D.M + spr::kAttnQT - 1) / spr::kAttnQT;
+    // (probe tiles have the attention tiles' height)
+    const int ptiles = (D.M + 32 * D.attn_w - 1) / (32 * D.attn_w);
     const long long want = ptiles > 0 ? (1024 + (long long)D.BH * ptiles - 1) / ((long long)D.BH * ptiles) : 1;
     const int maxch = (N + 511) / 512;
     int pch = (int)(want < 1 ? 1 : (want > maxch ? maxch : want));
