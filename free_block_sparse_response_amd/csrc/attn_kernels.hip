@@ -2,12 +2,13 @@
 // the exact attention of the probe rows (paper "Partition the Support, Reconstruct the
 // Residual", abstract; project website, Method section, stage 03 and the PFRR panel).
 //
-// Query rows of one query group are taken 128 at a time (one tile); the keys are the
-// union of the selected key groups, which the permutation made contiguous per group, so
-// consecutive selected groups merge into one key run. Softmax is renormalised over the
-// retained keys only (online softmax across key tiles).
+// Query rows of one query group are taken 128 or 256 at a time (a tile of 4 or 8 waves,
+// 32 rows each; the 8-wave kernel also runs two chunks of rows on separate key streams, see
+// below); the keys are the union of the selected key groups, which the permutation made
+// contiguous per group, so consecutive selected groups merge into one key run. Softmax is
+// renormalised over the retained keys only (online softmax across key tiles).
 //
-// bf16 path, per workgroup of 4 waves (32 query rows each):
+// bf16 path, per wave of 32 query rows:
 //   S^T = K Q^T   with v_mfma_f32_32x32x16_bf16: A = K tile rows from LDS, B = Q^T kept in
 //                 registers; each lane then holds the scores of ONE query (lane % 32) for 16
 //                 keys, so the row max / sum are in-lane plus one cross-half exchange.
@@ -120,8 +121,9 @@ struct TileWalk {
 
 // -------------------------------------------------------------------------------------
 // bf16 MFMA kernel, W waves of 32 query rows per workgroup (a tile of up to 32 W rows of one
-// query group), KT keys per step (a multiple of 32). MODE 0: block-sparse tiles from the
-// attention tile table, bf16 output in token order (plus float rows for probes). MODE 1:
+// query group), KT keys per step (a multiple of 32). MODE 0: block-sparse work items from the
+// attention tile table (4 waves) or the paired item table (8 waves), bf16 output in token
+// order (plus float rows for probes). MODE 1:
 // probe rows (32 W per block) over one chunk of all keys, partial outputs for the chunk
 // combine. MODE 2: the same code as MODE 0 under its own symbol, used by the dense
 // reference call so that traces keep the two apart.
