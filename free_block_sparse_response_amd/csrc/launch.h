@@ -13,7 +13,7 @@ void launch_route_probes(const Dims& D, const Bufs& B, hipStream_t s);
 void launch_identity_plan(const Dims& D, const Bufs& B, hipStream_t s);
 void launch_pair_tiles(const Dims& D, const Bufs& B, hipStream_t s);
 void launch_set_probes(const Dims& D, const Bufs& B, const int* probes, const float* weights, hipStream_t s);
-void launch_permute_kv(const void* k, const void* v, const Dims& D, const Bufs& B, hipStream_t s);
+void launch_permute_kv(const void* k, const void* v, const Dims& D, const Bufs& B, const int* perm, hipStream_t s);
 void launch_attend_sparse(const void* q, const Dims& D, const Bufs& B, void* o_sparse, float* o_probe_sparse,
                           hipStream_t s, bool dense = false);
 void launch_attend_probes(const void* q, const Dims& D, const Bufs& B, float* o_probe_dense, hipStream_t s);

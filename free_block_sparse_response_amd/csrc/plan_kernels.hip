@@ -1804,6 +1804,87 @@ __global__ __launch_bounds__(1024) void k_route_emit(Dims D, Bufs B) {
   if (tid == 0) B.gtiles[(size_t)bh * D.Cq + a] = tt;
 }
 
+// The bf16 attention's key order (per head): key groups ranked by the number of query groups
+// that select them, most first, ties to the lower index; the start of each rank's keys.
+__global__ __launch_bounds__(1024) void k_key_order(Dims D, Bufs B) {
+  __shared__ int cnt[kMaxGroups];
+  __shared__ int sz[kMaxGroups];
+  __shared__ int ws[16];
+  const int bh = blockIdx.x, b = threadIdx.x;
+  const int Ck = B.kst[bh].c_final, Cq = B.qst[bh].c_final;
+  cnt[b] = 0;
+  sz[b] = 0;
+  __syncthreads();
+  const int* rp = B.row_ptr + (size_t)bh * (D.Cq + 1);
+  const int* cols = B.cols + (size_t)bh * D.Cq * D.Ck;
+  const int tot = rp[Cq];
+  for (int e = b; e < tot; e += 1024) atomicAdd(&cnt[cols[e]], 1);
+  __syncthreads();
+  const int* ko = B.koff + (size_t)bh * (D.Ck + 1);
+  if (b < Ck) {
+    const int cb = cnt[b];
+    int rank = 0;
+    for (int x = 0; x < Ck; ++x) {
+      const int cx = cnt[x];
+      rank += (cx > cb || (cx == cb && x < b)) ? 1 : 0;
+    }
+    B.katt_rank[(size_t)bh * D.Ck + b] = rank;
+    sz[rank] = ko[b + 1] - ko[b];
+  }
+  __syncthreads();
+  int total;
+  const int st = block_excl_scan<1024, int>(b < Ck ? sz[b] : 0, &total, ws);
+  int* ks = B.katt_start + (size_t)bh * (D.Ck + 1);
+  if (b < Ck) ks[b] = st;
+  if (b == 0) ks[Ck] = total;
+}
+
+// Key runs of one query group in the attention order (maximal stretches of consecutive
+// ranks among its selected key groups), and their key tiles.
+__global__ __launch_bounds__(1024) void k_att_runs(Dims D, Bufs B) {
+  __shared__ int flag[kMaxGroups];
+  __shared__ int ws[16];
+  const int a = blockIdx.x, bh = blockIdx.y;
+  const int Cq = B.qst[bh].c_final, Ck = B.kst[bh].c_final;
+  if (a >= Cq) return;
+  const int tid = threadIdx.x;
+  flag[tid] = 0;
+  __syncthreads();
+  const int* rpa = B.row_ptr + (size_t)bh * (D.Cq + 1);
+  const int rp = rpa[a], j = rpa[a + 1] - rp;
+  if (tid < j) flag[B.katt_rank[(size_t)bh * D.Ck + B.cols[(size_t)bh * D.Cq * D.Ck + rp + tid]]] = 1;
+  __syncthreads();
+  const bool f = tid < Ck && flag[tid];
+  const bool st = f && (tid == 0 || !flag[tid - 1]);
+  const bool en = f && (tid + 1 == Ck || !flag[tid + 1]);
+  int nr;
+  const int rs = block_excl_scan_bool<1024>(st, &nr, ws);
+  const int* ks = B.katt_start + (size_t)bh * (D.Ck + 1);
+  int2* runs = B.runs + (size_t)bh * D.Cq * D.Ck + rp;
+  if (st) runs[rs].x = ks[tid];
+  if (en) runs[rs + (st ? 1 : 0) - 1].y = ks[tid + 1];
+  if (tid == 0) B.nruns[(size_t)bh * D.Cq + a] = nr;
+  __syncthreads();
+  int t = 0;
+  if (en) {
+    const int2 rv = runs[rs + (st ? 1 : 0) - 1];
+    t = (rv.y - (rv.x & ~7) + kKeyTile - 1) / kKeyTile;
+  }
+  const int tt = block_sum<1024, int>(t, ws);
+  if (tid == 0) B.gtiles[(size_t)bh * D.Cq + a] = tt;
+}
+
+// Key rows in the attention order: group b's rows (plan order) moved to its rank's start.
+__global__ __launch_bounds__(256) void k_att_perm(Dims D, Bufs B) {
+  const int b = blockIdx.x, bh = blockIdx.y;
+  if (b >= B.kst[bh].c_final) return;
+  const int* ko = B.koff + (size_t)bh * (D.Ck + 1);
+  const int lo = ko[b], n = ko[b + 1] - lo;
+  const int dst = B.katt_start[(size_t)bh * (D.Ck + 1) + B.katt_rank[(size_t)bh * D.Ck + b]];
+  for (int i = threadIdx.x; i < n; i += 256)
+    B.kperm_att[(size_t)bh * D.N + dst + i] = B.kperm[(size_t)bh * D.N + lo + i];
+}
+
 // Work items of the 8-wave attention kernel, per head (one thread per query group). A group's
 // rows go in chunks of 256; a full chunk is one item on all 8 waves. The last chunk, of
 // w = ceil(r / 32) < 8 waves, runs on its own: all waves on its keys when w >= 5 (T_g steps,
@@ -2334,6 +2415,14 @@ void launch_route_probes(const Dims& D, const Bufs& B, hipStream_t s) {
   hipLaunchKernelGGL(k_route_sort, dim3(D.Cq, D.BH), dim3(1024), 0, s, D, B);
   hipLaunchKernelGGL(k_route_tau, dim3(D.BH), dim3(1024), 0, s, D, B);
   hipLaunchKernelGGL(k_route_emit, dim3(D.Cq, D.BH), dim3(1024), 0, s, D, B);
+  if (D.dtype == 1 && D.attn_w == 8) {
+    // the 8-wave attention's key order and its runs (on small calls, whose 4-wave tiles are
+    // short, the three launches cost more than the shorter runs save; the fp32 kernel reads
+    // the route itself)
+    hipLaunchKernelGGL(k_key_order, dim3(D.BH), dim3(1024), 0, s, D, B);
+    hipLaunchKernelGGL(k_att_runs, dim3(D.Cq, D.BH), dim3(1024), 0, s, D, B);
+    hipLaunchKernelGGL(k_att_perm, dim3(D.Ck, D.BH), dim3(256), 0, s, D, B);
+  }
   hipLaunchKernelGGL(k_fill_i32, dim3(256), dim3(256), 0, s, B.pslot, (long long)D.BH * D.N, -1);
   if (D.M > 0 && D.probe_sel == 0) {
     hipLaunchKernelGGL(k_probe_alloc, dim3(D.BH), dim3(1024), 0, s, D, B);
@@ -2344,13 +2433,13 @@ void launch_route_probes(const Dims& D, const Bufs& B, hipStream_t s) {
 }
 
 template <typename T, int DD>
-static void permute_impl(const void* k, const void* v, const Dims& D, const Bufs& B, hipStream_t s) {
+static void permute_impl(const void* k, const void* v, const Dims& D, const Bufs& B, const int* perm, hipStream_t s) {
   hipLaunchKernelGGL((k_permute_kv<T, DD>), dim3(D.Npad / 64, D.BH), dim3(256), 0, s, (const T*)k, (const T*)v,
-                     B.kperm, D.N, D.Npad, (T*)B.kp, (T*)B.vpt);
+                     perm, D.N, D.Npad, (T*)B.kp, (T*)B.vpt);
 }
 
-void launch_permute_kv(const void* k, const void* v, const Dims& D, const Bufs& B, hipStream_t s) {
-  SPR_DISPATCH(D.dtype, D.d, permute_impl, k, v, D, B, s);
+void launch_permute_kv(const void* k, const void* v, const Dims& D, const Bufs& B, const int* perm, hipStream_t s) {
+  SPR_DISPATCH(D.dtype, D.d, permute_impl, k, v, D, B, perm, s);
 }
 
 void launch_residual_projector(const Dims& D, const Bufs& B, hipStream_t s) {

@@ -119,6 +119,12 @@ struct Bufs {
                      // waves, or (-2, 0): one chunk whose keys the two wave halves split
   int* nptiles;      // [BH]
   int* gtiles;       // [BH][Cq] key tiles (kKeyTile keys each) over a query group's key runs
+  // 8-wave (bf16) attention layout of the keys: key groups by how many query groups select
+  // them (most first, ties by index), so that groups selected together sit together and the
+  // runs are fewer and longer; the plan's own key order (kperm, koff) is unchanged
+  int* katt_rank;    // [BH][Ck]   position of key group b in that order
+  int* katt_start;   // [BH][Ck+1] first key of the group at each position
+  int* kperm_att;    // [BH][N]    key rows in that order (the permuted K and V follow it)
   int* tstart;       // [BH][Cq+1] first tile of each query group
   float* mass_part;  // [BH][max_tiles][Ck] per-tile column sums of the group masses
   float* pp_o;       // [BH][M][pch][d] probe attention partial outputs (unnormalised)

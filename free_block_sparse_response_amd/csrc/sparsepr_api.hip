@@ -131,6 +131,9 @@ Bufs carve(const Dims& D, void* base, size_t* total) {
   B.ptiles = c.take<int4>(BH * D.max_tiles);
   B.nptiles = c.take<int>(BH);
   B.gtiles = c.take<int>(BH * D.Cq);
+  B.katt_rank = c.take<int>(BH * D.Ck);
+  B.katt_start = c.take<int>(BH * (D.Ck + 1));
+  B.kperm_att = c.take<int>(BH * N);
   B.tstart = c.take<int>(BH * (D.Cq + 1));
   B.mass_part = c.take<float>(BH * D.max_tiles * D.Ck);
   B.pp_o = c.take<float>(BH * D.M * D.pch * d);
@@ -432,7 +435,7 @@ sparsepr_status sparsepr_attend(sparsepr_plan_t p, const void* q, const void* k,
   Bufs B = carve(p->D, p->ws, nullptr);
   {
     StageTimer t(p, SPARSEPR_STAGE_PERMUTE, s);
-    spr::launch_permute_kv(k, v, p->D, B, s);
+    spr::launch_permute_kv(k, v, p->D, B, p->D.dtype == 1 && p->D.attn_w == 8 ? B.kperm_att : B.kperm, s);
   }
   {
     StageTimer t(p, SPARSEPR_STAGE_SPARSE, s);
@@ -483,7 +486,7 @@ sparsepr_status sparsepr_dense_attention(sparsepr_plan_t p, const void* q, const
   Dd.attn_w = 8;
   Dd.max_atiles = (Dd.N + 255) / 256 + Dd.Cq;
   spr::launch_identity_plan(Dd, B, s);
-  spr::launch_permute_kv(k, v, Dd, B, s);
+  spr::launch_permute_kv(k, v, Dd, B, B.kperm, s);
   spr::launch_attend_sparse(q, Dd, B, out, nullptr, s, true);
   return hip_status();
 }
