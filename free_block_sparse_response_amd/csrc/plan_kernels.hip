@@ -1169,7 +1169,7 @@ __device__ inline f32x16 mfma_cols(const bf16* Yh, const bf16* Yl, int y0, const
 template <int DD, int RS, bool LO>
 __global__ __launch_bounds__(256, RS == 1 ? 4 : 2) void k_km_assign_bf16(const bf16* x, Dims D, Bufs B, int C,
                                                                            KmState* st, int t) {
-  constexpr int CB = 64, KS = DD + 8, NB = kKmRows * RS;
+  constexpr int CB = 64, KS = DD + 8;
   constexpr int NL = CB * DD / 8 / 256;  // 16-byte loads per thread per chunk and operand
   constexpr int NO = LO ? 2 : 1;
   // the centroid operands; after the last chunk the same bytes hold the per-wave label counts
