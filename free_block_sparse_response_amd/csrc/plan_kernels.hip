@@ -1656,39 +1656,66 @@ __global__ __launch_bounds__(256) void k_group_mass(const T* q, Dims D, Bufs B) 
 // picks the shortest reaching prefix (at least one group) per row; tau* is the largest
 // tau whose total pair cost fits floor(rho N^2) - M N.
 // =====================================================================================
-__global__ __launch_bounds__(1024) void k_route_sort(Dims D, Bufs B) {
+__global__ __launch_bounds__(256) void k_route_sort(Dims D, Bufs B) {
   __shared__ unsigned long long key[kMaxGroups];
-  __shared__ long long ws[16];
+  __shared__ long long ws[4];
   const int a = blockIdx.x, bh = blockIdx.y;
   const int Cq = B.qst[bh].c_final, Ck = B.kst[bh].c_final;
   if (a >= Cq) return;
   const int tid = threadIdx.x;
   const long long* u = B.u + ((size_t)bh * D.Cq + a) * D.Ck;
-  // order by (-u, b): each key group's rank is the number of keys below its own (distinct
-  // keys: the group id is in the low bits); every thread reads the same key at a time
-  __shared__ int order[kMaxGroups];
-  key[tid] = tid < Ck ? ((((1ull << 34) - 1ull - (unsigned long long)u[tid]) << 10) | (unsigned)tid) : ~0ull;
+  // order by (-u, b): the keys (distinct: the group id is in the low bits) sorted ascending by
+  // a bitonic network over the next power of two at or above C_k (padding keys sort last)
+  int n = 1;
+  while (n < Ck) n <<= 1;
+  for (int i = tid; i < n; i += 256)
+    key[i] = i < Ck ? ((((1ull << 34) - 1ull - (unsigned long long)u[i]) << 10) | (unsigned)i) : ~0ull;
+  for (int k = 2; k <= n; k <<= 1)
+    for (int j = k >> 1; j > 0; j >>= 1) {
+      __syncthreads();
+      for (int i = tid; i < n; i += 256) {
+        const int l = i ^ j;
+        if (l > i) {
+          const unsigned long long x = key[i], y = key[l];
+          if ((x > y) == ((i & k) == 0)) {
+            key[i] = y;
+            key[l] = x;
+          }
+        }
+      }
+    }
   __syncthreads();
-  if (tid < Ck) {
-    const unsigned long long kv = key[tid];
-    int rank = 0;
-    for (int j = 0; j < Ck; ++j) rank += key[j] < kv;
-    order[rank] = tid;
-  }
-  __syncthreads();
+  // thread t takes sorted positions 4t .. 4t + 3: group, mass and key count, then the prefix
+  // sums of mass and cost in that order
   const int* ko = B.koff + (size_t)bh * (D.Ck + 1);
-  const int b = tid < Ck ? order[tid] : 0;
-  const long long mass = tid < Ck ? u[b] : 0;
-  const long long nk = tid < Ck ? (long long)(ko[b + 1] - ko[b]) : 0;
+  const int* qo = B.qoff + (size_t)bh * (D.Cq + 1);
+  const long long nq = qo[a + 1] - qo[a];
+  int bq[4];
+  long long mq[4], kq[4], sm = 0, sk = 0;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int p = 4 * tid + q;
+    const bool v = p < Ck;
+    bq[q] = v ? (int)(key[p] & 1023ull) : 0;
+    mq[q] = v ? u[bq[q]] : 0;
+    kq[q] = v ? (long long)(ko[bq[q] + 1] - ko[bq[q]]) : 0;
+    sm += mq[q];
+    sk += kq[q];
+  }
   long long t1, t2;
-  const long long cm = block_excl_scan<1024, long long>(mass, &t1, ws) + mass;
-  const long long cn = block_excl_scan<1024, long long>(nk, &t2, ws) + nk;
-  if (tid < Ck) {
-    const size_t o = ((size_t)bh * D.Cq + a) * D.Ck + tid;
-    const int* qo = B.qoff + (size_t)bh * (D.Cq + 1);
-    B.sorted_b[o] = b;
-    B.cum[o] = cm;
-    B.ccost[o] = (long long)(qo[a + 1] - qo[a]) * cn;
+  long long cm = block_excl_scan<256, long long>(sm, &t1, ws);
+  long long cn = block_excl_scan<256, long long>(sk, &t2, ws);
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int p = 4 * tid + q;
+    cm += mq[q];
+    cn += kq[q];
+    if (p < Ck) {
+      const size_t o = ((size_t)bh * D.Cq + a) * D.Ck + p;
+      B.sorted_b[o] = bq[q];
+      B.cum[o] = cm;
+      B.ccost[o] = nq * cn;
+    }
   }
 }
 
@@ -1764,43 +1791,57 @@ __global__ __launch_bounds__(1024) void k_route_tau(Dims D, Bufs B) {
 }
 
 // Selected key groups of one query group, in ascending key-group order.
-__global__ __launch_bounds__(1024) void k_route_emit(Dims D, Bufs B) {
+__global__ __launch_bounds__(256) void k_route_emit(Dims D, Bufs B) {
   __shared__ int flag[kMaxGroups];
-  __shared__ int ws[16];
+  __shared__ int ws[4];
   const int a = blockIdx.x, bh = blockIdx.y;
   const int Cq = B.qst[bh].c_final, Ck = B.kst[bh].c_final;
   if (a >= Cq) return;
   const int tid = threadIdx.x;
-  flag[tid] = 0;
+  for (int i = tid; i < kMaxGroups; i += 256) flag[i] = 0;
   __syncthreads();
   const int j = B.jsel[(size_t)bh * D.Cq + a];
-  if (tid < j) flag[B.sorted_b[((size_t)bh * D.Cq + a) * D.Ck + tid]] = 1;
+  for (int i = tid; i < j; i += 256) flag[B.sorted_b[((size_t)bh * D.Cq + a) * D.Ck + i]] = 1;
   __syncthreads();
-  int tot;
-  const bool f = tid < Ck && flag[tid];
-  const int pos = block_excl_scan_bool<1024>(f, &tot, ws);
+  // thread t takes key groups 4t .. 4t + 3: selected, and first / last of a run of
+  // consecutive selected groups (whose keys are contiguous after the permutation)
+  bool f[4], st[4], en[4];
+  int ns = 0, nst = 0;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int g = 4 * tid + q;
+    f[q] = g < Ck && flag[g];
+    st[q] = f[q] && (g == 0 || !flag[g - 1]);
+    en[q] = f[q] && (g + 1 == Ck || !flag[g + 1]);
+    ns += f[q] ? 1 : 0;
+    nst += st[q] ? 1 : 0;
+  }
+  int tot, nr;
+  int pos = block_excl_scan<256, int>(ns, &tot, ws);
+  int rs = block_excl_scan<256, int>(nst, &nr, ws);
   const int rp = B.row_ptr[(size_t)bh * (D.Cq + 1) + a];
-  if (f) B.cols[(size_t)bh * D.Cq * D.Ck + rp + pos] = tid;
-  // key runs: maximal stretches of consecutive selected groups, whose keys are contiguous
-  // after the permutation, as [koff[first], koff[last + 1])
-  const bool st = f && (tid == 0 || !flag[tid - 1]);
-  const bool en = f && (tid + 1 == Ck || !flag[tid + 1]);
-  int nr;
-  const int rs = block_excl_scan_bool<1024>(st, &nr, ws);
   const int* ko = B.koff + (size_t)bh * (D.Ck + 1);
   int2* runs = B.runs + (size_t)bh * D.Cq * D.Ck + rp;
-  if (st) runs[rs].x = ko[tid];
-  if (en) runs[rs + (st ? 1 : 0) - 1].y = ko[tid + 1];
+  int* cols = B.cols + (size_t)bh * D.Cq * D.Ck + rp;
+  // key runs [koff[first], koff[last + 1])
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int g = 4 * tid + q;
+    if (f[q]) cols[pos++] = g;
+    if (st[q]) runs[rs].x = ko[g];
+    if (en[q]) runs[rs + (st[q] ? 1 : 0) - 1].y = ko[g + 1];
+    rs += st[q] ? 1 : 0;
+  }
   if (tid == 0) B.nruns[(size_t)bh * D.Cq + a] = nr;
   // the attention kernel's key tiles over these runs (each run from its start rounded down to
   // 8 keys), for the pairing of its work items
   __syncthreads();
   int t = 0;
-  if (en) {
-    const int2 rv = runs[rs + (st ? 1 : 0) - 1];
-    t = (rv.y - (rv.x & ~7) + kKeyTile - 1) / kKeyTile;
+  for (int r = tid; r < nr; r += 256) {
+    const int2 rv = runs[r];
+    t += (rv.y - (rv.x & ~7) + kKeyTile - 1) / kKeyTile;
   }
-  const int tt = block_sum<1024, int>(t, ws);
+  const int tt = block_sum<256, int>(t, ws);
   if (tid == 0) B.gtiles[(size_t)bh * D.Cq + a] = tt;
 }
 
@@ -1841,36 +1882,50 @@ __global__ __launch_bounds__(1024) void k_key_order(Dims D, Bufs B) {
 
 // Key runs of one query group in the attention order (maximal stretches of consecutive
 // ranks among its selected key groups), and their key tiles.
-__global__ __launch_bounds__(1024) void k_att_runs(Dims D, Bufs B) {
+__global__ __launch_bounds__(256) void k_att_runs(Dims D, Bufs B) {
   __shared__ int flag[kMaxGroups];
-  __shared__ int ws[16];
+  __shared__ int ws[4];
   const int a = blockIdx.x, bh = blockIdx.y;
   const int Cq = B.qst[bh].c_final, Ck = B.kst[bh].c_final;
   if (a >= Cq) return;
   const int tid = threadIdx.x;
-  flag[tid] = 0;
+  for (int i = tid; i < kMaxGroups; i += 256) flag[i] = 0;
   __syncthreads();
   const int* rpa = B.row_ptr + (size_t)bh * (D.Cq + 1);
   const int rp = rpa[a], j = rpa[a + 1] - rp;
-  if (tid < j) flag[B.katt_rank[(size_t)bh * D.Ck + B.cols[(size_t)bh * D.Cq * D.Ck + rp + tid]]] = 1;
+  const int* rank = B.katt_rank + (size_t)bh * D.Ck;
+  for (int i = tid; i < j; i += 256) flag[rank[B.cols[(size_t)bh * D.Cq * D.Ck + rp + i]]] = 1;
   __syncthreads();
-  const bool f = tid < Ck && flag[tid];
-  const bool st = f && (tid == 0 || !flag[tid - 1]);
-  const bool en = f && (tid + 1 == Ck || !flag[tid + 1]);
+  // thread t takes positions 4t .. 4t + 3 of the order
+  bool st[4], en[4];
+  int nst = 0;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int r = 4 * tid + q;
+    const bool f = r < Ck && flag[r];
+    st[q] = f && (r == 0 || !flag[r - 1]);
+    en[q] = f && (r + 1 == Ck || !flag[r + 1]);
+    nst += st[q] ? 1 : 0;
+  }
   int nr;
-  const int rs = block_excl_scan_bool<1024>(st, &nr, ws);
+  int rs = block_excl_scan<256, int>(nst, &nr, ws);
   const int* ks = B.katt_start + (size_t)bh * (D.Ck + 1);
   int2* runs = B.runs + (size_t)bh * D.Cq * D.Ck + rp;
-  if (st) runs[rs].x = ks[tid];
-  if (en) runs[rs + (st ? 1 : 0) - 1].y = ks[tid + 1];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int r = 4 * tid + q;
+    if (st[q]) runs[rs].x = ks[r];
+    if (en[q]) runs[rs + (st[q] ? 1 : 0) - 1].y = ks[r + 1];
+    rs += st[q] ? 1 : 0;
+  }
   if (tid == 0) B.nruns[(size_t)bh * D.Cq + a] = nr;
   __syncthreads();
   int t = 0;
-  if (en) {
-    const int2 rv = runs[rs + (st ? 1 : 0) - 1];
-    t = (rv.y - (rv.x & ~7) + kKeyTile - 1) / kKeyTile;
+  for (int r = tid; r < nr; r += 256) {
+    const int2 rv = runs[r];
+    t += (rv.y - (rv.x & ~7) + kKeyTile - 1) / kKeyTile;
   }
-  const int tt = block_sum<1024, int>(t, ws);
+  const int tt = block_sum<256, int>(t, ws);
   if (tid == 0) B.gtiles[(size_t)bh * D.Cq + a] = tt;
 }
 
@@ -2412,15 +2467,15 @@ void launch_plan_from_labels(const void* q, const void* k, const int* klab, cons
 
 // Steps shared by both planners: routing, probes, attention tiles.
 void launch_route_probes(const Dims& D, const Bufs& B, hipStream_t s) {
-  hipLaunchKernelGGL(k_route_sort, dim3(D.Cq, D.BH), dim3(1024), 0, s, D, B);
+  hipLaunchKernelGGL(k_route_sort, dim3(D.Cq, D.BH), dim3(256), 0, s, D, B);
   hipLaunchKernelGGL(k_route_tau, dim3(D.BH), dim3(1024), 0, s, D, B);
-  hipLaunchKernelGGL(k_route_emit, dim3(D.Cq, D.BH), dim3(1024), 0, s, D, B);
+  hipLaunchKernelGGL(k_route_emit, dim3(D.Cq, D.BH), dim3(256), 0, s, D, B);
   if (D.dtype == 1 && D.attn_w == 8) {
     // the 8-wave attention's key order and its runs (on small calls, whose 4-wave tiles are
     // short, the three launches cost more than the shorter runs save; the fp32 kernel reads
     // the route itself)
     hipLaunchKernelGGL(k_key_order, dim3(D.BH), dim3(1024), 0, s, D, B);
-    hipLaunchKernelGGL(k_att_runs, dim3(D.Cq, D.BH), dim3(1024), 0, s, D, B);
+    hipLaunchKernelGGL(k_att_runs, dim3(D.Cq, D.BH), dim3(256), 0, s, D, B);
     hipLaunchKernelGGL(k_att_perm, dim3(D.Ck, D.BH), dim3(256), 0, s, D, B);
   }
   hipLaunchKernelGGL(k_fill_i32, dim3(256), dim3(256), 0, s, B.pslot, (long long)D.BH * D.N, -1);
