@@ -9,7 +9,8 @@ of the Lloyd assignment and of the group masses), against the CPU oracle:
 * the group masses u computed from given labels, entry by entry, and the route cells
   they select;
 * the library's own plan with 256 and 512 groups: unprobed error, partition quality
-  (inertia), label agreement and iteration counts against stated bounds.
+  (inertia), label agreement and iteration counts against stated bounds, on an 8-head input
+  and on one head of the 40 x 93,600 workload in its own launch configuration.
 """
 import numpy as np
 import pytest
@@ -292,3 +293,55 @@ def test_own_plan_with_many_groups(C):
         say(f"  mean unprobed error gpu {g.mean():.4f} oracle {o.mean():.4f}")
         assert abs(g.mean() - o.mean()) <= 0.05 * o.mean()
         sp.close()
+
+
+# ---------------------------------------------------------------- (a) own plan at full size
+def test_full_size_own_plan_one_head():
+    """The benchmark's workload (40 x 93,600, 512 key and 512 query groups, density 0.22) in
+    its own launch configuration, head 0 carrying the seeded inputs and the other heads filler:
+    the GPU's own plan for head 0 (k-means, masses, route, probes) against the oracle's own plan
+    for that head (float64 Lloyd from the same seeds): partitions as tight as the oracle's, a
+    comparable number of iterations, most labels shared, and the same unprobed error within 5%
+    on 2048 sampled rows."""
+    w = configs.CONFIGS["c5"]
+    N, d, H = configs.seq_len(w), w["head_dim"], w["heads"]
+    say(f"case: full-size own plan c5 N={N} H={H}, head 0 checked")
+    (cq, q64), (ck, k64), (cv, v64) = inputs(w, [0])
+    g = torch.Generator(device=DEV).manual_seed(11)
+    tq, tk, tv = (torch.randn((1, H, N, d), generator=g, device=DEV, dtype=torch.float32).to(torch.bfloat16)
+                  for _ in range(3))
+    tq[0, 0], tk[0, 0], tv[0, 0] = cq[0, 0], ck[0, 0], cv[0, 0]
+    sp = SparsePR(config_from_workload(w), device=DEV)
+    sp(tq, tk, tv)
+    torch.cuda.synchronize()
+    info = sp.info()[0]
+    ex = {k: np_(sp.export(k))[0] for k in ("KEY_LABELS", "QUERY_LABELS", "PROBES")}
+    out = np_(sp.out[0, 0])
+    sp.close()
+    p = O.call_params(w)
+    s = p["scale"]
+    hp = O.plan_head(q64[0], k64[0], p, 0, 25, 1e-4)
+    X = O.key_features(k64[0], q64[0][hp.sampled], s)
+    ik_g, ik_o = _inertia(X, ex["KEY_LABELS"]), _inertia(X, hp.key_labels)
+    del X
+    _, Fg = O.query_features(q64[0], O.group_means(k64[0], ex["KEY_LABELS"], info["key_groups"]), s)
+    iq_g = _inertia(Fg, ex["QUERY_LABELS"])
+    del Fg
+    iq_o = _inertia(O.query_features(q64[0], hp.key_centroids, s)[1], hp.query_labels)
+    ka, qa = np.mean(ex["KEY_LABELS"] == hp.key_labels), np.mean(ex["QUERY_LABELS"] == hp.query_labels)
+    say(f"  iters gpu {info['key_iters']}/{info['query_iters']} oracle {hp.key_iters}/{hp.query_iters}; "
+        f"groups gpu {info['key_groups']}/{info['query_groups']} oracle {hp.Ck}/{hp.Cq}; agreement key {ka:.3f} "
+        f"query {qa:.3f}; inertia ratio gpu/oracle key {ik_g / ik_o:.4f} query {iq_g / iq_o:.4f}")
+    assert ik_g <= 1.005 * ik_o and iq_g <= 1.005 * iq_o
+    assert 2 <= info["key_iters"] <= 25 and 2 <= info["query_iters"] <= 25
+    assert abs(info["key_iters"] - hp.key_iters) <= 5 and abs(info["query_iters"] - hp.query_iters) <= 5
+    assert ka >= AGREE[0][0] and qa >= AGREE[0][1]
+    mask = np.ones(N, bool)
+    mask[hp.probes] = False
+    mask[ex["PROBES"]] = False
+    rows = np.sort(np.random.default_rng(5).choice(np.flatnonzero(mask), 2048, replace=False))
+    dn = O.dense_attention(q64[0][rows], k64[0], v64[0], s)
+    ref = O.attend_fit_apply_rows(q64[0], k64[0], v64[0], p, hp, rows)
+    g_err, o_err = O.rel_l2(out[rows], dn), O.rel_l2(ref["out"], dn)
+    say(f"  mean unprobed error gpu {g_err.mean():.4f} oracle {o_err.mean():.4f}")
+    assert abs(g_err.mean() - o_err.mean()) <= 0.05 * o_err.mean()
