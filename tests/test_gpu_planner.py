@@ -10,7 +10,7 @@ of the Lloyd assignment and of the group masses), against the CPU oracle:
   they select;
 * the library's own plan with 256 and 512 groups: unprobed error, partition quality
   (inertia), label agreement and iteration counts against stated bounds, on an 8-head input
-  and on one head of the 40 x 93,600 workload in its own launch configuration.
+  and on one head of each full-size workload in its own launch configuration.
 """
 import numpy as np
 import pytest
@@ -296,16 +296,18 @@ def test_own_plan_with_many_groups(C):
 
 
 # ---------------------------------------------------------------- (a) own plan at full size
-def test_full_size_own_plan_one_head():
-    """The benchmark's workload (40 x 93,600, 512 key and 512 query groups, density 0.22) in
-    its own launch configuration, head 0 carrying the seeded inputs and the other heads filler:
-    the GPU's own plan for head 0 (k-means, masses, route, probes) against the oracle's own plan
-    for that head (float64 Lloyd from the same seeds): partitions as tight as the oracle's, a
-    comparable number of iterations, most labels shared, and the same unprobed error within 5%
-    on 2048 sampled rows."""
-    w = configs.CONFIGS["c5"]
+@pytest.mark.parametrize("name", ["c3", "c4", "c5"])
+def test_full_size_own_plan_one_head(name):
+    """A full-size workload (c5, the benchmark: 40 x 93,600, 512 key and 512 query groups;
+    c3: 40 x 75,600, 256 groups; c4: 24 x 119,056, 384 groups, text tokens) in its own launch
+    configuration, head 0 carrying the seeded inputs and the other heads filler: the GPU's own
+    plan for head 0 (k-means, masses, route, probes) against the oracle's own plan for that head
+    (float64 Lloyd from the same seeds): partitions as tight as the oracle's, a comparable
+    number of iterations, most labels shared, and the same unprobed error within 5% on 2048
+    sampled rows."""
+    w = configs.CONFIGS[name]
     N, d, H = configs.seq_len(w), w["head_dim"], w["heads"]
-    say(f"case: full-size own plan c5 N={N} H={H}, head 0 checked")
+    say(f"case: full-size own plan {name} N={N} H={H}, head 0 checked")
     (cq, q64), (ck, k64), (cv, v64) = inputs(w, [0])
     g = torch.Generator(device=DEV).manual_seed(11)
     tq, tk, tv = (torch.randn((1, H, N, d), generator=g, device=DEV, dtype=torch.float32).to(torch.bfloat16)
