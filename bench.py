@@ -117,8 +117,8 @@ def cpu_baseline(w, q64, k64, v64, heads, min_seconds=10.0):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py runs on one GPU only: the SparsePR call's heads are independent and this build "
-              f"measures one GPU's share; --gpus {args.gpus} is not supported.", file=sys.stderr)
+        print(f"bench.py runs on one GPU only: the SparsePR call's heads are independent and the benchmark "
+              f"measures one GPU's share of them; --gpus {args.gpus} is not supported.", file=sys.stderr)
         sys.exit(2)
     if args.copy_calibration:
         copy_calibration()
