@@ -233,9 +233,22 @@ sparsepr_status sparsepr_plan_create(const sparsepr_config* cfg, sparsepr_plan_t
   D.max_atiles = (N + 32 * D.attn_w - 1) / (32 * D.attn_w) + D.Cq;
   {
     // split the probe rows' keys so that about 1024 workgroups share the probe attention
-    // (probe tiles have the attention tiles' height)
+    // (probe tiles have the attention tiles' height), rounded up, when that at most doubles
+    // the split, to whole rounds of the workgroups the CUs hold at once (one per CU for
+    // 256-row tiles, two for 128-row ones), so that the last round is not a partial one
     const int ptiles = (D.M + 32 * D.attn_w - 1) / (32 * D.attn_w);
-    const long long want = ptiles > 0 ? (1024 + (long long)D.BH * ptiles - 1) / ((long long)D.BH * ptiles) : 1;
+    const long long items = (long long)D.BH * ptiles;
+    long long want = ptiles > 0 ? (1024 + items - 1) / items : 1;
+    int dev = 0, cus = 0;
+    if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) !=
+                                                 hipSuccess || cus <= 0)
+      cus = 256;  // (no device: the MI355X's count)
+    const long long slots = (long long)cus * (D.attn_w == 8 ? 1 : 2);
+    for (long long c = want; ptiles > 0 && c <= 2 * want; ++c)
+      if ((items * c) % slots == 0) {
+        want = c;
+        break;
+      }
     const int maxch = (N + 511) / 512;
     int pch = (int)(want < 1 ? 1 : (want > maxch ? maxch : want));
     if (pch < 1) pch = 1;
