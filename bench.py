@@ -11,6 +11,7 @@ The default workload is the largest one that fits one GPU: the tight-budget stre
 40 heads x 93,600 tokens, d = 128, 512 key and 512 query groups, 1,024 probes, at density
 0.22 (inside the 22-26% band the metric is quoted at).
   python bench.py --copy-calibration      # plain device copy of a known size (for PMC scaling)
+  python bench.py --power                 # board power and core clock while each stage family runs
 """
 from __future__ import annotations
 
@@ -70,6 +71,9 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-heads", type=int, default=1)
     ap.add_argument("--copy-calibration", action="store_true")
+    ap.add_argument("--power", action="store_true",
+                    help="instead of the benchmark: board power and core clock while planning, attention and "
+                         "dense attention each run back to back")
     return ap.parse_args()
 
 
@@ -85,6 +89,77 @@ def copy_calibration():
         dst.copy_(src)
     torch.cuda.synchronize()
     print(json.dumps({"copy_bytes": 2 * n, "launches": 3}))
+
+
+def power_probe(sp, spd, tq, tk, tv, seconds=6.0):
+    """Board power (the driver's hwmon power1_input, W) and core clock (the current level of
+    pp_dpm_sclk, MHz), sampled every 0.2 s from a host thread while one stage family runs back
+    to back: the cold plan (k-means, masses, routing, probes), the attention of a planned call
+    (permutation, block-sparse and probe attention) and the dense reference."""
+    import glob
+    import re
+    import statistics
+    import threading
+
+    import torch
+
+    dev = sorted(glob.glob("/sys/class/drm/card*/device/hwmon/hwmon*/power1_input"))
+    if not dev:
+        return {"error": "no hwmon power1_input"}
+    hw = os.path.dirname(dev[0])
+    sclk = os.path.join(hw, "..", "..", "pp_dpm_sclk")
+
+    def read(path, scale):
+        try:
+            return float(open(path).read()) * scale
+        except (OSError, ValueError):
+            return None
+
+    def clock():
+        try:
+            for line in open(sclk):
+                if "*" in line:
+                    m = re.search(r"(\d+)\s*Mhz", line, re.I)
+                    return float(m.group(1)) if m else None
+        except OSError:
+            return None
+        return None
+
+    phase, samples, stop = ["idle"], [], threading.Event()
+
+    def sampler():
+        while not stop.is_set():
+            samples.append((phase[0], read(dev[0], 1e-6), clock()))
+            time.sleep(0.2)
+
+    th = threading.Thread(target=sampler, daemon=True)
+    th.start()
+    time.sleep(2.0)
+    calls = {}
+    for name, fn in (("plan", lambda: sp.plan(tq, tk)), ("attend", lambda: sp.attend(tq, tk, tv)),
+                     ("dense", lambda: spd.dense(tq, tk, tv, torch.empty_like(tq)))):
+        phase[0] = name
+        t0, n = time.perf_counter(), 0
+        while time.perf_counter() - t0 < seconds:
+            fn()
+            torch.cuda.synchronize()
+            n += 1
+        calls[name] = (n, (time.perf_counter() - t0) / n * 1e3)
+        phase[0] = "between"
+        time.sleep(1.0)
+    stop.set()
+    th.join()
+    out = {"power_cap_w": read(os.path.join(hw, "power1_cap"), 1e-6), "sample_s": 0.2}
+    for name in ("idle", "plan", "attend", "dense"):
+        v = [s for s in samples if s[0] == name][2:]  # the first samples lag the phase change
+        pw = [s[1] for s in v if s[1] is not None]
+        ck = [s[2] for s in v if s[2] is not None]
+        out[name] = {"samples": len(v), "watts_median": round(statistics.median(pw), 1) if pw else None,
+                     "watts_max": round(max(pw), 1) if pw else None,
+                     "sclk_mhz_median": statistics.median(ck) if ck else None}
+        if name in calls:
+            out[name].update({"calls": calls[name][0], "ms_per_call": round(calls[name][1], 3)})
+    return out
 
 
 def cpu_baseline(w, q64, k64, v64, heads, min_seconds=10.0):
@@ -144,6 +219,16 @@ def main():
     log(f"inputs {args.config}: B*H={BH} N={N} d={d} {w['dtype']} ({time.perf_counter() - t0:.1f} s)")
 
     sp = SparsePR(config_from_workload(w), device=dev)
+    if args.power:
+        spd = SparsePR(config_from_workload(w), device=dev)
+        sp(tq, tk, tv)
+        torch.cuda.synchronize()
+        res = {"workload": args.config, "power": power_probe(sp, spd, tq, tk, tv)}
+        torch.cuda.synchronize()
+        sp.close()
+        spd.close()
+        print(json.dumps(res), flush=True)
+        return
     L.sparsepr_set_stage_timing(sp.plan_h, 1)
     for _ in range(args.warmup):
         sp(tq, tk, tv)
