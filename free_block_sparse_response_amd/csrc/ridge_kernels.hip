@@ -498,24 +498,33 @@ __global__ __launch_bounds__(256) void k_theta_split(Dims D, Bufs B, const float
 // bf16 apply on the matrix cores: Theta^T (hi + lo bf16, copied into LDS) times the exact
 // bf16 row of o (transposed product: lane l owns row l % 32 of a 32-row set and 16 output
 // dims per 32-dim block); each wave owns RS row sets so every operand read feeds RS
-// products. The epilogue adds o and the bias; probe rows take o_dense.
+// products. The epilogue adds o and the bias (probe rows take o_dense) and writes the rows
+// into LDS, where the operands were, so that they leave as whole contiguous rows: a store
+// of 8-byte pieces scattered over 32 rows costs the L2 one request per piece.
 template <int DD, int RS>
 __global__ __launch_bounds__(256) void k_apply_bf16(Dims D, Bufs B, const bf16* o_sp, const float* o_dn,
                                                     const float* coeffs, bf16* out) {
-  constexpr int KS = DD + 8;
-  __shared__ __attribute__((aligned(16))) bf16 Th[DD * KS];
-  __shared__ __attribute__((aligned(16))) bf16 Tl[DD * KS];
+  constexpr int KS = DD + 8;  // row stride (elements) of the operands and of the staged output
+  constexpr int NT = DD * DD / 8 / 256;  // 16-byte chunks per thread and operand
+  constexpr int TSZ = 2 * DD * KS > 4 * RS * 32 * KS ? 2 * DD * KS : 4 * RS * 32 * KS;
+  __shared__ __attribute__((aligned(16))) bf16 Tsm[TSZ];  // the operands, then the output rows
   __shared__ float bias[DD];
+  bf16* Th = Tsm;
+  bf16* Tl = Tsm + DD * KS;
   const int blk = blockIdx.x, bh = blockIdx.y;
   const int tid = threadIdx.x, w = tid / kWave, l32 = lane_id() & 31, h = lane_id() >> 5;
   const bf16* sh = B.theta_h + (size_t)bh * DD * DD;
   const bf16* sl = B.theta_l + (size_t)bh * DD * DD;
-  for (int e = tid; e < DD * DD / 8; e += 256) {
-    const int r = e / (DD / 8), c8 = (e % (DD / 8)) * 8;
-    *reinterpret_cast<bf16x8*>(&Th[r * KS + c8]) = *reinterpret_cast<const bf16x8*>(sh + (size_t)r * DD + c8);
-    *reinterpret_cast<bf16x8*>(&Tl[r * KS + c8]) = *reinterpret_cast<const bf16x8*>(sl + (size_t)r * DD + c8);
+  // every load in flight together: Theta^T (hi / lo), the bias, the rows of o; the LDS
+  // stores wait for the Theta loads only
+  bf16x8 th[NT], tl[NT];
+#pragma unroll
+  for (int i = 0; i < NT; ++i) {
+    const int e = tid + 256 * i, r = e / (DD / 8), c8 = (e % (DD / 8)) * 8;
+    th[i] = *reinterpret_cast<const bf16x8*>(sh + (size_t)r * DD + c8);
+    tl[i] = *reinterpret_cast<const bf16x8*>(sl + (size_t)r * DD + c8);
   }
-  if (tid < DD) bias[tid] = coeffs[(size_t)bh * (DD + 1) * DD + (size_t)DD * DD + tid];
+  const float bv = tid < DD ? coeffs[(size_t)bh * (DD + 1) * DD + (size_t)DD * DD + tid] : 0.f;
   int row[RS], slot[RS];
   bf16x8 xr[RS][DD / 16];
 #pragma unroll
@@ -527,9 +536,18 @@ __global__ __launch_bounds__(256) void k_apply_bf16(Dims D, Bufs B, const bf16* 
     for (int c = 0; c < DD / 16; ++c) xr[rs][c] = *reinterpret_cast<const bf16x8*>(orow + 16 * c + 8 * h);
     slot[rs] = (valid && D.M > 0) ? B.pslot[(size_t)bh * D.N + row[rs]] : -1;
   }
-  __syncthreads();
 #pragma unroll
-  for (int jb = 0; jb < DD; jb += 32) {
+  for (int i = 0; i < NT; ++i) {
+    const int e = tid + 256 * i, r = e / (DD / 8), c8 = (e % (DD / 8)) * 8;
+    *reinterpret_cast<bf16x8*>(&Th[r * KS + c8]) = th[i];
+    *reinterpret_cast<bf16x8*>(&Tl[r * KS + c8]) = tl[i];
+  }
+  if (tid < DD) bias[tid] = bv;
+  __syncthreads();
+  // the output values, bf16 pairs in the accumulator's layout, until the operands are free
+  uint32_t pk[RS][DD / 32][8];
+#pragma unroll
+  for (int jb = 0; jb < DD / 32; ++jb) {
     f32x16 acc[RS];
 #pragma unroll
     for (int rs = 0; rs < RS; ++rs)
@@ -537,8 +555,8 @@ __global__ __launch_bounds__(256) void k_apply_bf16(Dims D, Bufs B, const bf16* 
       for (int v = 0; v < 16; ++v) acc[rs][v] = 0.f;
 #pragma unroll
     for (int c = 0; c < DD / 16; ++c) {
-      const bf16x8 ah = *reinterpret_cast<const bf16x8*>(&Th[(jb + l32) * KS + 16 * c + 8 * h]);
-      const bf16x8 al = *reinterpret_cast<const bf16x8*>(&Tl[(jb + l32) * KS + 16 * c + 8 * h]);
+      const bf16x8 ah = *reinterpret_cast<const bf16x8*>(&Th[(32 * jb + l32) * KS + 16 * c + 8 * h]);
+      const bf16x8 al = *reinterpret_cast<const bf16x8*>(&Tl[(32 * jb + l32) * KS + 16 * c + 8 * h]);
 #pragma unroll
       for (int rs = 0; rs < RS; ++rs) {
         acc[rs] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah, xr[rs][c], acc[rs], 0, 0, 0);
@@ -547,13 +565,13 @@ __global__ __launch_bounds__(256) void k_apply_bf16(Dims D, Bufs B, const bf16* 
     }
 #pragma unroll
     for (int rs = 0; rs < RS; ++rs) {
-      // o's own entries for the output layout (dims jb + 8 g + 4 h + r) come from the operand
-      // registers: the 16 dims of chunk c sit 8 per lane half, and swapping dwords 0, 1 of
-      // the upper half with dwords 2, 3 of the lower one gives each lane its two runs of 4
+      // o's own entries for the output layout (dims 32 jb + 8 g + 4 h + r) come from the
+      // operand registers: the 16 dims of chunk c sit 8 per lane half, and swapping dwords
+      // 0, 1 of the upper half with dwords 2, 3 of the lower one gives each lane its two runs
       uint32_t xo[2][4];
 #pragma unroll
       for (int q = 0; q < 2; ++q) {
-        const bf16x8 xc = xr[rs][jb / 16 + q];
+        const bf16x8 xc = xr[rs][2 * jb + q];
         uint32_t dw[4];
         __builtin_memcpy(dw, &xc, 16);
         const auto s02 = __builtin_amdgcn_permlane32_swap(dw[0], dw[2], false, false);
@@ -563,11 +581,9 @@ __global__ __launch_bounds__(256) void k_apply_bf16(Dims D, Bufs B, const bf16* 
         xo[q][2] = s02[1];
         xo[q][3] = s13[1];
       }
-      if (row[rs] >= D.N) continue;
-      bf16* dst = out + ((size_t)bh * D.N + row[rs]) * DD;
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
-        const int j = jb + 8 * g + 4 * h;
+        const int j = 32 * jb + 8 * g + 4 * h;
         bf16x4 ov;
         if (slot[rs] >= 0) {
           const float4 dv = *reinterpret_cast<const float4*>(o_dn + ((size_t)bh * D.M + slot[rs]) * DD + j);
@@ -579,10 +595,33 @@ __global__ __launch_bounds__(256) void k_apply_bf16(Dims D, Bufs B, const bf16* 
 #pragma unroll
           for (int r = 0; r < 4; ++r) ov[r] = (bf16)((float)xv[r] + acc[rs][4 * g + r] + bias[j + r]);
         }
-        *reinterpret_cast<bf16x4*>(dst + j) = ov;
+        __builtin_memcpy(&pk[rs][jb][2 * g], &ov, 8);
       }
     }
   }
+  __syncthreads();  // every operand read is done: the region takes the output rows
+  bf16* stg = Tsm + (size_t)w * RS * 32 * KS;  // this wave's rows, RS sets of 32
+#pragma unroll
+  for (int rs = 0; rs < RS; ++rs)
+#pragma unroll
+    for (int jb = 0; jb < DD / 32; ++jb)
+#pragma unroll
+      for (int g = 0; g < 4; ++g)
+        __builtin_memcpy(stg + (rs * 32 + l32) * KS + 32 * jb + 8 * g + 4 * h, &pk[rs][jb][2 * g], 8);
+  __syncthreads();
+  // whole rows out: DD / 8 lanes per row, 64 / (DD / 8) rows per store
+  constexpr int LPR = DD / 8, RPI = kWave / LPR;
+  const int lr = lane_id() / LPR, lc = (lane_id() % LPR) * 8;
+#pragma unroll
+  for (int rs = 0; rs < RS; ++rs)
+#pragma unroll
+    for (int i = 0; i < 32 / RPI; ++i) {
+      const int r = RPI * i + lr;
+      const int grow = blk * 128 * RS + 128 * rs + 32 * w + r;
+      if (grow < D.N)
+        *reinterpret_cast<bf16x8*>(out + ((size_t)bh * D.N + grow) * DD + lc) =
+            *reinterpret_cast<const bf16x8*>(stg + (rs * 32 + r) * KS + lc);
+    }
 }
 
 // Output truncation of the fit: C = R^T W R (d x d) of the probe residuals R = o_dense -
