@@ -1356,7 +1356,10 @@ __global__ __launch_bounds__(256, RS == 1 ? 4 : 2) void k_km_assign_bf16(const b
 // Row constants (see k_rowquad) on the matrix cores: (G x)_i for 32 dims at a time, dotted
 // with x in the lane that owns the row. G (bf16 hi / lo) is staged in LDS once per
 // workgroup, which then takes the 128-row blocks blockIdx.x, + gridDim.x, ... of its head;
-// the next block's rows are loaded while the current block's products run.
+// the next block's rows are loaded while the current block's products run. Lane l32
+// supplies G row 32 ib + pi(l32) (bits 2 and 3 of the index swapped), so the 16 dims whose
+// (G x) a lane half receives are the ones its own share of the row operand holds (G is
+// symmetric, but any row order works: only the pairing of (G x)_i with x_i matters).
 template <int DD>
 __global__ __launch_bounds__(256, 2) void k_rowquad_bf16(const bf16* x, Dims D, const bf16* Gsh, const bf16* Gsl,
                                                          float* rowconst, float* alpha_out,
@@ -1368,14 +1371,17 @@ __global__ __launch_bounds__(256, 2) void k_rowquad_bf16(const bf16* x, Dims D, 
   const int w = threadIdx.x / kWave, l32 = lane_id() & 31, h = lane_id() >> 5;
   const bf16* xb = x + (size_t)bh * D.N * DD;
   auto row_of = [&](int blk) { return min(blk * kKmRows + 32 * w + l32, D.N - 1); };
-  bf16x8 xr[DD / 16];
+  bf16x8 xr[DD / 16], xn[DD / 16];
   load_row_operand<DD>(xb + (size_t)row_of(blockIdx.x) * DD, xr);
   copy_hilo<DD, DD>(Gsh + (size_t)bh * DD * DD, Gsl + (size_t)bh * DD * DD, 0, DD, Gh, Gl);
   __syncthreads();
   const float cf = alpha_out ? (float)kst_for_c[bh].c_final : 0.f;
+  const int prow = (l32 & ~12) | ((l32 & 4) << 1) | ((l32 & 8) >> 1);  // pi(l32)
   for (int blk = blockIdx.x; blk < D.nblk; blk += gridDim.x) {
     const int row = blk * kKmRows + 32 * w + l32;
-    const bf16* xrow = xb + (size_t)row_of(blk) * DD;
+    // the next block's rows (past the last block the current rows again: no branch)
+    const int nx = blk + gridDim.x;
+    load_row_operand<DD>(xb + (size_t)row_of(nx < D.nblk ? nx : blk) * DD, xn);
     // (the G operand reads are the same every block: a zero offset the compiler cannot see
     // through keeps them from being hoisted into registers)
     int z = 0;
@@ -1383,19 +1389,21 @@ __global__ __launch_bounds__(256, 2) void k_rowquad_bf16(const bf16* x, Dims D, 
     float part = 0.f;
 #pragma unroll
     for (int ib = 0; ib < DD / 32; ++ib) {
-      const f32x16 acc = mfma_rows<DD>(Gh + z, Gl + z, 32 * ib, xr);
-      if (ib == DD / 32 - 1) {
-        // the last products are issued: the next block's rows replace the operand (past the
-        // last block the current rows are read again, so no branch goes around the loads)
-        const int nx = blk + gridDim.x;
-        load_row_operand<DD>(xb + (size_t)row_of(nx < D.nblk ? nx : blk) * DD, xr);
-      }
+      f32x16 acc;
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const bf16x4 xv = *reinterpret_cast<const bf16x4*>(xrow + 32 * ib + 8 * g + 4 * h);
+      for (int v = 0; v < 16; ++v) acc[v] = 0.f;
 #pragma unroll
-        for (int r = 0; r < 4; ++r) part = fmaf(acc[4 * g + r], (float)xv[r], part);
+      for (int c = 0; c < DD / 16; ++c) {
+        const int o = (32 * ib + prow) * KS + 16 * c + 8 * h + z;
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*reinterpret_cast<const bf16x8*>(&Gh[o]), xr[c], acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*reinterpret_cast<const bf16x8*>(&Gl[o]), xr[c], acc, 0, 0, 0);
       }
+      // acc[4 g + r] = (G x)_i, i = 32 ib + pi(8 g + 4 h + r) = 32 ib + 16 (g >> 1) + 8 h + 4 (g & 1) + r:
+      // element 4 (g & 1) + r of the lane's operand chunk 2 ib + (g >> 1)
+#pragma unroll
+      for (int g = 0; g < 4; ++g)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) part = fmaf(acc[4 * g + r], (float)xr[2 * ib + (g >> 1)][4 * (g & 1) + r], part);
     }
     part += __shfl_xor(part, 32, kWave);
     if (h == 0 && row < D.N) {
@@ -1407,41 +1415,53 @@ __global__ __launch_bounds__(256, 2) void k_rowquad_bf16(const bf16* x, Dims D, 
         rowconst[o] = part;
       }
     }
+#pragma unroll
+    for (int c = 0; c < DD / 16; ++c) xr[c] = xn[c];
   }
 }
 
-// Group masses over one attention tile (128 rows of one query group): pass 1 finds each
-// row's softmax max and sum over the key groups, pass 2 adds the normalised masses into
-// per-tile column sums (rows reduced inside the wave, waves in a fixed order).
-template <int DD>
-__global__ __launch_bounds__(256) void k_group_mass_bf16(const bf16* q, Dims D, Bufs B) {
-  constexpr int CB = 64, KS = DD + 8;
+// Group masses over attention tiles (128 rows of one query group, four waves each; TPB
+// consecutive tiles per workgroup, so that each staged centroid chunk serves 128 TPB rows):
+// pass 1 finds each row's softmax max and sum over the key groups, pass 2 adds the
+// normalised masses into per-tile column sums (rows reduced inside the wave, the tile's
+// waves in a fixed order).
+template <int DD, int TPB>
+__global__ __launch_bounds__(256 * TPB) void k_group_mass_bf16(const bf16* q, Dims D, Bufs B) {
+  constexpr int CB = 64, KS = DD + 8, NT = 256 * TPB;
   __shared__ __attribute__((aligned(16))) bf16 Yh[CB * KS];
   __shared__ __attribute__((aligned(16))) bf16 Yl[CB * KS];
   __shared__ float lg[kMaxGroups];
-  __shared__ float colw[4][CB];
-  const int t = blockIdx.x, bh = blockIdx.y;
-  if (t >= B.ntiles[bh]) return;
-  const int2 tl = B.tiles[(size_t)bh * D.max_tiles + t];
-  const int a = tl.x, pos0 = tl.y;
-  const int rows = min(D.qt, B.qoff[(size_t)bh * (D.Cq + 1) + a + 1] - pos0);
+  __shared__ float colw[TPB][4][CB];
+  __shared__ float rowm[TPB][128], rowinv[TPB][128];
+  const int bh = blockIdx.y, nt = B.ntiles[bh];
+  if (blockIdx.x * TPB >= nt) return;  // (uniform over the workgroup)
   const int tid = threadIdx.x, w = tid / kWave, l32 = lane_id() & 31;
-  const int lrow = 32 * w + l32;
+  const int k = w >> 2, wl = w & 3;  // this wave's tile in the workgroup, and its wave there
+  const int t = blockIdx.x * TPB + k;
+  const bool tile_ok = t < nt;
+  const int2 tl = B.tiles[(size_t)bh * D.max_tiles + (tile_ok ? t : blockIdx.x * TPB)];
+  const int a = tl.x, pos0 = tl.y;
+  const int rows = tile_ok ? min(D.qt, B.qoff[(size_t)bh * (D.Cq + 1) + a + 1] - pos0) : 0;
+  const int lrow = 32 * wl + l32;
   const bool valid = lrow < rows;
   const int tok = B.qperm[(size_t)bh * D.N + pos0 + (valid ? lrow : 0)];
   bf16x8 xr[DD / 16];
   load_row_operand<DD>(q + ((size_t)bh * D.N + tok) * DD, xr);
   const int Ck = B.kst[bh].c_final;
   const int* ko = B.koff + (size_t)bh * (D.Ck + 1);
-  for (int b = tid; b < Ck; b += 256) lg[b] = log2f((float)(ko[b + 1] - ko[b]));  // log2 domain
+  for (int b = tid; b < Ck; b += NT) lg[b] = log2f((float)(ko[b + 1] - ko[b]));  // log2 domain
   const bf16* Kh = B.kcent_h + (size_t)bh * D.Ck * DD;
   const bf16* Kl = B.kcent_l + (size_t)bh * D.Ck * DD;
   const float sc2 = D.scale * 1.4426950408889634f;  // logits in the log2 domain
+  // a wave past its tile's last row (or in a workgroup's missing last tile) only helps stage
+  // the centroids: its products, which no row would use, are skipped
+  const bool live = 32 * wl < rows;
   float m = -INFINITY, ssum = 0.f;
   for (int c0 = 0; c0 < Ck; c0 += CB) {  // pass 1
     __syncthreads();
     copy_hilo<DD, CB>(Kh, Kl, c0, Ck, Yh, Yl);
     __syncthreads();
+    if (!live) continue;
 #pragma unroll
     for (int yb = 0; yb < CB; yb += 32) {
       const f32x16 acc = mfma_rows<DD>(Yh, Yl, yb, xr);
@@ -1464,25 +1484,29 @@ __global__ __launch_bounds__(256) void k_group_mass_bf16(const bf16* q, Dims D, 
   }
   {
     const float mo = __shfl_xor(m, 32, kWave), so = __shfl_xor(ssum, 32, kWave);
-    const float mm = fmaxf(m, mo);  // finite: lane half 0 holds centroid 0
+    const float mm = fmaxf(m, mo);  // finite on a live wave: lane half 0 holds centroid 0
     ssum = ssum * __builtin_amdgcn_exp2f(m - mm) + so * __builtin_amdgcn_exp2f(mo - mm);
     m = mm;
   }
-  const float inv = valid ? 1.f / ssum : 0.f;
+  const float inv = valid ? 1.f / ssum : 0.f;  // (a dead wave's rows are never read below)
   // pass 2 with the operands swapped, so that a lane holds one centroid against 16 rows and
   // the column sums are in-lane: the rows' max and 1 / sum come from LDS
-  __shared__ float rowm[128], rowinv[128];
   if (lane_id() < 32) {
-    rowm[lrow] = m;
-    rowinv[lrow] = inv;
+    rowm[k][lrow] = m;
+    rowinv[k][lrow] = inv;
   }
   float* part = B.mass_part + ((size_t)bh * D.max_tiles + t) * D.Ck;
+  const int ttid = tid & 255;  // thread index within the tile's four waves
   for (int c0 = 0; c0 < Ck; c0 += CB) {  // pass 2
     __syncthreads();
     copy_hilo<DD, CB>(Kh, Kl, c0, Ck, Yh, Yl);
     __syncthreads();
 #pragma unroll
     for (int yb = 0; yb < CB; yb += 32) {
+      if (!live) {
+        if (lane_id() < 32) colw[k][wl][yb + l32] = 0.f;
+        continue;
+      }
       const f32x16 acc = mfma_cols<DD>(Yh, Yl, yb, xr);
       const int col = c0 + yb + l32;
       float cs = 0.f;
@@ -1490,15 +1514,16 @@ __global__ __launch_bounds__(256) void k_group_mass_bf16(const bf16* q, Dims D, 
         const float lgc = lg[col];
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
-          const int r = 32 * w + acc_row(v);
-          cs += __builtin_amdgcn_exp2f(fmaf(sc2, acc[v], lgc) - rowm[r]) * rowinv[r];
+          const int r = 32 * wl + acc_row(v);
+          cs += __builtin_amdgcn_exp2f(fmaf(sc2, acc[v], lgc) - rowm[k][r]) * rowinv[k][r];
         }
       }
       cs += xor32(cs);
-      if (lane_id() < 32) colw[w][yb + l32] = cs;
+      if (lane_id() < 32) colw[k][wl][yb + l32] = cs;
     }
     __syncthreads();
-    if (tid < CB && c0 + tid < Ck) part[c0 + tid] = ((colw[0][tid] + colw[1][tid]) + colw[2][tid]) + colw[3][tid];
+    if (tile_ok && ttid < CB && c0 + ttid < Ck)
+      part[c0 + ttid] = ((colw[k][0][ttid] + colw[k][1][ttid]) + colw[k][2][ttid]) + colw[k][3][ttid];
   }
 }
 
@@ -2205,7 +2230,9 @@ static void rowquad(const T* x, const Dims& D, const Bufs& B, const float* G, fl
 template <typename T, int DD>
 static void group_mass(const T* q, const Dims& D, const Bufs& B, hipStream_t s) {
   if constexpr (std::is_same<T, bf16>::value) {
-    hipLaunchKernelGGL((k_group_mass_bf16<DD>), dim3(D.max_tiles, D.BH), dim3(256), 0, s, q, D, B);
+    constexpr int TPB = kMassTiles;
+    hipLaunchKernelGGL((k_group_mass_bf16<DD, TPB>), dim3((D.max_tiles + TPB - 1) / TPB, D.BH), dim3(256 * TPB), 0, s,
+                       q, D, B);
     hipLaunchKernelGGL(k_group_mass_final, dim3(D.Cq, D.BH), dim3(256), 0, s, D, B);
   } else {
     hipLaunchKernelGGL((k_group_mass<T, DD>), dim3(D.Cq, D.BH), dim3(256), 0, s, q, D, B);

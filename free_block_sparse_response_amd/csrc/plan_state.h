@@ -140,5 +140,6 @@ struct Bufs {
 constexpr int kKmRows = 128;   // rows per Lloyd assignment block
 constexpr int kAttnQT = 128;   // query rows per attention tile (4 waves x 32)
 constexpr int kKeyTile = 64;   // keys per attention tile
+constexpr int kMassTiles = 2;  // attention tiles per group-mass workgroup (one staged centroid chunk each)
 
 }  // namespace spr
