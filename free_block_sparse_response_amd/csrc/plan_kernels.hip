@@ -1449,7 +1449,10 @@ __global__ __launch_bounds__(256 * TPB) void k_group_mass_bf16(const bf16* q, Di
   load_row_operand<DD>(q + ((size_t)bh * D.N + tok) * DD, xr);
   const int Ck = B.kst[bh].c_final;
   const int* ko = B.koff + (size_t)bh * (D.Ck + 1);
-  for (int b = tid; b < Ck; b += NT) lg[b] = log2f((float)(ko[b + 1] - ko[b]));  // log2 domain
+  // log2 of the group sizes; -inf past the last group, so that a padded centroid (zero
+  // operand) scores -inf with no test (every read below stays inside the array: C_k <=
+  // kMaxGroups, a multiple of the 64-centroid chunk)
+  for (int b = tid; b < kMaxGroups; b += NT) lg[b] = b < Ck ? log2f((float)(ko[b + 1] - ko[b])) : -INFINITY;
   const bf16* Kh = B.kcent_h + (size_t)bh * D.Ck * DD;
   const bf16* Kl = B.kcent_l + (size_t)bh * D.Ck * DD;
   const float sc2 = D.scale * 1.4426950408889634f;  // logits in the log2 domain
@@ -1468,8 +1471,7 @@ __global__ __launch_bounds__(256 * TPB) void k_group_mass_bf16(const bf16* q, Di
       float z[16], mx = m;
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
-        const int col = c0 + yb + acc_row(v);
-        z[v] = col < Ck ? fmaf(sc2, acc[v], lg[col]) : -INFINITY;
+        z[v] = fmaf(sc2, acc[v], lg[c0 + yb + acc_row(v)]);
         mx = fmaxf(mx, z[v]);
       }
       // a lane half whose 16 centroids are all past the last group (C_k' <= 4) has no
@@ -1508,15 +1510,13 @@ __global__ __launch_bounds__(256 * TPB) void k_group_mass_bf16(const bf16* q, Di
         continue;
       }
       const f32x16 acc = mfma_cols<DD>(Yh, Yl, yb, xr);
-      const int col = c0 + yb + l32;
+      // (a column past the last group has lg = -inf: its terms are exp2(-inf) = 0)
+      const float lgc = lg[c0 + yb + l32];
       float cs = 0.f;
-      if (col < Ck) {
-        const float lgc = lg[col];
 #pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          const int r = 32 * wl + acc_row(v);
-          cs += __builtin_amdgcn_exp2f(fmaf(sc2, acc[v], lgc) - rowm[k][r]) * rowinv[k][r];
-        }
+      for (int v = 0; v < 16; ++v) {
+        const int r = 32 * wl + acc_row(v);
+        cs += __builtin_amdgcn_exp2f(fmaf(sc2, acc[v], lgc) - rowm[k][r]) * rowinv[k][r];
       }
       cs += xor32(cs);
       if (lane_id() < 32) colw[k][wl][yb + l32] = cs;
