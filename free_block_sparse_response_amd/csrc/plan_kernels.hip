@@ -828,17 +828,19 @@ __global__ __launch_bounds__(256) void k_km_update(const T* x, Dims D, Bufs B, K
   for (int q = 0; q < 4; ++q) tv0[q] = tab[min(4 * tid + q, D.nblk - 1)];
   const double* ip = B.ipart + (size_t)bh * D.nblk;
   double pv0[8];
+  if (tid < kWave) {  // (only wave 0 sums them: the other waves would re-read the same bytes)
 #pragma unroll
-  for (int u = 0; u < 8; ++u) pv0[u] = ip[min(lane_id() + u * kWave, D.nblk - 1)];
+    for (int u = 0; u < 8; ++u) pv0[u] = ip[min(lane_id() + u * kWave, D.nblk - 1)];
+  }
   asm volatile("" ::: "memory");  // (keeps the loads above ahead of the test)
   if (done_iter < t) return;
 #pragma unroll
   for (int q = 0; q < 4; ++q)
     if (4 * tid + q >= D.nblk) tv0[q] = 0;
-#pragma unroll
-  for (int u = 0; u < 8; ++u)
-    if (lane_id() + u * kWave >= D.nblk) pv0[u] = 0.0;
   if (tid < kWave) {
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+      if (lane_id() + u * kWave >= D.nblk) pv0[u] = 0.0;
     double sum = 0.0;
 #pragma unroll
     for (int u = 0; u < 8; ++u) sum += pv0[u];
