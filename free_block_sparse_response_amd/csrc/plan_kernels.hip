@@ -535,6 +535,7 @@ __device__ void km_init_item(const T* x, const Dims& D, const Bufs& B, int C, co
     for (int w = 0; w < DD / kWave; ++w) sum += red[w];
     B.cnorm[(size_t)bh * D.C + b] = sum;
     store_bias_operand(B.cent_b + ((size_t)bh * D.C + b) * 16, sum);
+    B.gcount[(size_t)bh * D.C + b] = 0;  // no update has moved the centroid yet
     if (b == 0) {
       st[bh].done_iter = 0x7fffffff;
       st[bh].iters = 0;
@@ -796,8 +797,8 @@ constexpr int kUpdChunk = 1024; // members listed in LDS at a time
 // First the stopping rule of the head: every block of the head evaluates it identically
 // (the inertia of assignment t is the fixed-order sum of the sort blocks' partials, set
 // against the inertia of assignment t - 1); block 0 records it. Unless the head stops at t,
-// the new centroid m_b is the mean of the group's rows alpha_j x_j, then G m_b and
-// m_b G m_b. The members are read in stable group order (sort blocks in order, each
+// the new centroid m_b is the mean of the group's rows alpha_j x_j, marked with t for
+// k_km_metric_terms, which forms G m_b and m_b G m_b next. The members are read in stable group order (sort blocks in order, each
 // block's rows of group b from its lists: count and start in tab, rows in lperm), listed
 // in LDS a chunk at a time; member r of a chunk sits in slot r % RS and the slots are
 // summed in a fixed order, so the result does not depend on scheduling.
@@ -807,20 +808,16 @@ __global__ __launch_bounds__(256) void k_km_update(const T* x, Dims D, Bufs B, K
   constexpr int LPR = DD / EV;
   constexpr int RS = 256 / LPR;
   __shared__ float sh[RS * DD];
-  __shared__ float m[DD];
-  __shared__ float red[4];
   __shared__ int wpre[kUpdWin], wbeg[kUpdWin], mlist[kUpdChunk], ws[4];
   __shared__ int go;
   const int b = blockIdx.x, bh = blockIdx.y, tid = threadIdx.x;
   // Independent loads first, so that their latencies overlap: the head's state, the first
   // window of the group's per-block counts and (wave 0) the inertia partials, read 8 at a
   // time per lane and summed in the fixed order; the state is tested once they are all in
-  // flight. (The metric column for G m is read after the gather, so that the gather runs
-  // with few registers and many workgroups per CU.)
+  // flight. (The terms under the metric G are formed by k_km_metric_terms, for 32 groups
+  // per read of G.)
   const int done_iter = st[bh].done_iter;
   const double prev = st[bh].inertia[(t - 1) & 1];  // (this launch writes the other slot)
-  constexpr int KH = 256 / DD;
-  const int i = tid % DD, part = tid / DD;
   const int* tab = B.tab + ((size_t)bh * D.C + b) * D.nblk;
   // (clamped, unconditional loads, masked afterwards: no branch between them)
   int tv0[4];
@@ -936,40 +933,104 @@ __global__ __launch_bounds__(256) void k_km_update(const T* x, Dims D, Bufs B, K
   if (tid < DD) {
     float tot = 0.f;
     for (int q = 0; q < RS; ++q) tot += sh[q * DD + tid];
-    m[tid] = tot / (float)n;
+    B.cent[((size_t)bh * D.C + b) * DD + tid] = tot / (float)n;
   }
-  __syncthreads();
-  float p = 0.f;
-  {
-    const float* G = B.metric + (size_t)bh * DD * DD;
-    float gv[DD / KH];
+  // the mark k_km_metric_terms looks for (the group sizes are written here only after the run)
+  if (tid == 0) B.gcount[(size_t)bh * D.C + b] = t;
+}
+
+// The metric terms of the centroids that iteration t's update moved (marked with t): G m_b,
+// -2 G m_b as the assignment's bf16 hi / lo operands, m_b G m_b and its bias operand. One
+// workgroup per 32 groups of a head reads G once (the update's workgroups read it once per
+// group). Each entry of G m_b is formed in the order the update used to: KH = 256 / DD
+// partial chains over k = q + KH kk (kk ascending), added q = 0, 1, ... to 0; m_b G m_b sums
+// m_i (G m_b)_i over 64-lane halves by the same butterfly, the halves in order. Threads take
+// 4 groups x DD / 32 dims, so every G row read from LDS feeds 4 groups.
+template <int DD>
+__global__ __launch_bounds__(256) void k_km_metric_terms(Dims D, Bufs B, int C, const KmState* st, int t) {
+  constexpr int GB = 32, KH = 256 / DD, DPT = DD / 32;
+  constexpr int GH = DD / 2;  // rows of G staged at a time (two halves: three workgroups fit a CU)
+  __shared__ __attribute__((aligned(16))) float Gs[GH * DD];  // half of G, then G m_b of the groups
+  __shared__ __attribute__((aligned(16))) float mT[DD][GB];   // m_b, transposed
+  __shared__ int mark[GB];
+  const int bh = blockIdx.y, g0 = blockIdx.x * GB, tid = threadIdx.x;
+  if (st[bh].done_iter < t) return;  // the head stopped before iteration t: no update ran
+  if (tid < GB) mark[tid] = g0 + tid < C && B.gcount[(size_t)bh * D.C + g0 + tid] == t;
+  const int any = __syncthreads_or(tid < GB && mark[tid]);
+  if (!any) return;
+  const float* G = B.metric + (size_t)bh * DD * DD;
+  for (int e = tid; e < GB * DD; e += 256) {
+    const int gl = e / DD, k = e % DD;
+    mT[k][gl] = mark[gl] ? B.cent[((size_t)bh * D.C + g0 + gl) * DD + k] : 0.f;
+  }
+  const int gq = tid / 32, dq = tid % 32;  // groups 4 gq .. 4 gq + 3, dims DPT dq .. DPT dq + DPT - 1
+  float acc[KH][4][DPT];
 #pragma unroll
-    for (int kk = 0; kk < DD / KH; ++kk) gv[kk] = G[(size_t)(part + kk * KH) * DD + i];
-    float tt = 0.f;
+  for (int q = 0; q < KH; ++q)
 #pragma unroll
-    for (int kk = 0; kk < DD / KH; ++kk) tt = fmaf(gv[kk], m[part + kk * KH], tt);
-    sh[tid] = tt;
+    for (int g = 0; g < 4; ++g)
+#pragma unroll
+      for (int j = 0; j < DPT; ++j) acc[q][g][j] = 0.f;
+  // rows k of G in two halves; each chain still takes its k in ascending order
+  for (int hf = 0; hf < 2; ++hf) {
+    if (hf) __syncthreads();  // the first half's reads are done
+    for (int e = tid; e < GH * DD / 4; e += 256)
+      reinterpret_cast<float4*>(Gs)[e] = reinterpret_cast<const float4*>(G + (size_t)hf * GH * DD)[e];
     __syncthreads();
-    if (tid < DD) {
-      float tot = 0.f;
-      for (int q = 0; q < KH; ++q) tot += sh[q * DD + i];
-      const size_t o = ((size_t)bh * D.C + b) * DD + i;
-      B.cent[o] = m[i];
-      B.cent_t[o] = tot;
-      const bf16 th = (bf16)(-2.f * tot);  // the assignment's operand: -2 G m_b, hi / lo
-      B.cent_h[o] = th;
-      B.cent_l[o] = (bf16)(-2.f * tot - (float)th);
-      p = m[i] * tot;
+#pragma unroll 4
+    for (int kk = 0; kk < GH / KH; ++kk) {
+#pragma unroll
+      for (int q = 0; q < KH; ++q) {
+        const int kl = q + KH * kk, k = hf * GH + kl;
+        float gv[DPT];
+        if constexpr (DPT == 4) {
+          const float4 v = *reinterpret_cast<const float4*>(&Gs[kl * DD + 4 * dq]);
+          gv[0] = v.x; gv[1] = v.y; gv[2] = v.z; gv[3] = v.w;
+        } else {
+          const float2 v = *reinterpret_cast<const float2*>(&Gs[kl * DD + 2 * dq]);
+          gv[0] = v.x; gv[1] = v.y;
+        }
+        const float4 mv4 = *reinterpret_cast<const float4*>(&mT[k][4 * gq]);
+        const float mv[4] = {mv4.x, mv4.y, mv4.z, mv4.w};
+#pragma unroll
+        for (int g = 0; g < 4; ++g)
+#pragma unroll
+          for (int j = 0; j < DPT; ++j) acc[q][g][j] = fmaf(gv[j], mv[g], acc[q][g][j]);
+      }
     }
   }
-  p = wave_sum(p);
-  if (lane_id() == 0) red[tid / kWave] = p;
+  __syncthreads();  // every read of G is done: Gs takes G m_b, [group][dim]
+  float* tT = Gs;
+#pragma unroll
+  for (int g = 0; g < 4; ++g)
+#pragma unroll
+    for (int j = 0; j < DPT; ++j) {
+      float tot = 0.f;
+#pragma unroll
+      for (int q = 0; q < KH; ++q) tot += acc[q][g][j];
+      tT[(4 * gq + g) * DD + DPT * dq + j] = tot;
+    }
   __syncthreads();
-  if (tid == 0) {
+  // operands, and m_b G m_b: wave w takes groups w, w + 4, ...
+  const int w = tid / kWave, l = lane_id();
+  for (int gl = w; gl < GB; gl += 4) {
+    if (!mark[gl]) continue;  // (uniform over the wave)
+    const size_t ob = ((size_t)bh * D.C + g0 + gl) * DD;
     float sum = 0.f;
-    for (int w = 0; w < DD / kWave; ++w) sum += red[w];
-    B.cnorm[(size_t)bh * D.C + b] = sum;
-    store_bias_operand(B.cent_b + ((size_t)bh * D.C + b) * 16, sum);
+#pragma unroll
+    for (int hh = 0; hh < DD / kWave; ++hh) {
+      const int i = hh * kWave + l;
+      const float tot = tT[gl * DD + i];
+      B.cent_t[ob + i] = tot;
+      const bf16 th = (bf16)(-2.f * tot);
+      B.cent_h[ob + i] = th;
+      B.cent_l[ob + i] = (bf16)(-2.f * tot - (float)th);
+      sum += wave_sum(mT[i][gl] * tot);
+    }
+    if (l == 0) {
+      B.cnorm[(size_t)bh * D.C + g0 + gl] = sum;
+      store_bias_operand(B.cent_b + ((size_t)bh * D.C + g0 + gl) * 16, sum);
+    }
   }
 }
 
@@ -1009,6 +1070,7 @@ __global__ __launch_bounds__(256) void k_km_warm_init(Dims D, Bufs B, const floa
     for (int w = 0; w < DD / kWave; ++w) sum += red[w];
     B.cnorm[(size_t)bh * D.C + b] = live ? sum : INFINITY;
     store_bias_operand(B.cent_b + ((size_t)bh * D.C + b) * 16, live ? sum : INFINITY);
+    B.gcount[(size_t)bh * D.C + b] = 0;  // no update has moved the centroid yet
   }
 }
 
@@ -2201,6 +2263,7 @@ static void lloyd_iterations(const T* x, const Dims& D, const Bufs& B, int C, Km
     else
       hipLaunchKernelGGL((k_km_assign<T, DD>), dim3(D.nblk, D.BH), dim3(256), 0, s, x, D, B, C, st, t);
     hipLaunchKernelGGL((k_km_update<T, DD>), dim3(C, D.BH), dim3(256), 0, s, x, D, B, st, t);
+    hipLaunchKernelGGL((k_km_metric_terms<DD>), dim3((C + 31) / 32, D.BH), dim3(256), 0, s, D, B, C, st, t);
   }
   // group starts and the permutation of the final assignment
   hipLaunchKernelGGL(k_km_scan_groups, dim3(C, D.BH), dim3(64), 0, s, D, B, C, st, 0);
