@@ -797,17 +797,20 @@ constexpr int kUpdChunk = 1024; // members listed in LDS at a time
 // First the stopping rule of the head: every block of the head evaluates it identically
 // (the inertia of assignment t is the fixed-order sum of the sort blocks' partials, set
 // against the inertia of assignment t - 1); block 0 records it. Unless the head stops at t,
-// the new centroid m_b is the mean of the group's rows alpha_j x_j, marked with t for
-// k_km_metric_terms, which forms G m_b and m_b G m_b next. The members are read in stable group order (sort blocks in order, each
+// the new centroid m_b is the mean of the group's rows alpha_j x_j; with TERMS the block
+// then forms G m_b and m_b G m_b itself, without it marks the group with t for
+// k_km_metric_terms, which forms them next (same arithmetic). The members are read in stable group order (sort blocks in order, each
 // block's rows of group b from its lists: count and start in tab, rows in lperm), listed
 // in LDS a chunk at a time; member r of a chunk sits in slot r % RS and the slots are
 // summed in a fixed order, so the result does not depend on scheduling.
-template <typename T, int DD>
+template <typename T, int DD, bool TERMS>
 __global__ __launch_bounds__(256) void k_km_update(const T* x, Dims D, Bufs B, KmState* st, int t) {
   constexpr int EV = 16 / sizeof(T);
   constexpr int LPR = DD / EV;
   constexpr int RS = 256 / LPR;
   __shared__ float sh[RS * DD];
+  __shared__ float m[TERMS ? DD : 1];
+  __shared__ float red[4];
   __shared__ int wpre[kUpdWin], wbeg[kUpdWin], mlist[kUpdChunk], ws[4];
   __shared__ int go;
   const int b = blockIdx.x, bh = blockIdx.y, tid = threadIdx.x;
@@ -930,19 +933,61 @@ __global__ __launch_bounds__(256) void k_km_update(const T* x, Dims D, Bufs B, K
 #pragma unroll
   for (int e = 0; e < EV; ++e) sh[slot * DD + c0 + e] = acc[e];
   __syncthreads();
-  if (tid < DD) {
-    float tot = 0.f;
-    for (int q = 0; q < RS; ++q) tot += sh[q * DD + tid];
-    B.cent[((size_t)bh * D.C + b) * DD + tid] = tot / (float)n;
+  if constexpr (!TERMS) {
+    if (tid < DD) {
+      float tot = 0.f;
+      for (int q = 0; q < RS; ++q) tot += sh[q * DD + tid];
+      B.cent[((size_t)bh * D.C + b) * DD + tid] = tot / (float)n;
+    }
+    // the mark k_km_metric_terms looks for (the group sizes are written here only after the run)
+    if (tid == 0) B.gcount[(size_t)bh * D.C + b] = t;
+  } else {
+    // small launches: the terms here, in the order k_km_metric_terms reproduces
+    constexpr int KH = 256 / DD;
+    const int i = tid % DD, part = tid / DD;
+    if (tid < DD) {
+      float tot = 0.f;
+      for (int q = 0; q < RS; ++q) tot += sh[q * DD + tid];
+      m[tid] = tot / (float)n;
+    }
+    __syncthreads();
+    float p = 0.f;
+    const float* G = B.metric + (size_t)bh * DD * DD;
+    float gv[DD / KH];
+#pragma unroll
+    for (int kk = 0; kk < DD / KH; ++kk) gv[kk] = G[(size_t)(part + kk * KH) * DD + i];
+    float tt = 0.f;
+#pragma unroll
+    for (int kk = 0; kk < DD / KH; ++kk) tt = fmaf(gv[kk], m[part + kk * KH], tt);
+    sh[tid] = tt;
+    __syncthreads();
+    if (tid < DD) {
+      float tot = 0.f;
+      for (int q = 0; q < KH; ++q) tot += sh[q * DD + i];
+      const size_t o = ((size_t)bh * D.C + b) * DD + i;
+      B.cent[o] = m[i];
+      B.cent_t[o] = tot;
+      const bf16 th = (bf16)(-2.f * tot);  // the assignment's operand: -2 G m_b, hi / lo
+      B.cent_h[o] = th;
+      B.cent_l[o] = (bf16)(-2.f * tot - (float)th);
+      p = m[i] * tot;
+    }
+    p = wave_sum(p);
+    if (lane_id() == 0) red[tid / kWave] = p;
+    __syncthreads();
+    if (tid == 0) {
+      float sum = 0.f;
+      for (int w = 0; w < DD / kWave; ++w) sum += red[w];
+      B.cnorm[(size_t)bh * D.C + b] = sum;
+      store_bias_operand(B.cent_b + ((size_t)bh * D.C + b) * 16, sum);
+    }
   }
-  // the mark k_km_metric_terms looks for (the group sizes are written here only after the run)
-  if (tid == 0) B.gcount[(size_t)bh * D.C + b] = t;
 }
 
 // The metric terms of the centroids that iteration t's update moved (marked with t): G m_b,
 // -2 G m_b as the assignment's bf16 hi / lo operands, m_b G m_b and its bias operand. One
 // workgroup per 32 groups of a head reads G once (the update's workgroups read it once per
-// group). Each entry of G m_b is formed in the order the update used to: KH = 256 / DD
+// group). Each entry of G m_b is formed in the order the update uses on small launches: KH = 256 / DD
 // partial chains over k = q + KH kk (kk ascending), added q = 0, 1, ... to 0; m_b G m_b sums
 // m_i (G m_b)_i over 64-lane halves by the same butterfly, the halves in order. Threads take
 // 4 groups x DD / 32 dims, so every G row read from LDS feeds 4 groups.
@@ -2253,6 +2298,10 @@ __global__ void k_identity_plan(Dims D, Bufs B) {
 template <typename T, int DD>
 static void lloyd_iterations(const T* x, const Dims& D, const Bufs& B, int C, KmState* st, int* perm,
                              hipStream_t s) {
+  // The metric terms (G m_b, m_b G m_b, the operands) in their own launch, one read of G per 32
+  // groups, when the update has at least 16 workgroups per CU to feed; on smaller launches the
+  // extra launch's latency costs more than the update's reads of G (same arithmetic either way).
+  const bool split_terms = (long long)C * D.BH >= 16 * 256;
   for (int t = 1; t <= D.max_iter; ++t) {
     if constexpr (std::is_same<T, bf16>::value)
       if (D.assign_lo)
@@ -2262,8 +2311,12 @@ static void lloyd_iterations(const T* x, const Dims& D, const Bufs& B, int C, Km
         hipLaunchKernelGGL((k_km_assign_bf16<DD, 1, false>), dim3(D.nblk, D.BH), dim3(256), 0, s, x, D, B, C, st, t);
     else
       hipLaunchKernelGGL((k_km_assign<T, DD>), dim3(D.nblk, D.BH), dim3(256), 0, s, x, D, B, C, st, t);
-    hipLaunchKernelGGL((k_km_update<T, DD>), dim3(C, D.BH), dim3(256), 0, s, x, D, B, st, t);
-    hipLaunchKernelGGL((k_km_metric_terms<DD>), dim3((C + 31) / 32, D.BH), dim3(256), 0, s, D, B, C, st, t);
+    if (split_terms) {
+      hipLaunchKernelGGL((k_km_update<T, DD, false>), dim3(C, D.BH), dim3(256), 0, s, x, D, B, st, t);
+      hipLaunchKernelGGL((k_km_metric_terms<DD>), dim3((C + 31) / 32, D.BH), dim3(256), 0, s, D, B, C, st, t);
+    } else {
+      hipLaunchKernelGGL((k_km_update<T, DD, true>), dim3(C, D.BH), dim3(256), 0, s, x, D, B, st, t);
+    }
   }
   // group starts and the permutation of the final assignment
   hipLaunchKernelGGL(k_km_scan_groups, dim3(C, D.BH), dim3(64), 0, s, D, B, C, st, 0);
