@@ -987,10 +987,10 @@ __global__ __launch_bounds__(256) void k_km_update(const T* x, Dims D, Bufs B, K
 // The metric terms of the centroids that iteration t's update moved (marked with t): G m_b,
 // -2 G m_b as the assignment's bf16 hi / lo operands, m_b G m_b and its bias operand. One
 // workgroup per 32 groups of a head reads G once (the update's workgroups read it once per
-// group). Each entry of G m_b is formed in the order the update uses on small launches: KH = 256 / DD
-// partial chains over k = q + KH kk (kk ascending), added q = 0, 1, ... to 0; m_b G m_b sums
-// m_i (G m_b)_i over 64-lane halves by the same butterfly, the halves in order. Threads take
-// 4 groups x DD / 32 dims, so every G row read from LDS feeds 4 groups.
+// group). Each entry of G m_b is formed in the order the update uses on small launches:
+// KH = 256 / DD partial chains over k = q + KH kk (kk ascending), added q = 0, 1, ... to 0;
+// m_b G m_b sums m_i (G m_b)_i over 64-lane halves by the same butterfly, the halves in
+// order. Threads take 4 groups x DD / 32 dims, so every G row read from LDS feeds 4 groups.
 template <int DD>
 __global__ __launch_bounds__(256) void k_km_metric_terms(Dims D, Bufs B, int C, const KmState* st, int t) {
   constexpr int GB = 32, KH = 256 / DD, DPT = DD / 32;
