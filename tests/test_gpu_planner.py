@@ -295,6 +295,33 @@ def test_own_plan_with_many_groups(C):
         sp.close()
 
 
+# ------------------------------------------- metric terms: separate launch against in-update
+@pytest.mark.parametrize("d", [64, 128])
+def test_metric_terms_split_matches_in_update(d):
+    """The Lloyd update forms G m_b and m_b G m_b itself when C * heads < 4096 and leaves them
+    to a separate launch otherwise, in the same arithmetic. The hashes depend on the head
+    index only, so heads 0..14 of a 16-head call (separate launch) and of a 15-head call on
+    the same inputs (in the update) must plan bit for bit alike."""
+    w = configs.with_overrides("c2", heads=16, head_dim=d, grid=(8, 32, 32), n_key_groups=256,
+                               n_query_groups=256, n_sampled=256, n_probes=128)
+    assert 256 * 16 >= 4096 > 256 * 15
+    say(f"case: metric terms split vs in-update, d={d}, N={configs.seq_len(w)}, C=256, heads 16 / 15")
+    (tq, _), (tk, _), (tv, _) = inputs(w)
+    res = []
+    for H in (16, 15):
+        sp = SparsePR(config_from_workload(w, heads=H), device=DEV)
+        sp(*(t[:, :H].contiguous() for t in (tq, tk, tv)))
+        torch.cuda.synchronize()
+        info = sp.info()
+        ex = {k: np_(sp.export(k))[:15] for k in ("KEY_LABELS", "QUERY_LABELS", "GROUP_MASS", "PROBES")}
+        ex["iters"] = np.array([[info[i]["key_iters"], info[i]["query_iters"]] for i in range(15)])
+        res.append(ex)
+        sp.close()
+    for k in res[0]:
+        assert np.array_equal(res[0][k], res[1][k]), k
+    say(f"  iterations {res[0]['iters'][:4].tolist()} ..., identical on both paths")
+
+
 # ---------------------------------------------------------------- (a) own plan at full size
 @pytest.mark.parametrize("name", ["c3", "c4", "c5"])
 def test_full_size_own_plan_one_head(name):
